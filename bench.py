@@ -1,0 +1,215 @@
+"""Benchmark of the Packed-linear hot path on one MI355X.
+
+Default workload (the headline metric): the q_proj-shaped decode GEMV,
+K = 5120, N = 6144, batch 1, bf16 activations, 2.25-bit packed weights.
+One step = one full pass of the path over one input vector: the signed
+1024-block transform of x, its exact split into integer limbs, and the
+weight-streaming ternary matmul (tb_ternary_gemv_prepare + _run).  Steps
+rotate over enough distinct copies of the packed weights (>= 1 GiB in
+total) that the 256 MB last-level cache cannot serve a repeat, so every
+step streams its weights from HBM.
+
+Prints ONE JSON line.  `value` is effective weight GB/s of the whole step
+(N*K*9/32 bytes of codes, scales and biases per step, over the HIP-event
+time of the timed region); `roofline` prices the weight-streaming kernel
+alone against the 8 TB/s HBM peak, its duration taken from HIP events
+around each of its launches inside the timed region; `cpu_baseline` times
+the fp64 oracle on the host on the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload q_proj]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+METRIC = "effective weight GB/s (2.25 bpw) for fused FWHT+ternary GEMV; % of HBM peak"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline_gemv(p, codes, scales, biases, budget_s=12.0):
+    """Time the fp64 oracle on the same workload (bounded number of calls)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    t0 = time.perf_counter()
+    oracle.packed_linear(p.x64, p.signs, p.block, codes, scales, biases)
+    one = time.perf_counter() - t0
+    reps = max(1, min(20, int(budget_s / max(one, 1e-3))))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.packed_linear(p.x64, p.signs, p.block, codes, scales, biases)
+    per = (time.perf_counter() - t0) / reps
+    return per, reps + 1, blas_threads
+
+
+def run_q_proj(args):
+    import torch
+
+    import hadamard_rotated_quantized_amd as tb
+    import oracle
+    from hadamard_rotated_quantized_amd import synth
+
+    p = synth.config_problem(args.workload)
+    N, K, B = p.N, p.K, p.B
+    wbytes = N * K * 9 // 32
+    log(f"workload {args.workload}: N={N} K={K} B={B} weight bytes {wbytes}")
+    codes, s, b = tb.tb_pack(p.t, p.scales)
+    dev = torch.device("cuda:0")
+    c0 = torch.from_numpy(codes.view(np.int32)).to(dev)
+    s0 = torch.from_numpy(s).to(dev)
+    b0 = torch.from_numpy(b).to(dev)
+    R = args.replicas or max(1, math.ceil((1 << 30) / wbytes))
+    reps = [(c0, s0, b0)] + [(c0.clone(), s0.clone(), b0.clone()) for _ in range(R - 1)]
+    x = (torch.from_numpy(p.x_store.view(np.int16)).view(torch.bfloat16) if p.xdtype == "bf16"
+         else torch.from_numpy(p.x_store)).to(dev)
+    sg = torch.from_numpy(p.signs).to(dev)
+    ws = torch.empty(tb.tb_ternary_gemv_workspace_size(B, K), dtype=torch.uint8, device=dev)
+    y = torch.empty((B, N), dtype=torch.float32, device=dev)
+
+    # parity of the exact configuration that is timed
+    oc, osc, ob = oracle.pack(p.t, p.scales)
+    want = oracle.packed_linear(p.x64, p.signs, p.block, oc, osc, ob)
+    tb.tb_ternary_gemv_prepare(x, sg, p.block, ws)
+    tb.tb_ternary_gemv_run(ws, B, K, *reps[R - 1], out=y)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    rel = float(np.linalg.norm(got - want) / np.linalg.norm(want))
+    mabs = float(np.abs(got - want).max() / np.abs(want).max())
+    log(f"parity rel L2 {rel:.2e} max-abs {mabs:.2e}")
+    if not (rel <= 1e-4 and mabs <= 1e-3):
+        raise SystemExit("parity check failed; refusing to report a number")
+
+    def capture(n, with_prepare):
+        """HIP graph of n consecutive steps over the replica ring (the step's
+        kernels are recorded exactly as the eager calls enqueue them)."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                if with_prepare:
+                    tb.tb_ternary_gemv_prepare(x, sg, p.block, ws)
+                c, sc, bi = reps[i % R]
+                tb.tb_ternary_gemv_run(ws, B, K, c, sc, bi, out=y)
+        return g
+
+    y_eager = y.clone()
+    full, rem = divmod(args.steps, R)
+    g_steps = capture(R, True)
+    g_rem = capture(rem, True) if rem else None
+    g_runs = capture(R, False)
+    for _ in range(max(1, args.warmup // R)):
+        g_steps.replay()
+    torch.cuda.synchronize()
+
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(full):
+        g_steps.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    if not torch.equal(y, y_eager):
+        raise SystemExit("graph replay result differs from the eager result")
+
+    # the weight-streaming kernel alone: run launches back to back over the ring
+    reps_k = max(1, args.steps // R)
+    k0 = torch.cuda.Event(enable_timing=True)
+    k1 = torch.cuda.Event(enable_timing=True)
+    k0.record()
+    for _ in range(reps_k):
+        g_runs.replay()
+    k1.record()
+    torch.cuda.synchronize()
+    main_us = k0.elapsed_time(k1) * 1e3 / (reps_k * R)
+
+    ms_step = total_ms / args.steps
+    value = wbytes * args.steps / (total_ms * 1e-3) / 1e9
+    achieved = wbytes / (main_us * 1e-6) / 1e9
+
+    # hot (cache-resident) repeat of one replica, labelled as such
+    g_hot = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_hot):
+        for _ in range(100):
+            tb.tb_ternary_gemv_run(ws, B, K, c0, s0, b0, out=y)
+    h0 = torch.cuda.Event(enable_timing=True)
+    h1 = torch.cuda.Event(enable_timing=True)
+    h0.record()
+    for _ in range(5):
+        g_hot.replay()
+    h1.record()
+    torch.cuda.synchronize()
+    hot_us = h0.elapsed_time(h1) * 1e3 / 500
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        per, ncalls, thr = cpu_baseline_gemv(p, oc, osc, ob)
+        cpu = {"value": round(wbytes / per / 1e9, 4), "unit": "GB/s", "cores": thr, "kind": "oracle",
+               "sample": f"{ncalls} full {args.workload} calls (N={N}, K={K}, B={B}), "
+                         f"{per * 1e3:.1f} ms each, numpy fp64 (decode single-threaded, BLAS {thr} threads)"}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload} decode GEMV N={N} K={K} batch {B} bf16 activations, "
+                               f"2.25 bpw packed weights, {R} rotating weight replicas",
+                   "N": N, "K": K, "batch": B, "block": p.block, "replicas": R},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "detail": {"kernel": "gemv_main_kernel", "main_kernel_us_mean": round(main_us, 3),
+                   "timing": "HIP graphs of the step sequence; main kernel timed as a graph of run "
+                             "launches over the same replica ring",
+                   "step_us": round(ms_step * 1e3, 3), "hot_run_us_same_replica": round(hot_us, 3),
+                   "parity_rel_l2": rel, "parity_max_abs_rel": mabs},
+    }
+    print(json.dumps(out), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=12200)
+    ap.add_argument("--warmup", type=int, default=1220)
+    ap.add_argument("--workload", default="q_proj", choices=["q_proj", "tiny"])
+    ap.add_argument("--replicas", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    run_q_proj(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,314 @@
+"""Python binding of libtb, the gfx950 folded-Hadamard ternary Packed-linear
+library.  Argument marshalling only: every step of the path runs in the HIP
+kernels behind the C ABI declared in include/tb.h.  Functions carry the C
+names; device functions take torch tensors already on the GPU and enqueue on
+torch's current stream.  There is no fallback: if libtb.so is missing or a
+call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libtb.so")
+
+TB_OK = 0
+TB_F32 = 0
+TB_BF16 = 1
+TB_GEMV_MAX_BATCH = 8
+STATUS = {
+    0: "TB_OK", -1: "TB_ERR_ARG", -2: "TB_ERR_SHAPE", -3: "TB_ERR_BLOCK", -4: "TB_ERR_UNSUPPORTED",
+    -5: "TB_ERR_SIGN", -6: "TB_ERR_CODE", -7: "TB_ERR_DTYPE", -8: "TB_ERR_ALIGN", -9: "TB_ERR_HIP",
+    -10: "TB_ERR_WORKSPACE",
+}
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "tb_abi_version": (_I, []),
+    "tb_last_error": (ctypes.c_char_p, []),
+    "tb_status_str": (ctypes.c_char_p, [_I]),
+    "tb_pack": (_I, [_P, _P, _I64, _I64, _P, _P, _P]),
+    "tb_unpack": (_I, [_P, _I64, _I64, _P]),
+    "tb_signs_validate": (_I, [_P, _I64]),
+    "tb_pack_device": (_I, [_P, _P, _I64, _I64, _P, _P, _P, _P, _P]),
+    "tb_fwht_signed": (_I, [_P, _I, _P, _P, _I64, _I64, _I, _I, _P]),
+    "tb_ternary_gemv_workspace_size": (_SZ, [_I64, _I64]),
+    "tb_ternary_gemv": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
+    "tb_ternary_gemv_prepare": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _SZ, _P]),
+    "tb_ternary_gemv_run": (_I, [_P, _SZ, _I64, _I64, _P, _P, _P, _I64, _P, _P]),
+    "tb_ternary_gemm_workspace_size": (_SZ, [_I64, _I64]),
+    "tb_ternary_gemm_prepare": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _SZ, _P]),
+    "tb_ternary_gemm_run": (_I, [_P, _SZ, _I64, _I64, _P, _P, _P, _I64, _P, _P]),
+    "tb_ternary_gemm": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
+    "tb_embed_inverse": (_I, [_P, _I64, _P, _P, _P, _I64, _I64, _P, _I, _P, _P]),
+}
+
+
+class TBError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib():
+    """The loaded libtb.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m hadamard_rotated_quantized_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != TB_OK:
+        raise TBError(status, lib().tb_last_error().decode())
+
+
+# ---------------------------------------------------------------------------
+# host container functions (numpy)
+# ---------------------------------------------------------------------------
+def tb_pack(t: np.ndarray, scales: np.ndarray):
+    """t int8 (N, K) in {-1,0,1}, scales float16 (N, K/128) ->
+    (codes uint32 (N, K/16), scales float16, biases float16)."""
+    t = np.ascontiguousarray(t, dtype=np.int8)
+    sc = np.ascontiguousarray(scales)
+    if sc.dtype == np.float16:
+        sc = sc.view(np.uint16)
+    N, K = t.shape
+    if sc.shape != (N, K // 128) or sc.dtype != np.uint16:
+        raise ValueError("scales must be float16 (N, K/128)")
+    codes = np.empty((N, K // 16), np.uint32)
+    so = np.empty_like(sc)
+    bo = np.empty_like(sc)
+    _check(lib().tb_pack(t.ctypes.data, sc.ctypes.data, N, K, codes.ctypes.data, so.ctypes.data,
+                         bo.ctypes.data))
+    return codes, so.view(np.float16), bo.view(np.float16)
+
+
+def tb_unpack(codes: np.ndarray, K: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint32)
+    N = codes.shape[0]
+    out = np.empty((N, K), np.int8)
+    _check(lib().tb_unpack(codes.ctypes.data, N, K, out.ctypes.data))
+    return out
+
+
+def tb_signs_validate(signs: np.ndarray) -> None:
+    s = np.ascontiguousarray(signs, dtype=np.int8)
+    _check(lib().tb_signs_validate(s.ctypes.data, s.size))
+
+
+# ---------------------------------------------------------------------------
+# device functions (torch tensors on the GPU)
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _dev(t, name, dtype=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _xdtype(x):
+    torch = _torch()
+    if x.dtype == torch.float32:
+        return TB_F32
+    if x.dtype == torch.bfloat16:
+        return TB_BF16
+    raise TypeError(f"activations must be float32 or bfloat16, got {x.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def tb_pack_device(t, scales, check: bool = True):
+    """Pack on the device.  t int8 (N, K), scales float16 (N, K/128), both on
+    the GPU.  With check=True, synchronizes and raises on invalid values."""
+    torch = _torch()
+    _dev(t, "t", torch.int8)
+    _dev(scales, "scales", torch.float16)
+    N, K = t.shape
+    codes = torch.empty((N, K // 16), dtype=torch.int32, device=t.device)
+    so = torch.empty_like(scales)
+    bo = torch.empty_like(scales)
+    bad = torch.zeros(1, dtype=torch.int32, device=t.device)
+    _check(lib().tb_pack_device(t.data_ptr(), scales.data_ptr(), N, K, codes.data_ptr(), so.data_ptr(),
+                                bo.data_ptr(), bad.data_ptr(), _stream()))
+    if check and int(bad.item()) != 0:
+        raise TBError(-6, f"tb_pack_device: {int(bad.item())} values outside {{-1,0,1}}")
+    return codes, so, bo
+
+
+def tb_fwht_signed(x, signs, block: int, inverse: bool = False, out=None):
+    torch = _torch()
+    _dev(x, "x")
+    _dev(signs, "signs", torch.int8)
+    rows, K = x.shape
+    if out is None:
+        out = torch.empty((rows, K), dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    _check(lib().tb_fwht_signed(x.data_ptr(), _xdtype(x), out.data_ptr(), signs.data_ptr(), rows, K,
+                                block, int(bool(inverse)), _stream()))
+    return out
+
+
+def tb_ternary_gemv_workspace_size(B: int, K: int) -> int:
+    return int(lib().tb_ternary_gemv_workspace_size(B, K))
+
+
+def tb_ternary_gemm_workspace_size(M: int, K: int) -> int:
+    return int(lib().tb_ternary_gemm_workspace_size(M, K))
+
+
+def _container(codes, scales, biases):
+    torch = _torch()
+    _dev(codes, "codes")
+    if codes.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("codes must be int32/uint32 words")
+    _dev(scales, "scales", torch.float16)
+    _dev(biases, "biases", torch.float16)
+
+
+def tb_ternary_gemv(x, signs, block: int, codes, scales, biases, out=None, workspace=None):
+    """y (B, N) float32 = Packed linear of x (B, K) for B <= 8."""
+    torch = _torch()
+    _dev(x, "x")
+    _container(codes, scales, biases)
+    if signs is not None:
+        _dev(signs, "signs", torch.int8)
+    B, K = x.shape
+    N = codes.shape[0]
+    if out is None:
+        out = torch.empty((B, N), dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    need = tb_ternary_gemv_workspace_size(B, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check(lib().tb_ternary_gemv(x.data_ptr(), _xdtype(x), B, K, _ptr(signs), block, codes.data_ptr(),
+                                 scales.data_ptr(), biases.data_ptr(), N, out.data_ptr(),
+                                 workspace.data_ptr(), workspace.numel(), _stream()))
+    return out
+
+
+def tb_ternary_gemv_prepare(x, signs, block: int, workspace=None):
+    """Rotate and split x (B, K) into a workspace (uint8 tensor) for
+    tb_ternary_gemv_run; returns the workspace."""
+    torch = _torch()
+    _dev(x, "x")
+    if signs is not None:
+        _dev(signs, "signs", torch.int8)
+    B, K = x.shape
+    need = tb_ternary_gemv_workspace_size(B, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check(lib().tb_ternary_gemv_prepare(x.data_ptr(), _xdtype(x), B, K, _ptr(signs), block,
+                                         workspace.data_ptr(), workspace.numel(), _stream()))
+    return workspace
+
+
+def tb_ternary_gemv_run(workspace, B: int, K: int, codes, scales, biases, out=None):
+    torch = _torch()
+    _dev(workspace, "workspace", torch.uint8)
+    _container(codes, scales, biases)
+    N = codes.shape[0]
+    if out is None:
+        out = torch.empty((B, N), dtype=torch.float32, device=workspace.device)
+    _dev(out, "out", torch.float32)
+    _check(lib().tb_ternary_gemv_run(workspace.data_ptr(), workspace.numel(), B, K, codes.data_ptr(),
+                                     scales.data_ptr(), biases.data_ptr(), N, out.data_ptr(), _stream()))
+    return out
+
+
+def tb_ternary_gemm_prepare(x, signs, block: int, workspace=None):
+    torch = _torch()
+    _dev(x, "x")
+    if signs is not None:
+        _dev(signs, "signs", torch.int8)
+    M, K = x.shape
+    need = tb_ternary_gemm_workspace_size(M, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check(lib().tb_ternary_gemm_prepare(x.data_ptr(), _xdtype(x), M, K, _ptr(signs), block,
+                                         workspace.data_ptr(), workspace.numel(), _stream()))
+    return workspace
+
+
+def tb_ternary_gemm_run(workspace, M: int, K: int, codes, scales, biases, out=None):
+    torch = _torch()
+    _dev(workspace, "workspace", torch.uint8)
+    _container(codes, scales, biases)
+    N = codes.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=workspace.device)
+    _dev(out, "out", torch.float32)
+    _check(lib().tb_ternary_gemm_run(workspace.data_ptr(), workspace.numel(), M, K, codes.data_ptr(),
+                                     scales.data_ptr(), biases.data_ptr(), N, out.data_ptr(), _stream()))
+    return out
+
+
+def tb_ternary_gemm(x, signs, block: int, codes, scales, biases, out=None, workspace=None):
+    """y (M, N) float32 = Packed linear of x (M, K), bf16 MFMA path."""
+    torch = _torch()
+    _dev(x, "x")
+    _container(codes, scales, biases)
+    if signs is not None:
+        _dev(signs, "signs", torch.int8)
+    M, K = x.shape
+    N = codes.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    need = tb_ternary_gemm_workspace_size(M, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check(lib().tb_ternary_gemm(x.data_ptr(), _xdtype(x), M, K, _ptr(signs), block, codes.data_ptr(),
+                                 scales.data_ptr(), biases.data_ptr(), N, out.data_ptr(),
+                                 workspace.data_ptr(), workspace.numel(), _stream()))
+    return out
+
+
+def tb_embed_inverse(ids, codes, scales, biases, signs, block: int, out=None):
+    """(T, K) float32 rows: inverse-transformed dequantized table rows."""
+    torch = _torch()
+    _dev(ids, "ids", torch.int32)
+    _container(codes, scales, biases)
+    if signs is not None:
+        _dev(signs, "signs", torch.int8)
+    T = ids.numel()
+    V = codes.shape[0]
+    K = codes.shape[1] * 16
+    if out is None:
+        out = torch.empty((T, K), dtype=torch.float32, device=ids.device)
+    _dev(out, "out", torch.float32)
+    _check(lib().tb_embed_inverse(ids.data_ptr(), T, codes.data_ptr(), scales.data_ptr(),
+                                  biases.data_ptr(), V, K, _ptr(signs), block, out.data_ptr(), _stream()))
+    return out

@@ -1,0 +1,208 @@
+/*
+ * tb.h -- C ABI of the folded-Hadamard ternary Packed-linear library (gfx950).
+ *
+ * The operation (sources cited by address and section):
+ *
+ *   [P2] kwkr.cn/news/564617, "ternary weights + folded Hadamard rotation":
+ *        every weight matrix was rotated offline in blocks of 1024 along its
+ *        input axis by an orthogonal Hadamard transform with an explicit +-1
+ *        sign vector (widths 5120 / 6144 / 17408); at run time only the
+ *        activation is rotated, by fwht() = normalized transform with scale
+ *        1/sqrt(block), signs multiplied before it on the forward pass and
+ *        again after it on the inverse pass; the matmul then consumes the
+ *        packed 2-bit weights directly (quantized_matmul, transpose=True,
+ *        group_size=128, bits=2).
+ *   [P2] "packing-format engineering": MLX affine 2-bit container, one fp16
+ *        scale and one fp16 bias per group of 128 weights, bias = -scale,
+ *        codes {0,1,2} decode to -s/0/s, 2.25 bits/weight.
+ *   [P3] lpnh.cn/news/2438023, "text model loading": Packed applies
+ *        fwht(x, block, signs) when the module declares a block, then the
+ *        quantized matmul on uint32 code words; the embedding module
+ *        dequantizes the looked-up row and applies fwht(..., inverse=True).
+ *   [P3] "affine 2-bit format and Prism contract v1": block sizes
+ *        512/1024/2048/4096, normalized Sylvester-Walsh-Hadamard, axis = the
+ *        input (last) dimension, explicit signs, every sign must be +-1.
+ *
+ * Definitions used by every entry point (K = input width, N = output rows):
+ *
+ *   codes    uint32 [N][K/16], row-major; code k of a row sits at bits
+ *            2*(k%16)..2*(k%16)+1 of word k/16 (little end first).
+ *   scales   fp16 bit patterns uint16 [N][K/128]; biases likewise.
+ *   W~[n][k] = scales[n][k/128] * c[n][k] + biases[n][k/128],  c = 2-bit code
+ *            (code 3 never comes out of tb_pack; kernels decode it affinely).
+ *   signs    int8 [K], each +-1; block j of the input uses signs[j*L:(j+1)*L].
+ *   R x      = for each block j of L contiguous inputs: H_L (signs .* x) / sqrt(L),
+ *            H_L the natural-order Sylvester matrix, H[i][j] = (-1)^popcount(i&j).
+ *   Packed linear:  y[b][n] = sum_k W~[n][k] * (R x[b])[k]        (fp32 out)
+ *   Embedding:      out[t]  = signs .* (H_L W~[ids[t]]) / sqrt(L) per block
+ *   block = 0 means "no rotation": signs must be NULL and R = identity.
+ *
+ * Conventions:
+ *   - Every function returns a status (TB_OK = 0 or a negative TB_ERR_*),
+ *     never aborts and never throws; tb_last_error() gives a thread-local
+ *     message for the last failure on the calling thread.
+ *   - Device entry points take device pointers and a hipStream_t passed as
+ *     void* (NULL = the default stream); they only validate scalars and
+ *     pointer alignment on the host, never read device memory, never
+ *     synchronize, and enqueue asynchronously on the stream.
+ *   - The caller owns every buffer.  The library never allocates or frees
+ *     memory and keeps no state between calls besides the error string.
+ *   - A size of 0 for N, B, rows, T or M is a no-op returning TB_OK; pointers
+ *     tied to an empty size may then be NULL.  K must be positive.
+ *   - Dimensions are int64; all index arithmetic is 64-bit.
+ */
+#ifndef TB_H
+#define TB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TB_ABI_VERSION 1
+
+/* status codes */
+#define TB_OK               0
+#define TB_ERR_ARG         -1   /* NULL pointer, negative size, K <= 0, bad flag */
+#define TB_ERR_SHAPE       -2   /* K % 128 != 0, K % block != 0, batch out of range */
+#define TB_ERR_BLOCK       -3   /* block not in {0, 512, 1024, 2048, 4096} */
+#define TB_ERR_UNSUPPORTED -4   /* valid contract value without a kernel */
+#define TB_ERR_SIGN        -5   /* a sign other than +-1 (host check) */
+#define TB_ERR_CODE        -6   /* ternary value outside {-1,0,1} / code 3 on unpack */
+#define TB_ERR_DTYPE       -7   /* activation dtype not TB_F32 / TB_BF16 */
+#define TB_ERR_ALIGN       -8   /* pointer not aligned as documented */
+#define TB_ERR_HIP         -9   /* the HIP runtime refused a launch */
+#define TB_ERR_WORKSPACE  -10   /* workspace NULL or smaller than required */
+
+/* activation dtypes */
+#define TB_F32  0
+#define TB_BF16 1
+
+/* largest batch the GEMV path takes (prefill batches use tb_ternary_gemm) */
+#define TB_GEMV_MAX_BATCH 8
+
+int tb_abi_version(void);
+const char* tb_last_error(void);
+const char* tb_status_str(int status);
+
+/* ---------------------------------------------------------------------------
+ * Host container functions (host pointers; no GPU involved).
+ * [P2 "packing-format engineering"]: code = t + 1 ([P1] trdm.cn/news/822023
+ * section 3.2 maps -1/0/1 to 0/1/2), 16 codes per uint32 word, bias = -scale
+ * (fp16 sign-bit flip, exact); an independent unpack() verifies packing.
+ * ------------------------------------------------------------------------ */
+
+/* Pack t (int8 [N][K], values -1/0/1) and scales (fp16 [N][K/128]) into
+ * codes (uint32 [N][K/16]), scales_out (copy) and biases_out (= -scales).
+ * K % 128 == 0.  Returns TB_ERR_CODE if any t is outside {-1,0,1}; outputs
+ * are then unspecified. */
+int tb_pack(const int8_t* t, const uint16_t* scales, int64_t N, int64_t K,
+            uint32_t* codes, uint16_t* scales_out, uint16_t* biases_out);
+
+/* Unpack codes (uint32 [N][K/16]) to t_out (int8 [N][K]) = code - 1.
+ * Returns TB_ERR_CODE if any code is 3 (t_out contents then unspecified). */
+int tb_unpack(const uint32_t* codes, int64_t N, int64_t K, int8_t* t_out);
+
+/* Load-time sign check [P3 "affine 2-bit format and Prism contract v1"]:
+ * TB_ERR_SIGN unless every signs[k] is +1 or -1.  The device entry points do
+ * not re-check signs; a value other than +-1 is used as a multiplier. */
+int tb_signs_validate(const int8_t* signs, int64_t K);
+
+/* ---------------------------------------------------------------------------
+ * Device entry points (device pointers, asynchronous on `stream`).
+ * ------------------------------------------------------------------------ */
+
+/* Device-side pack of the same container as tb_pack (for containers too large
+ * to stage on the host).  t, scales, codes, scales_out, biases_out as in
+ * tb_pack but in device memory; codes 16-byte aligned.  A value of t outside
+ * {-1,0,1} is stored as code 3 and counted into *bad_count (a device int32
+ * the caller zeroes first; required). */
+int tb_pack_device(const int8_t* t, const uint16_t* scales, int64_t N, int64_t K,
+                   uint32_t* codes, uint16_t* scales_out, uint16_t* biases_out,
+                   int32_t* bad_count, void* stream);
+
+/* Signed block transform of `rows` rows of K inputs [P3 "text model
+ * loading", P2 "ternary weights + folded Hadamard rotation"]:
+ *   inverse = 0:  y = H (signs .* x) / sqrt(block)      (forward)
+ *   inverse = 1:  y = signs .* (H x) / sqrt(block)      (inverse)
+ * x: rows x K of x_dtype (TB_F32 or TB_BF16), row-major; y: rows x K fp32.
+ * y may alias x when x is fp32.  block in {512,1024,2048,4096}, K % block == 0.
+ * x and y 4-byte aligned (x 2-byte for bf16). */
+int tb_fwht_signed(const void* x, int x_dtype, float* y, const int8_t* signs,
+                   int64_t rows, int64_t K, int block, int inverse, void* stream);
+
+/* Workspace bytes tb_ternary_gemv / _prepare / _run need for batch B and
+ * input width K (0 for invalid B or K). */
+size_t tb_ternary_gemv_workspace_size(int64_t B, int64_t K);
+
+/* Packed linear for decode batches [P3 "text model loading"]:
+ *   y[b][n] = sum_k W~[n][k] (R x[b])[k],  b < B <= TB_GEMV_MAX_BATCH.
+ * x: B x K (x_dtype), 16-byte aligned; signs 16-byte aligned; codes/scales/
+ * biases as defined above (codes 16-byte aligned); y: B x N fp32
+ * (overwritten, 4-byte aligned).  workspace: device
+ * scratch of at least tb_ternary_gemv_workspace_size(B, K) bytes, 16-byte
+ * aligned, needing no initialisation; it must not be reused by another call
+ * until this one completes on the stream.  Equivalent to
+ * tb_ternary_gemv_prepare followed by tb_ternary_gemv_run on one stream. */
+int tb_ternary_gemv(const void* x, int x_dtype, int64_t B, int64_t K,
+                    const int8_t* signs, int block,
+                    const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                    int64_t N, float* y, void* workspace, size_t ws_bytes, void* stream);
+
+/* First half of tb_ternary_gemv: rotate x (R x, signs then the normalized
+ * block transform) and store it in the workspace as exact integer limbs in
+ * the matmul kernel's operand layout (format private to the library).  One
+ * prepared workspace serves any number of tb_ternary_gemv_run calls with the
+ * same B and K -- e.g. the modules that read the same activation. */
+int tb_ternary_gemv_prepare(const void* x, int x_dtype, int64_t B, int64_t K,
+                            const int8_t* signs, int block, void* workspace, size_t ws_bytes,
+                            void* stream);
+
+/* Second half of tb_ternary_gemv: stream the packed weights against a
+ * workspace filled by tb_ternary_gemv_prepare(B, K) earlier on the stream. */
+int tb_ternary_gemv_run(const void* workspace, size_t ws_bytes, int64_t B, int64_t K,
+                        const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                        int64_t N, float* y, void* stream);
+
+/* Workspace bytes tb_ternary_gemm / _prepare / _run need for M rows of width K. */
+size_t tb_ternary_gemm_workspace_size(int64_t M, int64_t K);
+
+/* Packed linear for prefill (any M >= 1), same definition as the GEMV:
+ *   y[m][n] = sum_k W~[n][k] (R x[m])[k]   (fp32 out, M x N)
+ * Codes are expanded to exact bf16 tiles in LDS and multiplied on bf16 MFMA
+ * against a bf16 hi + lo split of the rotated activation; the per-group scale
+ * and bias are applied in fp32.  Same argument rules as tb_ternary_gemv;
+ * equivalent to tb_ternary_gemm_prepare then tb_ternary_gemm_run. */
+int tb_ternary_gemm(const void* x, int x_dtype, int64_t M, int64_t K,
+                    const int8_t* signs, int block,
+                    const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                    int64_t N, float* y, void* workspace, size_t ws_bytes, void* stream);
+
+/* Rotate the M x K activation into the workspace (bf16 hi/lo + group sums). */
+int tb_ternary_gemm_prepare(const void* x, int x_dtype, int64_t M, int64_t K,
+                            const int8_t* signs, int block, void* workspace, size_t ws_bytes,
+                            void* stream);
+
+/* Multiply a prepared workspace (same M, K) by a packed weight matrix. */
+int tb_ternary_gemm_run(const void* workspace, size_t ws_bytes, int64_t M, int64_t K,
+                        const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                        int64_t N, float* y, void* stream);
+
+/* Embedding lookup with the inverse transform [P3 "text model loading"]:
+ *   out[t] = signs .* (H_L W~[ids[t]]) / sqrt(L)   blockwise  (block > 0)
+ *   out[t] = W~[ids[t]]                                      (block = 0)
+ * ids: int32 [T] (device); table codes/scales/biases of V rows and width K;
+ * out: T x K fp32.  An id outside [0, V) yields a row of NaN (no error is
+ * returned: ids are not read on the host). */
+int tb_embed_inverse(const int32_t* ids, int64_t T,
+                     const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                     int64_t V, int64_t K, const int8_t* signs, int block,
+                     float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TB_H */

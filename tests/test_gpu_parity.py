@@ -1,0 +1,401 @@
+"""Parity of the HIP path against the fp64 oracle on the GPU.
+
+Bars: relative L2 <= 1e-4 and max |err| <= 1e-3 * max |y| for floating point
+results; bit-exact for packing and for code decoding (one-hot inputs through
+the unrotated GEMV, and unrotated embedding rows)."""
+import numpy as np
+import pytest
+
+import hadamard_rotated_quantized_amd as tb
+import oracle
+from hadamard_rotated_quantized_amd import synth
+from gpu_util import (announce, compare, cuda_available, oracle_pack, pack_to_device, signs_to_device,
+                      torch, x_to_device)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not cuda_available(), reason="needs a GPU")]
+
+
+def _gemv_case(p, B=None):
+    T = torch()
+    codes, s, b = pack_to_device(p.t, p.scales)
+    x = x_to_device(p)
+    sg = signs_to_device(p.signs)
+    y = tb.tb_ternary_gemv(x, sg, p.block, codes, s, b)
+    T.cuda.synchronize()
+    oc, osc, ob = oracle_pack(p)
+    want = oracle.packed_linear(p.x64, p.signs, p.block, oc, osc, ob)
+    return y.cpu().numpy(), want
+
+
+# --------------------------------------------------------------------------
+# the named workloads
+# --------------------------------------------------------------------------
+def test_tiny_packed_linear():
+    announce("tiny K=1024 N=256 B=1 fp32 seed 0")
+    p = synth.config_problem("tiny")
+    got, want = _gemv_case(p)
+    compare(got, want, "tiny")
+
+
+def test_q_proj_gemv():
+    announce("q_proj K=5120 N=6144 B=1 bf16 seed 2")
+    p = synth.config_problem("q_proj")
+    got, want = _gemv_case(p)
+    compare(got, want, "q_proj")
+
+
+def test_down_proj_gemv_batches():
+    announce("down_proj K=17408 N=5120 B=1/2/4/8 bf16 seed 3")
+    T = torch()
+    p = synth.config_problem("down_proj")
+    codes, s, b = pack_to_device(p.t, p.scales)
+    sg = signs_to_device(p.signs)
+    x8 = x_to_device(p)
+    oc, osc, ob = oracle_pack(p)
+    want = oracle.packed_linear(p.x64, p.signs, 1024, oc, osc, ob)  # rows are independent
+    for B in (1, 2, 4, 8):
+        announce(f"down_proj B={B}")
+        y = tb.tb_ternary_gemv(x8[:B].contiguous(), sg, 1024, codes, s, b)
+        T.cuda.synchronize()
+        compare(y.cpu().numpy(), want[:B], f"down_proj B={B}")
+
+
+def test_prefill_gemm_sampled_rows():
+    announce("prefill_gate_up M=2048 K=5120 N=17408 bf16 seed 4 (sampled rows)")
+    T = torch()
+    p = synth.config_problem("prefill_gate_up")
+    codes, s, b = pack_to_device(p.t, p.scales)
+    x = x_to_device(p)
+    sg = signs_to_device(p.signs)
+    y = tb.tb_ternary_gemm(x, sg, 1024, codes, s, b)
+    T.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 1023, 2047],
+                                     np.random.default_rng(44).integers(0, 2048, 26)]))
+    oc, osc, ob = oracle_pack(p)
+    want = oracle.packed_linear(p.x64[rows], p.signs, 1024, oc, osc, ob)
+    got = y[T.from_numpy(rows).cuda()].cpu().numpy()
+    compare(got, want, "prefill sampled rows")
+
+
+# --------------------------------------------------------------------------
+# ragged shapes, other block sizes, batches, dtypes
+# --------------------------------------------------------------------------
+RAGGED = [
+    # (N, K, B, block, xdtype)
+    (1, 1024, 1, 1024, "bf16"),
+    (17, 2048, 3, 512, "f32"),
+    (1000, 6144, 2, 2048, "bf16"),
+    (100, 8192, 5, 4096, "bf16"),
+    (45, 384, 1, 0, "f32"),       # 3 groups: partial super-span
+    (300, 640, 7, 0, "bf16"),     # 5 groups
+    (4099, 1024, 8, 1024, "f32"),
+    (16, 5120, 6, 1024, "bf16"),
+]
+
+
+@pytest.mark.parametrize("N,K,B,block,xd", RAGGED)
+def test_gemv_ragged(N, K, B, block, xd):
+    announce(f"gemv ragged N={N} K={K} B={B} block={block} x={xd}")
+    p = synth.make_problem("ragged", N, K, B, [N, K, B, block], xd, block)
+    got, want = _gemv_case(p)
+    compare(got, want, f"gemv N={N} K={K} B={B} block={block}")
+
+
+GEMM_CASES = [
+    (200, 300, 2048, 1024, "bf16"),
+    (1, 77, 1024, 512, "f32"),
+    (129, 129, 4096, 4096, "bf16"),
+    (64, 256, 384, 0, "f32"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,block,xd", GEMM_CASES)
+def test_gemm_small_full(M, N, K, block, xd):
+    announce(f"gemm M={M} N={N} K={K} block={block} x={xd}")
+    T = torch()
+    p = synth.make_problem("gemm", N, K, M, [M, N, K, block, 9], xd, block)
+    codes, s, b = pack_to_device(p.t, p.scales)
+    y = tb.tb_ternary_gemm(x_to_device(p), signs_to_device(p.signs), block, codes, s, b)
+    T.cuda.synchronize()
+    oc, osc, ob = oracle_pack(p)
+    want = oracle.packed_linear(p.x64, p.signs, block, oc, osc, ob)
+    compare(y.cpu().numpy(), want, f"gemm M={M} N={N} K={K}")
+
+
+# --------------------------------------------------------------------------
+# exact decode, general affine decode, degenerate cases
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("xd", ["f32", "bf16"])
+def test_gemv_one_hot_decode_is_exact(xd):
+    """Unrotated GEMV with x = e_k returns column k of W~ exactly."""
+    announce(f"gemv one-hot decode x={xd}")
+    T = torch()
+    N, K = 300, 1024
+    rng = np.random.default_rng(7)
+    t = synth.draw_ternary(rng, N, K)
+    sc = synth.draw_scales(rng, N, K)
+    codes, s, b = pack_to_device(t, sc)
+    oc, osc, ob = oracle.pack(t, sc)
+    W = oracle.dequantize(oc, osc, ob, K)
+    ks = [0, 1, 5, 15, 16, 127, 128, 511, 512, 1023]
+    dt = T.float32 if xd == "f32" else T.bfloat16
+    x = T.zeros((len(ks), K), dtype=dt)
+    for i, k in enumerate(ks):
+        x[i, k] = 1
+    xs = x.cuda()
+    for i0 in range(0, len(ks), 8):
+        y = tb.tb_ternary_gemv(xs[i0:i0 + 8].contiguous(), None, 0, codes, s, b)
+        T.cuda.synchronize()
+        for j, k in enumerate(ks[i0:i0 + 8]):
+            np.testing.assert_array_equal(y[j].cpu().numpy(), W[:, k].astype(np.float32))
+
+
+def test_gemv_general_bias_and_code3():
+    """Stored biases unrelated to the scales, and code 3 present: the kernel
+    decodes s*c + b from storage and does not assume b = -s."""
+    announce("gemv general affine decode")
+    T = torch()
+    N, K, B = 513, 3072, 3
+    rng = np.random.default_rng(8)
+    words = rng.integers(0, 2 ** 32, size=(N, K // 16), dtype=np.uint64).astype(np.uint32)
+    sc = (rng.standard_normal((N, K // 128)) * 0.05).astype(np.float16)
+    bi = (rng.standard_normal((N, K // 128)) * 0.05).astype(np.float16)
+    sig = synth.draw_signs(rng, K)
+    x64, xs = synth.draw_activations(rng, B, K, "bf16")
+    y = tb.tb_ternary_gemv(T.from_numpy(xs.view(np.int16)).view(T.bfloat16).cuda(),
+                           T.from_numpy(sig).cuda(), 1024, T.from_numpy(words.view(np.int32)).cuda(),
+                           T.from_numpy(sc).cuda(), T.from_numpy(bi).cuda())
+    T.cuda.synchronize()
+    want = oracle.packed_linear(x64, sig, 1024, words, sc, bi)
+    compare(y.cpu().numpy(), want, "general affine")
+    # the same container through the GEMM
+    yg = tb.tb_ternary_gemm(T.from_numpy(xs.view(np.int16)).view(T.bfloat16).cuda(),
+                            T.from_numpy(sig).cuda(), 1024, T.from_numpy(words.view(np.int32)).cuda(),
+                            T.from_numpy(sc).cuda(), T.from_numpy(bi).cuda())
+    T.cuda.synchronize()
+    compare(yg.cpu().numpy(), want, "general affine gemm")
+
+
+def test_gemv_zero_weights_give_zero():
+    """All ternary zeros (W~ = 0): the per-group factorization s*sum(c x) +
+    b*sum(x) cancels up to fp32 rounding of the two group terms, so |y| is
+    bounded by 1e-6 * max(s) * sum|xr| (exact zero is not promised)."""
+    announce("gemv all-zero ternary")
+    T = torch()
+    N, K = 77, 2048
+    rng = np.random.default_rng(9)
+    sc = synth.draw_scales(rng, N, K)
+    codes, s, b = pack_to_device(np.zeros((N, K), np.int8), sc)
+    sig = synth.draw_signs(rng, K)
+    x64, xs = synth.draw_activations(rng, 4, K, "bf16")
+    y = tb.tb_ternary_gemv(T.from_numpy(xs.view(np.int16)).view(T.bfloat16).cuda(), signs_to_device(sig),
+                           1024, codes, s, b)
+    T.cuda.synchronize()
+    xr = oracle.fwht_signed(x64, sig, 1024)
+    bound = 1e-6 * float(sc.astype(np.float64).max()) * np.abs(xr).sum(axis=1)
+    assert (np.abs(y.cpu().numpy()).max(axis=1) <= bound).all()
+
+
+def test_gemv_batch_rows_match_single_rows():
+    """Row b of a batched call equals the call on x[b] alone.  Batch sizes
+    that share a kernel configuration ({2, 3, 4} and {5, ..., 8}) give
+    bitwise-identical rows; across configurations (batch 1 runs a different
+    MFMA shape) rows agree within 1e-6 relative."""
+    announce("gemv batch consistency")
+    T = torch()
+    p = synth.make_problem("batch", 700, 5120, 8, 31, "bf16", 1024)
+    codes, s, b = pack_to_device(p.t, p.scales)
+    x = x_to_device(p)
+    sg = signs_to_device(p.signs)
+    y = {B: tb.tb_ternary_gemv(x[:B].contiguous(), sg, 1024, codes, s, b) for B in range(1, 9)}
+    T.cuda.synchronize()
+    for B in (3, 4):
+        assert T.equal(y[B][:2], y[2]), B
+    for B in (6, 7, 8):
+        assert T.equal(y[B][:5], y[5]), B
+    for i in range(8):
+        y1 = tb.tb_ternary_gemv(x[i:i + 1].contiguous(), sg, 1024, codes, s, b)
+        T.cuda.synchronize()
+        d = (y1[0].double() - y[8][i].double()).abs().max().item()
+        assert d <= 1e-6 * y1[0].abs().max().item(), (i, d)
+
+
+def test_gemv_linearity():
+    announce("gemv linearity")
+    T = torch()
+    p = synth.make_problem("lin", 256, 2048, 2, 32, "f32", 1024)
+    codes, s, b = pack_to_device(p.t, p.scales)
+    x = x_to_device(p)
+    sg = signs_to_device(p.signs)
+    y = tb.tb_ternary_gemv(x, sg, 1024, codes, s, b)
+    z = tb.tb_ternary_gemv((2.5 * x[0:1] - 0.5 * x[1:2]).contiguous(), sg, 1024, codes, s, b)
+    T.cuda.synchronize()
+    want = 2.5 * y[0].double() - 0.5 * y[1].double()
+    err = (z[0].double() - want).abs().max().item()
+    assert err <= 1e-5 * want.abs().max().item()
+
+
+def test_gemv_writes_only_its_output():
+    announce("gemv output bounds")
+    T = torch()
+    p = synth.make_problem("bounds", 33, 1024, 2, 33, "bf16", 1024)
+    codes, s, b = pack_to_device(p.t, p.scales)
+    out = T.full((2 * 33 + 64,), 12345.0, device="cuda")
+    y = out[:66].view(2, 33)
+    tb.tb_ternary_gemv(x_to_device(p), signs_to_device(p.signs), 1024, codes, s, b, out=y)
+    T.cuda.synchronize()
+    assert (out[66:] == 12345.0).all()
+
+
+# --------------------------------------------------------------------------
+# standalone transform
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("block", [512, 1024, 2048, 4096])
+def test_fwht_matches_oracle_and_inverts(block):
+    announce(f"fwht block={block}")
+    T = torch()
+    rng = np.random.default_rng(block)
+    K = 2 * block if block < 4096 else 8192
+    rows = 5
+    x = rng.standard_normal((rows, K)).astype(np.float32)
+    sig = synth.draw_signs(rng, K)
+    xd = T.from_numpy(x).cuda()
+    sd = T.from_numpy(sig).cuda()
+    y = tb.tb_fwht_signed(xd, sd, block)
+    back = tb.tb_fwht_signed(y, sd, block, inverse=True)
+    T.cuda.synchronize()
+    want = oracle.fwht_signed(x.astype(np.float64), sig, block)
+    np.testing.assert_allclose(y.cpu().numpy(), want, rtol=0, atol=2e-6 * np.abs(want).max())
+    np.testing.assert_allclose(back.cpu().numpy(), x, rtol=0, atol=2e-6 * np.abs(x).max())
+    wi = oracle.fwht_signed(x.astype(np.float64), sig, block, inverse=True)
+    yi = tb.tb_fwht_signed(xd, sd, block, inverse=True)
+    xb = xd.clone()
+    tb.tb_fwht_signed(xb, sd, block, out=xb)  # in place
+    T.cuda.synchronize()
+    np.testing.assert_allclose(yi.cpu().numpy(), wi, rtol=0, atol=2e-6 * np.abs(wi).max())
+    assert T.equal(xb, y)
+
+
+def test_fwht_bf16_input():
+    announce("fwht bf16")
+    T = torch()
+    rng = np.random.default_rng(5)
+    x64, xs = synth.draw_activations(rng, 3, 5120, "bf16")
+    sig = synth.draw_signs(rng, 5120)
+    y = tb.tb_fwht_signed(T.from_numpy(xs.view(np.int16)).view(T.bfloat16).cuda(), T.from_numpy(sig).cuda(),
+                          1024)
+    T.cuda.synchronize()
+    want = oracle.fwht_signed(x64, sig, 1024)
+    np.testing.assert_allclose(y.cpu().numpy(), want, rtol=0, atol=2e-6 * np.abs(want).max())
+
+
+# --------------------------------------------------------------------------
+# embedding
+# --------------------------------------------------------------------------
+def test_embed_inverse_parity_and_invalid_ids():
+    announce("embed V=1000 K=5120")
+    T = torch()
+    V, K = 1000, 5120
+    rng = np.random.default_rng(10)
+    t = synth.draw_ternary(rng, V, K)
+    sc = synth.draw_scales(rng, V, K)
+    sig = synth.draw_signs(rng, K)
+    codes, s, b = pack_to_device(t, sc)
+    ids = np.array([0, V - 1, 17, 17, -1, V, 512, 2 ** 31 - 1], np.int32)
+    out = tb.tb_embed_inverse(T.from_numpy(ids).cuda(), codes, s, b, signs_to_device(sig), 1024)
+    T.cuda.synchronize()
+    oc, osc, ob = oracle.pack(t, sc)
+    want = oracle.embed_inverse(ids, oc, osc, ob, sig, 1024)
+    got = out.cpu().numpy()
+    ok = (ids >= 0) & (ids < V)
+    assert np.isnan(got[~ok]).all()
+    compare(got[ok], want[ok], "embed")
+
+
+def test_embed_unrotated_decode_is_exact():
+    announce("embed block 0 exact decode")
+    T = torch()
+    V, K = 64, 640
+    rng = np.random.default_rng(11)
+    t = synth.draw_ternary(rng, V, K)
+    sc = synth.draw_scales(rng, V, K)
+    codes, s, b = pack_to_device(t, sc)
+    ids = np.arange(V, dtype=np.int32)[::-1].copy()
+    out = tb.tb_embed_inverse(T.from_numpy(ids).cuda(), codes, s, b, None, 0)
+    T.cuda.synchronize()
+    oc, osc, ob = oracle.pack(t, sc)
+    np.testing.assert_array_equal(out.cpu().numpy(),
+                                  oracle.dequantize_rows(oc, osc, ob, K, ids).astype(np.float32))
+
+
+def test_embed_gemv_duality():
+    """<embed(r), x> == gemv(x)[r] for the same pack and signs."""
+    announce("embed/gemv duality")
+    T = torch()
+    V, K = 96, 5120
+    rng = np.random.default_rng(12)
+    t = synth.draw_ternary(rng, V, K)
+    sc = synth.draw_scales(rng, V, K)
+    sig = synth.draw_signs(rng, K)
+    codes, s, b = pack_to_device(t, sc)
+    sd = signs_to_device(sig)
+    x64, xs = synth.draw_activations(rng, 1, K, "f32")
+    x = T.from_numpy(xs).cuda()
+    y = tb.tb_ternary_gemv(x, sd, 1024, codes, s, b)[0].double()
+    e = tb.tb_embed_inverse(T.arange(V, dtype=T.int32).cuda(), codes, s, b, sd, 1024).double()
+    T.cuda.synchronize()
+    d = e @ x[0].double()
+    assert (d - y).abs().max().item() <= 1e-4 * y.abs().max().item()
+
+
+# --------------------------------------------------------------------------
+# device packer
+# --------------------------------------------------------------------------
+def test_pack_device_matches_host_pack():
+    announce("pack_device")
+    T = torch()
+    N, K = 333, 5120
+    rng = np.random.default_rng(13)
+    t = synth.draw_ternary(rng, N, K)
+    sc = synth.draw_scales(rng, N, K)
+    c, s, b = tb.tb_pack_device(T.from_numpy(t).cuda(), T.from_numpy(sc).cuda())
+    T.cuda.synchronize()
+    hc, hs, hb = tb.tb_pack(t, sc)
+    np.testing.assert_array_equal(c.cpu().numpy().view(np.uint32), hc)
+    np.testing.assert_array_equal(s.cpu().numpy().view(np.uint16), hs.view(np.uint16))
+    np.testing.assert_array_equal(b.cpu().numpy().view(np.uint16), hb.view(np.uint16))
+    t[5, 9] = 3
+    t[300, 0] = -2
+    with pytest.raises(tb.TBError):
+        tb.tb_pack_device(T.from_numpy(t).cuda(), T.from_numpy(sc).cuda())
+
+
+# --------------------------------------------------------------------------
+# graph capture of the step (prepare + run)
+# --------------------------------------------------------------------------
+def test_gemv_graph_replays_match_eager():
+    """Capture prepare + run in a HIP graph, replay it several times with
+    eager work in between, and compare every replay bitwise with the eager
+    result (the kernels are deterministic)."""
+    announce("gemv graph replay")
+    T = torch()
+    p = synth.make_problem("graph", 1000, 5120, 2, 41, "bf16", 1024)
+    codes, s, b = pack_to_device(p.t, p.scales)
+    x = x_to_device(p)
+    sg = signs_to_device(p.signs)
+    ws = tb.tb_ternary_gemv_prepare(x, sg, 1024)
+    eager = tb.tb_ternary_gemv_run(ws, 2, 5120, codes, s, b)
+    T.cuda.synchronize()
+    y = T.empty_like(eager)
+    g = T.cuda.CUDAGraph()
+    with T.cuda.graph(g):
+        tb.tb_ternary_gemv_prepare(x, sg, 1024, ws)
+        tb.tb_ternary_gemv_run(ws, 2, 5120, codes, s, b, out=y)
+    for i in range(4):
+        y.fill_(float("nan"))
+        g.replay()
+        T.cuda.synchronize()
+        assert T.equal(y, eager), i
+        tb.tb_ternary_gemv(x, sg, 1024, codes, s, b)  # eager work between replays
+        T.cuda.synchronize()
