@@ -31,6 +31,9 @@ FLAGS = [
     "-Wall",
     # never emit packed fp32 VALU ops (v_pk_add/mul/fma_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the first 16 SGPRs of kernel arguments arrive preloaded (no fetch on
+    # the critical path of short kernels)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -10,12 +10,15 @@
 //
 // which is sum_k (s c + b) xr, i.e. W~ xr, regrouped per 128-weight group.
 //
-// Design for gfx950 (the weight stream is the cost: 9/32 byte per weight):
+// Design for gfx950 (the weight stream is the cost: 9/32 byte per weight).
+// tb_ternary_gemv runs the single-launch kernel of tb_gemv_fused.hip when a
+// workgroup can afford to transform the input itself (short inputs, small
+// batches); otherwise, and always for the prepare/run pair, two kernels:
 //
 // 1. gemv_prep_kernel: one wave per 1024 inputs of one batch row.  Lane l
 //    holds inputs 16 l .. 16 l + 15 of the chunk in registers: the transform
-//    runs as 4 in-lane butterfly stages and 6 cross-lane stages (shuffles),
-//    with no LDS and no barrier.  The fp32 result is then split exactly into
+//    runs as 4 in-lane butterfly stages and 6 cross-lane stages (DPP and
+//    permlane exchanges), with no LDS and no barrier.  The fp32 result is then split exactly into
 //    integers: per group of 128 inputs (8 lanes), xr ~= f * q with f = 2^E
 //    chosen so |q| <= 2^22 (rounding error below 2^-22 of the group's
 //    largest |xr|), and q = h*2^16 + m*2^8 + l with balanced digits h, m, l
@@ -45,30 +48,12 @@
 //    flight while a span computes; the lane groups and waves are reduced at
 //    the end and y is written once (no atomics).
 #include <algorithm>
-#include <type_traits>
 
-#include "tb_device.h"
+#include "tb_gemv.h"
 
 namespace tb {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
-typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-typedef unsigned int v2u __attribute__((ext_vector_type(2)));
-
-constexpr int kLimbs = 3;
-constexpr int kWordsPerGroup = kGroup / kCodesPerWord;  // 8
-constexpr int kGroupPad = 4;                            // groups padded to a multiple of 4
-// bytes of prepared A operand per (batch row, group): 3 limbs x 8 words x 16 B
-constexpr int64_t kAopsGroupBytes = (int64_t)kLimbs * kWordsPerGroup * 16;  // 384
-constexpr int kLdsBudget = 96 * 1024;   // LDS bytes for one window of limbs
-constexpr int kRsrcWord3 = 0x00020000;  // buffer resource word 3 for gfx9-family raw buffers
-constexpr int kOob = 0x7FFFFFF0;        // a buffer offset past any size: loads return 0
-
 static inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
-static inline int64_t padded_groups(int64_t K) {
-  return (K / kGroup + kGroupPad - 1) / kGroupPad * kGroupPad;
-}
 
 struct GemvWs {
   int64_t aops_off, xg_off, total;
@@ -83,13 +68,6 @@ static inline GemvWs gemv_ws_layout(int64_t B, int64_t K) {
   w.xg_off = align256(B * padded_groups(K) * kAopsGroupBytes);
   w.total = w.xg_off + align256(B * G * (int64_t)sizeof(float2));
   return w;
-}
-
-// Limb byte r of q (balanced base-256 digits): q = h*65536 + m*256 + l.
-__device__ __forceinline__ uint32_t limb_byte(int q, int r) {
-  if (r == 0) return static_cast<uint32_t>(q) & 0xFFu;
-  if (r == 1) return static_cast<uint32_t>((q + 128) >> 8) & 0xFFu;
-  return static_cast<uint32_t>((q + 32896) >> 16) & 0xFFu;
 }
 
 // Load 16 consecutive activations (16-element aligned) as fp32.
@@ -115,39 +93,6 @@ __device__ __forceinline__ void load16(const void* x, int64_t i0, float v[16]) {
       }
     }
   }
-}
-
-// Value of lane l ^ 2^j, with VALU lane exchanges only (no LDS round trip):
-// DPP quad permutations for j = 0, 1; DPP row shifts with bank masks for
-// j = 2, 3 (the banks whose partner is 4 or 8 lanes up read row_shl, the
-// others row_shr); gfx950's permlane16/32 swaps for j = 4, 5 (each swap
-// hands one half of the lanes its partner's value in each output).
-__device__ __forceinline__ float xor_lane(float v, int j, int lane) {
-  const int vi = __float_as_int(v);
-  int p;
-  switch (j) {
-    case 0: p = __builtin_amdgcn_mov_dpp(vi, 0xB1, 0xF, 0xF, false); break;  // quad_perm [1,0,3,2]
-    case 1: p = __builtin_amdgcn_mov_dpp(vi, 0x4E, 0xF, 0xF, false); break;  // quad_perm [2,3,0,1]
-    case 2:
-      p = __builtin_amdgcn_update_dpp(0, vi, 0x104, 0xF, 0x5, false);        // row_shl:4, banks 0, 2
-      p = __builtin_amdgcn_update_dpp(p, vi, 0x114, 0xF, 0xA, false);        // row_shr:4, banks 1, 3
-      break;
-    case 3:
-      p = __builtin_amdgcn_update_dpp(0, vi, 0x108, 0xF, 0x3, false);        // row_shl:8, banks 0, 1
-      p = __builtin_amdgcn_update_dpp(p, vi, 0x118, 0xF, 0xC, false);        // row_shr:8, banks 2, 3
-      break;
-    case 4: {
-      const auto r = __builtin_amdgcn_permlane16_swap(vi, vi, false, false);
-      p = (lane & 16) ? static_cast<int>(r[0]) : static_cast<int>(r[1]);
-      break;
-    }
-    default: {
-      const auto r = __builtin_amdgcn_permlane32_swap(vi, vi, false, false);
-      p = (lane & 32) ? static_cast<int>(r[0]) : static_cast<int>(r[1]);
-      break;
-    }
-  }
-  return __int_as_float(p);
 }
 
 // One wave per CH-input chunk of one batch row (CH = max(L, 1024); block 0
@@ -197,28 +142,10 @@ __global__ __launch_bounds__(kThreads) void gemv_prep_kernel(const void* __restr
 
   float sc = 1.f;
   if constexpr (L > 0) {
-    // Sylvester butterflies, natural order [trdm.cn/news/822023 section 2.2]:
-    // index bits 0-3 live in r, bits 4-9 in the lane id, bits 10+ in u.
+    // index bits 0-9 of a 1024 sub-chunk: in-lane and lane bits; bits 10+
+    // of a larger block: u
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-#pragma unroll
-      for (int hb = 1; hb < 16; hb <<= 1)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (!(r & hb)) {
-            const float a0 = v[u][r], a1 = v[u][r + hb];
-            v[u][r] = a0 + a1;
-            v[u][r + hb] = a0 - a1;
-          }
-      constexpr int XSTAGES = (L == 512) ? 5 : 6;  // 512-blocks: each lane half is one block
-#pragma unroll
-      for (int j = 0; j < XSTAGES; ++j) {
-        // butterfly with lane l ^ 2^j: lower lane v + p, upper lane p - v
-        const float sgn = ((lane >> j) & 1) ? -1.f : 1.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) v[u][r] = fmaf(sgn, v[u][r], xor_lane(v[u][r], j, lane));
-      }
-    }
+    for (int u = 0; u < U; ++u) fwht_lane16<(L == 512) ? 5 : 6>(v[u], lane);
 #pragma unroll
     for (int hu = 1; hu < U; hu <<= 1)
 #pragma unroll
@@ -235,72 +162,19 @@ __global__ __launch_bounds__(kThreads) void gemv_prep_kernel(const void* __restr
 
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    float m = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      v[u][r] *= sc;
-      m = fmaxf(m, fabsf(v[u][r]));
-    }
-    // group of 128 inputs = 8 consecutive lanes
-    m = fmaxf(m, __shfl_xor(m, 1));
-    m = fmaxf(m, __shfl_xor(m, 2));
-    m = fmaxf(m, __shfl_xor(m, 4));
-    const int E = (m > 0.f) ? ilogbf(m) - 21 : 0;
-    int q[16];
-    int qs = 0;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      q[r] = static_cast<int>(rintf(ldexpf(v[u][r], -E)));
-      qs += q[r];
-    }
-    qs += __shfl_xor(qs, 1);
-    qs += __shfl_xor(qs, 2);
-    qs += __shfl_xor(qs, 4);
+    for (int r = 0; r < 16; ++r) v[u][r] *= sc;
+    uint4 limb[kLimbs];
+    float2 xf;
+    split_limbs(v[u], lane, limb, xf);
     if (!ok[u]) continue;
     const int64_t g = (k0 + 1024 * u) / kGroup + (lane >> 3);
     const int t = lane & 7;
-    if (t == 0) {
-      const float f = ldexpf(1.f, E);
-      xg[b * G + g] = make_float2(f * static_cast<float>(qs), f);
-    }
-    // dword d of the operand carries, in byte j, element d + 4 j of the word:
-    // the order (w >> 2d) & 0x03030303 gives the codes in the main kernel.
+    if (t == 0) xg[b * G + g] = xf;
 #pragma unroll
-    for (int limb = 0; limb < kLimbs; ++limb) {
-      uint32_t dw[4];
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-        dw[d] = limb_byte(q[d], limb) | (limb_byte(q[d + 4], limb) << 8) |
-                (limb_byte(q[d + 8], limb) << 16) | (limb_byte(q[d + 12], limb) << 24);
-      aops[((b * Gp + g) * kLimbs + limb) * kWordsPerGroup + t] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
-    }
+    for (int l = 0; l < kLimbs; ++l) aops[((b * Gp + g) * kLimbs + l) * kWordsPerGroup + t] = limb[l];
   }
 }
-
-__device__ __forceinline__ v4i decode_word(uint32_t w) {
-  v4i r;
-  r[0] = static_cast<int>(w & 0x03030303u);
-  r[1] = static_cast<int>((w >> 2) & 0x03030303u);
-  r[2] = static_cast<int>((w >> 4) & 0x03030303u);
-  r[3] = static_cast<int>((w >> 6) & 0x03030303u);
-  return r;
-}
-
-// Shapes of the two MFMA variants.
-//   M = 16: v_mfma_i32_16x16x64_i8, 4 lane groups of 16 lanes, one batch row
-//           per instruction, 4 groups per span, A row i = 4 lg + r.
-//   M = 32: v_mfma_i32_32x32x32_i8, 2 lane halves of 32 lanes, 4 batch rows
-//           per instruction, 2 groups per span, A row i = 8 j + 4 lg + r.
-template <int M>
-struct Mfma {
-  static constexpr int GPS = 64 / M;         // groups per span = lane groups
-  static constexpr int BPI = M / (4 * GPS);  // batch rows per instruction
-  using acc_t = typename std::conditional<M == 16, v4i, v16i>::type;
-  __device__ static acc_t mac(v4i a, v4i b, acc_t c) {
-    if constexpr (M == 16) return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
-    else return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
-  }
-};
 
 // One module of a (possibly multi-module) matmul launch.
 struct ModDesc {
@@ -331,11 +205,6 @@ struct Span {
   float2 xf[NB];
   v4i a[AG ? NBC : 1][AG ? kWordsPerGroup : 1];
 };
-
-// LDS layout of the limbs: one 144-byte row (8 x 16 B + 16 B pad) per
-// (batch row, group, limb), so the 16-byte reads of the active A lanes (128,
-// 384 or 768 bytes apart in the dense layout) land on distinct banks.
-constexpr int kLdsRow = kWordsPerGroup + 1;  // uint4 per (batch, group, limb) row
 
 __host__ __device__ constexpr int64_t lds_limb_bytes(int nb, int64_t gp) {
   return (int64_t)nb * gp * kLimbs * kLdsRow * 16;
@@ -835,6 +704,11 @@ extern "C" int tb_ternary_gemv(const void* x, int x_dtype, int64_t B, int64_t K,
   TB_TRY(run_checks(N, K, codes, scales, biases, y, who));
   TB_TRY(gemv_ws_check(workspace, ws_bytes, B, K, who));
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (gemv_fused_eligible(B, K, N, block)) {
+    gemv_fused_launch(x, x_dtype, B, K, signs, block, codes, scales, biases, N, y, st);
+    TB_LAUNCH_CHECK(who);
+    return TB_OK;
+  }
   gemv_prepare_launch(x, x_dtype, B, K, signs, block, workspace, st);
   TB_LAUNCH_CHECK(who);
   gemv_run_launch(workspace, B, K, codes, scales, biases, N, y, st);

@@ -399,3 +399,81 @@ def test_gemv_graph_replays_match_eager():
         assert T.equal(y, eager), i
         tb.tb_ternary_gemv(x, sg, 1024, codes, s, b)  # eager work between replays
         T.cuda.synchronize()
+
+
+# --------------------------------------------------------------------------
+# the single-launch path (tb_ternary_gemv on short inputs) against the
+# oracle and against the two-kernel prepare/run path on the same inputs
+# --------------------------------------------------------------------------
+TWO_PATHS = [
+    # (N, K, B, block, xdtype)
+    (6144, 5120, 1, 1024, "bf16"),   # the q_proj shape
+    (777, 17408, 1, 1024, "bf16"),   # 17 chunks: three transforms on wave 0
+    (1000, 3072, 8, 1024, "bf16"),   # 24 chunk transforms: three per wave
+    (333, 1024, 4, 512, "f32"),
+    (250, 2304, 3, 0, "bf16"),       # partial last chunk, 18 groups (2 padding)
+    (5000, 640, 2, 0, "f32"),
+    (9000, 1024, 1, 1024, "bf16"),   # 563 tiles: 4 waves per tile
+]
+
+
+@pytest.mark.parametrize("N,K,B,block,xd", TWO_PATHS)
+def test_gemv_single_launch_matches_oracle_and_two_kernel_path(N, K, B, block, xd):
+    announce(f"gemv one call vs prepare/run N={N} K={K} B={B} block={block} x={xd}")
+    T = torch()
+    p = synth.make_problem("paths", N, K, B, [N, K, B, block, 3], xd, block)
+    codes, s, b = pack_to_device(p.t, p.scales)
+    x = x_to_device(p)
+    sg = signs_to_device(p.signs)
+    y1 = tb.tb_ternary_gemv(x, sg, block, codes, s, b)
+    ws = tb.tb_ternary_gemv_prepare(x, sg, block)
+    y2 = tb.tb_ternary_gemv_run(ws, B, K, codes, s, b)
+    T.cuda.synchronize()
+    oc, osc, ob = oracle_pack(p)
+    want = oracle.packed_linear(p.x64, p.signs, block, oc, osc, ob)
+    compare(y1.cpu().numpy(), want, "one call")
+    compare(y2.cpu().numpy(), want, "prepare/run")
+    d = (y1.double() - y2.double()).abs().max().item()
+    assert d <= 1e-6 * y2.abs().max().item(), d
+
+
+@pytest.mark.parametrize("N,B", [(70000, 1), (140000, 4)])
+def test_gemv_wide_layer_sampled_rows(N, B):
+    """Wide layers: one wave per tile and workgroups that loop over several
+    tile groups; checked on sampled output rows, the last rows included."""
+    announce(f"gemv wide N={N} K=1024 B={B}")
+    T = torch()
+    p = synth.make_problem("wide", N, 1024, B, [N, B, 5], "bf16", 1024)
+    codes, s, b = pack_to_device(p.t, p.scales)
+    y = tb.tb_ternary_gemv(x_to_device(p), signs_to_device(p.signs), 1024, codes, s, b)
+    T.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 15, 16, 31, 32, N // 2, N - 33, N - 17, N - 1],
+                                     np.random.default_rng(N).integers(0, N, 200)]))
+    oc, osc, ob = oracle_pack(p)
+    want = oracle.packed_linear_rows(p.x64, p.signs, 1024, oc, osc, ob, rows)
+    compare(y.cpu().numpy()[:, rows], want, f"wide N={N} B={B}")
+
+
+def test_gemv_one_call_graph_replays_match_eager():
+    """The single-launch call captured in a HIP graph: every replay, with
+    eager work in between, equals the eager result bitwise."""
+    announce("gemv one-call graph replay")
+    T = torch()
+    p = synth.make_problem("graph1", 6144, 5120, 1, 43, "bf16", 1024)
+    codes, s, b = pack_to_device(p.t, p.scales)
+    x = x_to_device(p)
+    sg = signs_to_device(p.signs)
+    ws = T.empty(tb.tb_ternary_gemv_workspace_size(1, 5120), dtype=T.uint8, device="cuda")
+    eager = tb.tb_ternary_gemv(x, sg, 1024, codes, s, b, workspace=ws)
+    T.cuda.synchronize()
+    y = T.empty_like(eager)
+    g = T.cuda.CUDAGraph()
+    with T.cuda.graph(g):
+        tb.tb_ternary_gemv(x, sg, 1024, codes, s, b, out=y, workspace=ws)
+    for i in range(4):
+        y.fill_(float("nan"))
+        g.replay()
+        T.cuda.synchronize()
+        assert T.equal(y, eager), i
+        tb.tb_ternary_gemv_run(tb.tb_ternary_gemv_prepare(x, sg, 1024), 1, 5120, codes, s, b)
+        T.cuda.synchronize()
