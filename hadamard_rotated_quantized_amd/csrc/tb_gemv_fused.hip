@@ -123,12 +123,12 @@ __device__ __forceinline__ void transform_chunk(float v[16], int lane, float* sc
   }
 }
 
-// cfg: batch rows B (bits 0-3), split mode (bit 4), subtiles per workgroup
-// (bits 5-7), grid size (bits 8-31).  aux: split mode, rows per workgroup;
+// cfg: batch rows B (bits 0-3), subtiles per workgroup (bits 5-7, split
+// mode), grid size (bits 8-31).  aux: split mode, rows per workgroup;
 // persistent mode, tile groups (8 tiles of M rows).  The 14 argument SGPRs
 // the dispatcher can preload (16 user SGPRs minus the kernel-argument
 // pointer) hold everything but y, which is needed last.
-template <int NB, int M, int L, int DT>
+template <int NB, int M, int L, int DT, bool SPLIT>
 __global__ __launch_bounds__(kFusedThreads, 4) void gemv_fused_kernel(
     const void* __restrict__ x, const int8_t* __restrict__ signs, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases, int N, int K, int cfg, int aux,
@@ -141,13 +141,13 @@ __global__ __launch_bounds__(kFusedThreads, 4) void gemv_fused_kernel(
   constexpr int XW = 8 * ESZ / 2;            // dwords of 16 activations
   extern __shared__ uint4 lds_dyn[];
 
-  const int B = cfg & 15;
-  const bool split = (cfg >> 4) & 1;
+  const int B = NB == 1 ? 1 : (cfg & 15);
   const int tsub = (cfg >> 5) & 7;
   const int grid = cfg >> 8;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bid = static_cast<int>(blockIdx.x);
   const int lg = lane / M, c = lane % M;
   // A-operand role of this lane: A row c = (batch jb, group alg, limb ar) is
   // non-zero only in lane group alg == lg, for limbs 0..2.
@@ -159,10 +159,10 @@ __global__ __launch_bounds__(kFusedThreads, 4) void gemv_fused_kernel(
   const int G = K / kGroup;
   const int W = K / kCodesPerWord;
   const int Gp = (G + kGroupPad - 1) / kGroupPad * kGroupPad;
-  const int S = Gp / GPS;  // spans (items) per row band
+  const int S = Gp / GPS;  // spans per row band
   const int nch = (K + 1023) >> 10;
 
-  const FusedLds lay = fused_lds_layout(B, Gp, split ? tsub * kFusedWaves * NB * M : 0);
+  const FusedLds lay = fused_lds_layout(B, Gp, SPLIT ? tsub * kFusedWaves * NB * M : 0);
   char* const lds_base = reinterpret_cast<char*>(lds_dyn);
   uint4* const lds_zero = lds_dyn;
   uint4* const lds_a = reinterpret_cast<uint4*>(lds_base + lay.limbs);
@@ -175,13 +175,24 @@ __global__ __launch_bounds__(kFusedThreads, 4) void gemv_fused_kernel(
   const auto rxa = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(x), 0, B * K * ESZ, kRsrcWord3);
   const auto rsg = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(signs), 0, L > 0 ? K : 0, kRsrcWord3);
   const int nitems = B * nch;
+  auto item_chunk = [&](int it, int& b, int& ch) {
+    b = 0;
+    ch = it;
+    if constexpr (NB > 1) {
+      while (ch >= nch) {
+        ch -= nch;
+        ++b;
+      }
+    }
+  };
   uint32_t xr[kFusedChunksPerWave][XW];
   uint32_t sr[kFusedChunksPerWave][4];
 #pragma unroll
   for (int r = 0; r < kFusedChunksPerWave; ++r) {
     const int it = wave + kFusedWaves * r;
     if (it < nitems) {
-      const int b = it / nch, ch = it - (it / nch) * nch;
+      int b, ch;
+      item_chunk(it, b, ch);
       const int k = ch * 1024 + 16 * lane;
       const int xo = k < K ? (b * K + k) * ESZ : kOob;
 #pragma unroll
@@ -196,61 +207,66 @@ __global__ __launch_bounds__(kFusedThreads, 4) void gemv_fused_kernel(
     }
   }
 
-  // 2. weight stream.  A cursor names one item: span s of the rows of tile
-  //    `tile`.  Split mode: the workgroup's band holds tsub subtiles of M
-  //    rows; item i = tile * S + s, and wave w takes items w, w + 8, ...
-  //    Persistent mode: wave w owns tile 8 q + w of each tile group q =
-  //    blockIdx.x, + grid, ..., all S spans of it.  The refill cursor runs P
-  //    items ahead of the consume cursor; items past the end read as zero.
-  const auto rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(codes), 0, N * W * 4, kRsrcWord3);
-  const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(scales), 0, N * G * 2, kRsrcWord3);
-  const auto rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(biases), 0, N * G * 2, kRsrcWord3);
-  const int bid = static_cast<int>(blockIdx.x);
-  const int band0 = split ? bid * aux : 0;  // split mode: first row of the band
-  const int band_rows = split ? min(aux, N - band0) : 0;
-  int total;
-  if (split) {
+  // 2. weight stream.  An item is span s (GPS groups) of the M rows of a
+  //    tile.  Split mode: the workgroup owns a band of rows, tsub subtiles
+  //    of M rows; item i = t * S + s, and wave w takes items w, w + 8, ...
+  //    Persistent mode: wave w owns tile 8 t + w of each tile group t =
+  //    blockIdx.x, + grid, ..., all S spans of it.  The buffer resources
+  //    cover exactly the band (split) or the matrix (persistent), so rows
+  //    past the end read as zero; an item past the end of the wave's stream
+  //    reads from an offset past any buffer.  Only the row of the tile and
+  //    the lane group vary per lane, so an item's offsets are one add.
+  int band0 = 0, nrows = N, total;
+  if constexpr (SPLIT) {
+    band0 = bid * aux;
+    nrows = min(aux, N - band0);
     const int items = tsub * S;
     total = items > wave ? (items - wave + kFusedWaves - 1) / kFusedWaves : 0;
   } else {
     total = ((aux - 1 - bid) / grid + 1) * S;
   }
+  const auto rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(codes + (int64_t)band0 * W), 0,
+                                                    nrows * W * 4, kRsrcWord3);
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(scales + (int64_t)band0 * G), 0,
+                                                    nrows * G * 2, kRsrcWord3);
+  const auto rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(biases + (int64_t)band0 * G), 0,
+                                                    nrows * G * 2, kRsrcWord3);
+  const uint32_t lane_c = static_cast<uint32_t>(c * (W * 4) + lg * 32);
+  const uint32_t lane_s = static_cast<uint32_t>(c * (G * 2) + lg * 2);
   struct Cursor {
-    int tile, s, j;
+    int j, s, t;
   };
-  auto c_row0 = [&](const Cursor& cu) { return split ? band0 + cu.tile * M : (cu.tile * kFusedWaves + wave) * M; };
-  auto c_limit = [&](const Cursor& cu) { return split ? band_rows - cu.tile * M : N - c_row0(cu); };
+  // first row of the cursor's tile, relative to the buffer resources
+  auto tile_row = [&](const Cursor& cu) { return SPLIT ? cu.t * M : (cu.t * kFusedWaves + wave) * M; };
   auto step = [&](Cursor& cu) {
     ++cu.j;
-    if (split) {
+    if constexpr (SPLIT) {
       cu.s += kFusedWaves;
       while (cu.s >= S) {
         cu.s -= S;
-        ++cu.tile;
+        ++cu.t;
       }
     } else if (++cu.s == S) {
       cu.s = 0;
-      cu.tile += grid;
+      cu.t += grid;
     }
   };
-  Cursor first;
-  first.j = 0;
-  first.s = split ? wave : 0;
-  first.tile = split ? 0 : bid;
+  Cursor first{0, SPLIT ? wave : 0, SPLIT ? 0 : bid};
   while (first.s >= S) {
     first.s -= S;
-    ++first.tile;
+    ++first.t;
   }
   auto load_item = [&](const Cursor& cu, FusedSpan& sp) {
-    const int g = cu.s * GPS + lg;
-    const bool in = cu.j < total && c < c_limit(cu) && g < G;
-    const uint32_t row = static_cast<uint32_t>(c_row0(cu) + c);
-    const int cw = in ? static_cast<int>(row * static_cast<uint32_t>(W * 4) + g * 32) : kOob;
+    const bool live = cu.j < total;
+    const uint32_t row = static_cast<uint32_t>(tile_row(cu));
+    const uint32_t uc = live ? row * static_cast<uint32_t>(W * 4) + cu.s * (GPS * 32) : kOob;
+    const uint32_t us = live ? row * static_cast<uint32_t>(G * 2) + cu.s * (GPS * 2) : kOob;
+    const int cw = static_cast<int>(lane_c + uc);
     const v4u w0 = __builtin_amdgcn_raw_buffer_load_b128(rc, cw, 0, 0);
     const v4u w1 = __builtin_amdgcn_raw_buffer_load_b128(rc, cw + 16, 0, 0);
     sp.w0 = make_uint4(w0.x, w0.y, w0.z, w0.w);
     sp.w1 = make_uint4(w1.x, w1.y, w1.z, w1.w);
-    const int so = in ? static_cast<int>((row * static_cast<uint32_t>(G) + g) * 2) : kOob;
+    const int so = static_cast<int>(lane_s + us);
     sp.s = __builtin_amdgcn_raw_buffer_load_b16(rs, so, 0, 0);
     sp.bias = __builtin_amdgcn_raw_buffer_load_b16(rb, so, 0, 0);
   };
@@ -268,7 +284,8 @@ __global__ __launch_bounds__(kFusedThreads, 4) void gemv_fused_kernel(
   for (int r = 0; r < kFusedChunksPerWave; ++r) {
     const int it = wave + kFusedWaves * r;
     if (it < nitems) {
-      const int b = it / nch, ch = it - (it / nch) * nch;
+      int b, ch;
+      item_chunk(it, b, ch);
       float v[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -295,14 +312,19 @@ __global__ __launch_bounds__(kFusedThreads, 4) void gemv_fused_kernel(
   }
   if (tid < kWordsPerGroup) lds_zero[tid] = make_uint4(0, 0, 0, 0);
   {
-    // groups G .. Gp-1 pad the last span: their (f sum q, f) must be finite
+    // groups G .. Gp-1 pad the last span: zero limbs and (f sum q, f) make
+    // whatever their code loads return contribute nothing
     const int npad = Gp - G;
-    if (npad > 0 && tid < B * npad) {
+    for (int i = tid; i < B * npad * kLimbs * kLdsRow; i += kFusedThreads) {
+      const int b = i / (npad * kLimbs * kLdsRow), rem = i - b * (npad * kLimbs * kLdsRow);
+      lds_a[(b * Gp + G) * kLimbs * kLdsRow + rem] = make_uint4(0, 0, 0, 0);
+    }
+    if (tid < B * npad) {
       const int b = tid / npad;
       lds_xf[b * Gp + G + (tid - b * npad)] = make_float2(0.f, 0.f);
     }
   }
-  if (split) {
+  if constexpr (SPLIT) {
     for (int i = tid; i < tsub * kFusedWaves * NB * M; i += kFusedThreads) red[i] = 0.f;
   }
   __syncthreads();
@@ -314,6 +336,17 @@ __global__ __launch_bounds__(kFusedThreads, 4) void gemv_fused_kernel(
   float yacc[NB];
 #pragma unroll
   for (int bq = 0; bq < NB; ++bq) yacc[bq] = 0.f;
+  // LDS address of this lane's A operand for span 0, and its step per span
+  // (lanes whose A rows are zero read the zero row at every span)
+  const uint4* a_base[NBC];
+  int a_step[NBC];
+#pragma unroll
+  for (int bc = 0; bc < NBC; ++bc) {
+    const int bq_a = bc * BPI + ajb;
+    const bool on = a_lane && bq_a < B;
+    a_base[bc] = on ? lds_a + ((bq_a * Gp + alg) * kLimbs + ar) * kLdsRow : lds_zero;
+    a_step[bc] = on ? GPS * kLimbs * kLdsRow : 0;
+  }
   auto consume = [&](const FusedSpan& cur, int s) {
     v4i bop[kWordsPerGroup];
     bop[0] = decode_word(cur.w0.x);
@@ -325,12 +358,10 @@ __global__ __launch_bounds__(kFusedThreads, 4) void gemv_fused_kernel(
     bop[6] = decode_word(cur.w1.z);
     bop[7] = decode_word(cur.w1.w);
     const float sc = half_bits_to_float(cur.s), bi = half_bits_to_float(cur.bias);
-    const int ge = s * GPS + lg;  // group of this lane's (row, group) sums
+    const float2* xfp = lds_xf + s * GPS + lg;  // (f sum q, f) of this lane's group, batch row 0
 #pragma unroll
     for (int bc = 0; bc < NBC; ++bc) {
-      const int bq_a = bc * BPI + ajb;
-      const int ga = s * GPS + alg;
-      const uint4* ap = (a_lane && bq_a < B) ? lds_a + ((bq_a * Gp + ga) * kLimbs + ar) * kLdsRow : lds_zero;
+      const uint4* ap = a_base[bc] + s * a_step[bc];
       v4i av[kWordsPerGroup];
 #pragma unroll
       for (int t = 0; t < kWordsPerGroup; ++t) {
@@ -346,7 +377,7 @@ __global__ __launch_bounds__(kFusedThreads, 4) void gemv_fused_kernel(
       }
       const typename MF::acc_t acc = acc0 + acc1;
       // lane (lg, c) holds D[(4 GPS) j + 4 lg + r][c]: the limb-r sums of
-      // row c, group ge, batch row BPI bc + j  (register 4 j + r)
+      // row c, group s GPS + lg, batch row BPI bc + j  (register 4 j + r)
 #pragma unroll
       for (int jj = 0; jj < BPI; ++jj) {
         const int bq = bc * BPI + jj;
@@ -354,7 +385,7 @@ __global__ __launch_bounds__(kFusedThreads, 4) void gemv_fused_kernel(
           // limb 0 = low digit l, limb 1 = m, limb 2 = high digit h
           const float v = static_cast<float>(acc[4 * jj + 2]) * 65536.f +
                           static_cast<float>(acc[4 * jj + 1]) * 256.f + static_cast<float>(acc[4 * jj]);
-          const float2 xf = lds_xf[bq * Gp + ge];
+          const float2 xf = xfp[bq * Gp];
           yacc[bq] += sc * (v * xf.y) + bi * xf.x;
         }
       }
@@ -374,17 +405,16 @@ __global__ __launch_bounds__(kFusedThreads, 4) void gemv_fused_kernel(
         consume(ring[sl], ccur.s);
         Cursor nxt = ccur;
         step(nxt);
-        if (nxt.j >= total || nxt.tile != ccur.tile) {
+        if (nxt.j >= total || nxt.t != ccur.t) {
           // this wave is done with the tile: split mode parks its partial
           // sums, persistent mode stores the rows it owns
-          const int row0 = c_row0(ccur);
-          const int lim = c_limit(ccur);
+          const int row0 = tile_row(ccur);
 #pragma unroll
           for (int bq = 0; bq < NB; ++bq) {
             const float v = lane_group_sum(yacc[bq]);
             if (lg == 0 && bq < B) {
-              if (split) red[((ccur.tile * kFusedWaves + wave) * NB + bq) * M + c] = v;
-              else if (c < lim) y[(int64_t)bq * N + row0 + c] = v;
+              if constexpr (SPLIT) red[((ccur.t * kFusedWaves + wave) * NB + bq) * M + c] = v;
+              else if (row0 + c < N) y[(int64_t)bq * N + row0 + c] = v;
             }
             yacc[bq] = 0.f;
           }
@@ -395,12 +425,12 @@ __global__ __launch_bounds__(kFusedThreads, 4) void gemv_fused_kernel(
       step(rcur);
     }
   }
-  if (split) {
+  if constexpr (SPLIT) {
     // add up the waves' partial sums of every row of the band
     __syncthreads();
     for (int i = tid; i < tsub * NB * M; i += kFusedThreads) {
       const int t = i / (NB * M), bq = (i / M) % NB, cc = i % M;
-      if (bq < B && t * M + cc < band_rows) {
+      if (bq < B && t * M + cc < nrows) {
         float a = 0.f;
 #pragma unroll
         for (int w = 0; w < kFusedWaves; ++w) a += red[((t * kFusedWaves + w) * NB + bq) * M + cc];
@@ -459,12 +489,12 @@ bool gemv_fused_eligible(int64_t B, int64_t K, int64_t N, int block) {
   return fused_plan(B, K, N, fused_device_cus()).lds <= kFusedLdsMax;
 }
 
-template <int NB, int L, int DT>
-static void fused_launch_t(const void* x, const int8_t* signs, const uint32_t* codes, const uint16_t* scales,
+template <int NB, int L, int DT, bool SPLIT>
+static void fused_launch_m(const void* x, const int8_t* signs, const uint32_t* codes, const uint16_t* scales,
                            const uint16_t* biases, float* y, int N, int K, int cfg, int aux, int grid,
                            size_t lds, hipStream_t st) {
   constexpr int M = NB == 1 ? 16 : 32;
-  auto kern = gemv_fused_kernel<NB, M, L, DT>;
+  auto kern = gemv_fused_kernel<NB, M, L, DT, SPLIT>;
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -473,6 +503,16 @@ static void fused_launch_t(const void* x, const int8_t* signs, const uint32_t* c
   }
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kFusedThreads), lds, st, x, signs, codes, scales, biases, N, K, cfg,
                      aux, y);
+}
+
+template <int NB, int L, int DT>
+static void fused_launch_t(const void* x, const int8_t* signs, const uint32_t* codes, const uint16_t* scales,
+                           const uint16_t* biases, float* y, int N, int K, int cfg, int aux, int grid,
+                           size_t lds, hipStream_t st) {
+  if (cfg & 16)
+    fused_launch_m<NB, L, DT, true>(x, signs, codes, scales, biases, y, N, K, cfg, aux, grid, lds, st);
+  else
+    fused_launch_m<NB, L, DT, false>(x, signs, codes, scales, biases, y, N, K, cfg, aux, grid, lds, st);
 }
 
 template <int NB, int L>
