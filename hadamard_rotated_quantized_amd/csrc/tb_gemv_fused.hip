@@ -42,6 +42,12 @@ constexpr int kFusedRing = 4;
 constexpr int kFusedMaxSub = 7;        // subtiles per workgroup in split mode (3 bits of cfg)
 constexpr int kScratchFloats = 64 * 17;  // per-wave transpose area (64 rows of 16 + 1 pad)
 constexpr int64_t kFusedLdsMax = 150 * 1024;
+constexpr int kPersistent = 0, kSplitRing = 1, kSplitStaged = 2;  // kernel modes
+constexpr int kStageSlot = 1024 + 16;  // LDS bytes per staged 1 KB of band
+constexpr int kStageLoads = 6;         // direct-to-LDS loads per wave: at most 48 KB of band codes
+constexpr int kStagedItems = 4;        // items per wave in the staged mode
+// s_waitcnt immediate with vmcnt(0) and the other counters left alone
+constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
 
 // LDS layout (bytes): 8 zero uint4; limbs [B][Gp][3] rows of kLdsRow uint4;
 // (f * sum q, f) float2 [B][Gp]; per-wave transpose scratch; split mode:
@@ -124,16 +130,25 @@ __device__ __forceinline__ void transform_chunk(float v[16], int lane, float* sc
 }
 
 // cfg: batch rows B (bits 0-3), subtiles per workgroup (bits 5-7, split
-// mode), grid size (bits 8-31).  aux: split mode, rows per workgroup;
+// modes), grid size (bits 8-31).  aux: split modes, rows per workgroup;
 // persistent mode, tile groups (8 tiles of M rows).  The 14 argument SGPRs
 // the dispatcher can preload (16 user SGPRs minus the kernel-argument
 // pointer) hold everything but y, which is needed last.
-template <int NB, int M, int L, int DT, bool SPLIT>
-__global__ __launch_bounds__(kFusedThreads, 4) void gemv_fused_kernel(
+//
+// MODE kPersistent / kSplitRing stream each wave's items through a ring of
+// registers; kSplitStaged first copies the codes of the workgroup's whole
+// band (contiguous in memory) into LDS with direct-to-LDS buffer loads of
+// 1 KB per wave instruction -- fully coalesced, where the per-item loads of
+// a tile touch 16 rows per instruction -- and fetches the scale and bias of
+// each of its (at most kStagedItems) items with 2-byte loads up front.
+template <int NB, int M, int L, int DT, int MODE>
+__global__ __launch_bounds__(kFusedThreads, NB == 8 ? 2 : 4) void gemv_fused_kernel(
     const void* __restrict__ x, const int8_t* __restrict__ signs, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases, int N, int K, int cfg, int aux,
     float* __restrict__ y) {
   using MF = Mfma<M>;
+  constexpr bool SPLIT = MODE != kPersistent;
+  constexpr bool STAGED = MODE == kSplitStaged;
   constexpr int GPS = MF::GPS, BPI = MF::BPI;
   constexpr int NBC = (NB + BPI - 1) / BPI;  // MFMA chains per item
   constexpr int P = kFusedRing;
@@ -169,6 +184,7 @@ __global__ __launch_bounds__(kFusedThreads, 4) void gemv_fused_kernel(
   float2* const lds_xf = reinterpret_cast<float2*>(lds_base + lay.xf);
   float* const scratch = reinterpret_cast<float*>(lds_base + lay.scratch) + wave * kScratchFloats;
   float* const red = reinterpret_cast<float*>(lds_base + lay.red);
+  char* const stage = lds_base + lay.total;  // staged band (kSplitStaged)
 
   // 1. activation chunks of this wave (lane l: inputs 16 l .. 16 l + 15 of
   //    the chunk); inputs past K read as zero
@@ -208,7 +224,7 @@ __global__ __launch_bounds__(kFusedThreads, 4) void gemv_fused_kernel(
   }
 
   // 2. weight stream.  An item is span s (GPS groups) of the M rows of a
-  //    tile.  Split mode: the workgroup owns a band of rows, tsub subtiles
+  //    tile.  Split modes: the workgroup owns a band of rows, tsub subtiles
   //    of M rows; item i = t * S + s, and wave w takes items w, w + 8, ...
   //    Persistent mode: wave w owns tile 8 t + w of each tile group t =
   //    blockIdx.x, + grid, ..., all S spans of it.  The buffer resources
@@ -271,12 +287,43 @@ __global__ __launch_bounds__(kFusedThreads, 4) void gemv_fused_kernel(
     sp.bias = __builtin_amdgcn_raw_buffer_load_b16(rb, so, 0, 0);
   };
 
+  // staged codes: 1 KB slots of kStageSlot bytes (16 B of padding keeps the
+  // 16 rows of an item on distinct LDS banks) in [0, ncc), then one dump
+  // slot that the surplus loads (past the band) fill with zeros.  Every row
+  // is a whole number of 32-byte groups, so no load straddles the band end.
+  const int ncc = STAGED ? (nrows * W * 4 + 1023) >> 10 : 0;
+  auto stage_at = [&](uint32_t off) {  // LDS offset of byte `off` of the staged codes
+    return off + (off >> 10) * (kStageSlot - 1024);
+  };
+
   Cursor rcur = first;
-  FusedSpan ring[P];
+  FusedSpan ring[STAGED ? 1 : P];
+  uint16_t st_s[STAGED ? kStagedItems : 1], st_b[STAGED ? kStagedItems : 1];
+  if constexpr (STAGED) {
 #pragma unroll
-  for (int i = 0; i < P; ++i) {
-    load_item(rcur, ring[i]);
-    step(rcur);
+    for (int i = 0; i < kStageLoads; ++i) {
+      const int q = wave + kFusedWaves * i;  // slot
+      const bool real = q < ncc;
+      char* dst = stage + (real ? q : ncc) * kStageSlot;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (__attribute__((address_space(3))) void*)dst, 16,
+                                               real ? q * 1024 + lane * 16 : kOob, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < kStagedItems; ++j) {
+      const uint32_t us = rcur.j < total
+                              ? static_cast<uint32_t>(tile_row(rcur)) * static_cast<uint32_t>(G * 2) +
+                                    rcur.s * (GPS * 2)
+                              : kOob;
+      st_s[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, static_cast<int>(lane_s + us), 0, 0);
+      st_b[j] = __builtin_amdgcn_raw_buffer_load_b16(rb, static_cast<int>(lane_s + us), 0, 0);
+      step(rcur);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      load_item(rcur, ring[i]);
+      step(rcur);
+    }
   }
 
   // 3. transform the chunks into LDS while the weights are in flight
@@ -327,12 +374,13 @@ __global__ __launch_bounds__(kFusedThreads, 4) void gemv_fused_kernel(
   if constexpr (SPLIT) {
     for (int i = tid; i < tsub * kFusedWaves * NB * M; i += kFusedThreads) red[i] = 0.f;
   }
+  if constexpr (STAGED) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's band slots have landed
   __syncthreads();
 
-  // 4. the matmul.  The loop is unrolled over the ring slots, and every
-  //    slot is refilled unconditionally (with a zero-reading load past the
-  //    end), so the loads are issued in the same static order in every
-  //    iteration and each wait covers exactly the slot being consumed.
+  // 4. the matmul.  Ring modes: the loop is unrolled over the ring slots,
+  //    and every slot is refilled unconditionally (with a zero-reading load
+  //    past the end), so the loads are issued in the same static order in
+  //    every iteration and each wait covers exactly the slot being consumed.
   float yacc[NB];
 #pragma unroll
   for (int bq = 0; bq < NB; ++bq) yacc[bq] = 0.f;
@@ -357,7 +405,10 @@ __global__ __launch_bounds__(kFusedThreads, 4) void gemv_fused_kernel(
     bop[5] = decode_word(cur.w1.y);
     bop[6] = decode_word(cur.w1.z);
     bop[7] = decode_word(cur.w1.w);
-    const float sc = half_bits_to_float(cur.s), bi = half_bits_to_float(cur.bias);
+    // groups past K (padding of the last span) contribute nothing, whatever
+    // their scale and bias loads returned
+    const bool gin = s * GPS + lg < G;
+    const float sc = gin ? half_bits_to_float(cur.s) : 0.f, bi = gin ? half_bits_to_float(cur.bias) : 0.f;
     const float2* xfp = lds_xf + s * GPS + lg;  // (f sum q, f) of this lane's group, batch row 0
 #pragma unroll
     for (int bc = 0; bc < NBC; ++bc) {
@@ -396,33 +447,57 @@ __global__ __launch_bounds__(kFusedThreads, 4) void gemv_fused_kernel(
     if constexpr (M == 16) v += xor_lane(v, 4, lane);
     return v + xor_lane(v, 5, lane);
   };
+  // after consuming the item at ccur: park or store the tile when it ends
+  auto tile_end = [&](const Cursor& ccur, const Cursor& nxt) {
+    if (nxt.j >= total || nxt.t != ccur.t) {
+      // this wave is done with the tile: split modes park its partial sums,
+      // persistent mode stores the rows it owns
+      const int row0 = tile_row(ccur);
+#pragma unroll
+      for (int bq = 0; bq < NB; ++bq) {
+        const float v = lane_group_sum(yacc[bq]);
+        if (lg == 0 && bq < B) {
+          if constexpr (SPLIT) red[((ccur.t * kFusedWaves + wave) * NB + bq) * M + c] = v;
+          else if (row0 + c < N) y[(int64_t)bq * N + row0 + c] = v;
+        }
+        yacc[bq] = 0.f;
+      }
+    }
+  };
 
   Cursor ccur = first;
-  for (int base = 0; base < total; base += P) {
+  if constexpr (STAGED) {
 #pragma unroll
-    for (int sl = 0; sl < P; ++sl) {
-      if (base + sl < total) {
-        consume(ring[sl], ccur.s);
+    for (int j = 0; j < kStagedItems; ++j) {
+      if (j < total) {
+        const uint32_t oc =
+            lane_c + static_cast<uint32_t>(tile_row(ccur)) * static_cast<uint32_t>(W * 4) + ccur.s * (GPS * 32);
+        FusedSpan cur;
+        cur.w0 = *reinterpret_cast<const uint4*>(stage + stage_at(oc));
+        cur.w1 = *reinterpret_cast<const uint4*>(stage + stage_at(oc) + 16);
+        cur.s = st_s[j];
+        cur.bias = st_b[j];
+        consume(cur, ccur.s);
         Cursor nxt = ccur;
         step(nxt);
-        if (nxt.j >= total || nxt.t != ccur.t) {
-          // this wave is done with the tile: split mode parks its partial
-          // sums, persistent mode stores the rows it owns
-          const int row0 = tile_row(ccur);
-#pragma unroll
-          for (int bq = 0; bq < NB; ++bq) {
-            const float v = lane_group_sum(yacc[bq]);
-            if (lg == 0 && bq < B) {
-              if constexpr (SPLIT) red[((ccur.t * kFusedWaves + wave) * NB + bq) * M + c] = v;
-              else if (row0 + c < N) y[(int64_t)bq * N + row0 + c] = v;
-            }
-            yacc[bq] = 0.f;
-          }
-        }
+        tile_end(ccur, nxt);
         ccur = nxt;
       }
-      load_item(rcur, ring[sl]);
-      step(rcur);
+    }
+  } else {
+    for (int base = 0; base < total; base += P) {
+#pragma unroll
+      for (int sl = 0; sl < P; ++sl) {
+        if (base + sl < total) {
+          consume(ring[sl], ccur.s);
+          Cursor nxt = ccur;
+          step(nxt);
+          tile_end(ccur, nxt);
+          ccur = nxt;
+        }
+        load_item(rcur, ring[sl]);
+        step(rcur);
+      }
     }
   }
   if constexpr (SPLIT) {
@@ -449,7 +524,7 @@ static int fused_device_cus() {
 
 // Launch shape of one call.
 struct FusedPlan {
-  bool split;
+  int mode;
   int tsub, aux, grid;
   int64_t lds;
 };
@@ -458,25 +533,41 @@ static FusedPlan fused_plan(int64_t B, int64_t K, int64_t N, int cus) {
   const int M = B == 1 ? 16 : 32;
   const int NB = B == 1 ? 1 : (B <= 4 ? 4 : 8);
   const int64_t Gp = padded_groups(K);
+  const int64_t rb = K / kCodesPerWord * 4;  // code bytes per row
   FusedPlan p;
-  // split mode: one band of about N / CUs rows (at least 16) per workgroup
+  // split modes: one band of about N / CUs rows (at least 16) per workgroup
   const int64_t rows = std::max<int64_t>((N + cus - 1) / cus, 16);
   const int64_t tsub = (rows + M - 1) / M;
   if (tsub <= kFusedMaxSub) {
-    p.split = true;
     p.tsub = static_cast<int>(tsub);
     p.aux = static_cast<int>(rows);
     p.grid = static_cast<int>((N + rows - 1) / rows);
-    p.lds = fused_lds_layout(B, Gp, tsub * kFusedWaves * NB * M).total;
+    const int64_t base = fused_lds_layout(B, Gp, tsub * kFusedWaves * NB * M).total;
+    // staged codes: the slots the loads fill, every slot an item of the last
+    // subtile can address (an item may run up to 3 padding groups past the
+    // last row), and the dump slot
+    const int64_t nst = (rows * rb + 1023) / 1024;
+    const int64_t slots = (tsub * M * rb + 96 + 1023) / 1024 + 1;
+    const int64_t staged = base + slots * kStageSlot;
+    const int64_t items = tsub * (Gp / (64 / M));
+    if (nst <= (int64_t)kFusedWaves * kStageLoads && items <= (int64_t)kFusedWaves * kStagedItems &&
+        staged <= kFusedLdsMax) {
+      p.mode = kSplitStaged;
+      p.lds = staged;
+    } else {
+      p.mode = kSplitRing;
+      p.lds = base;
+    }
   } else {
     // persistent mode: tile groups of 8 tiles, at most 2 workgroups per CU
     const int64_t tiles = (N + M - 1) / M;
     const int64_t ntg = (tiles + kFusedWaves - 1) / kFusedWaves;
-    p.split = false;
+    p.mode = kPersistent;
     p.tsub = 0;
     p.aux = static_cast<int>(ntg);
     p.lds = fused_lds_layout(B, Gp, 0).total;
-    const int per_cu = p.lds <= 75 * 1024 ? 2 : 1;
+    // two per CU when LDS allows and the registers do (8 batch rows need 2x)
+    const int per_cu = (p.lds <= 75 * 1024 && NB < 8) ? 2 : 1;
     p.grid = static_cast<int>(std::min<int64_t>(ntg, (int64_t)cus * per_cu));
   }
   return p;
@@ -489,12 +580,12 @@ bool gemv_fused_eligible(int64_t B, int64_t K, int64_t N, int block) {
   return fused_plan(B, K, N, fused_device_cus()).lds <= kFusedLdsMax;
 }
 
-template <int NB, int L, int DT, bool SPLIT>
+template <int NB, int L, int DT, int MODE>
 static void fused_launch_m(const void* x, const int8_t* signs, const uint32_t* codes, const uint16_t* scales,
                            const uint16_t* biases, float* y, int N, int K, int cfg, int aux, int grid,
                            size_t lds, hipStream_t st) {
   constexpr int M = NB == 1 ? 16 : 32;
-  auto kern = gemv_fused_kernel<NB, M, L, DT, SPLIT>;
+  auto kern = gemv_fused_kernel<NB, M, L, DT, MODE>;
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -506,31 +597,41 @@ static void fused_launch_m(const void* x, const int8_t* signs, const uint32_t* c
 }
 
 template <int NB, int L, int DT>
-static void fused_launch_t(const void* x, const int8_t* signs, const uint32_t* codes, const uint16_t* scales,
-                           const uint16_t* biases, float* y, int N, int K, int cfg, int aux, int grid,
-                           size_t lds, hipStream_t st) {
-  if (cfg & 16)
-    fused_launch_m<NB, L, DT, true>(x, signs, codes, scales, biases, y, N, K, cfg, aux, grid, lds, st);
+static void fused_launch_t(int mode, const void* x, const int8_t* signs, const uint32_t* codes,
+                           const uint16_t* scales, const uint16_t* biases, float* y, int N, int K, int cfg,
+                           int aux, int grid, size_t lds, hipStream_t st) {
+  if (mode == kSplitStaged)
+    fused_launch_m<NB, L, DT, kSplitStaged>(x, signs, codes, scales, biases, y, N, K, cfg, aux, grid, lds, st);
+  else if (mode == kSplitRing)
+    fused_launch_m<NB, L, DT, kSplitRing>(x, signs, codes, scales, biases, y, N, K, cfg, aux, grid, lds, st);
   else
-    fused_launch_m<NB, L, DT, false>(x, signs, codes, scales, biases, y, N, K, cfg, aux, grid, lds, st);
+    fused_launch_m<NB, L, DT, kPersistent>(x, signs, codes, scales, biases, y, N, K, cfg, aux, grid, lds, st);
 }
 
 template <int NB, int L>
-static void fused_launch_dt(int dt, const void* x, const int8_t* signs, const uint32_t* codes,
+static void fused_launch_dt(int mode, int dt, const void* x, const int8_t* signs, const uint32_t* codes,
                             const uint16_t* scales, const uint16_t* biases, float* y, int N, int K, int cfg,
                             int aux, int grid, size_t lds, hipStream_t st) {
-  if (dt == TB_F32) fused_launch_t<NB, L, TB_F32>(x, signs, codes, scales, biases, y, N, K, cfg, aux, grid, lds, st);
-  else fused_launch_t<NB, L, TB_BF16>(x, signs, codes, scales, biases, y, N, K, cfg, aux, grid, lds, st);
+  if (dt == TB_F32)
+    fused_launch_t<NB, L, TB_F32>(mode, x, signs, codes, scales, biases, y, N, K, cfg, aux, grid, lds, st);
+  else
+    fused_launch_t<NB, L, TB_BF16>(mode, x, signs, codes, scales, biases, y, N, K, cfg, aux, grid, lds, st);
 }
 
 template <int NB>
-static void fused_launch_l(int block, int dt, const void* x, const int8_t* signs, const uint32_t* codes,
-                           const uint16_t* scales, const uint16_t* biases, float* y, int N, int K, int cfg,
-                           int aux, int grid, size_t lds, hipStream_t st) {
+static void fused_launch_l(int mode, int block, int dt, const void* x, const int8_t* signs,
+                           const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, float* y,
+                           int N, int K, int cfg, int aux, int grid, size_t lds, hipStream_t st) {
   switch (block) {
-    case 0: fused_launch_dt<NB, 0>(dt, x, signs, codes, scales, biases, y, N, K, cfg, aux, grid, lds, st); break;
-    case 512: fused_launch_dt<NB, 512>(dt, x, signs, codes, scales, biases, y, N, K, cfg, aux, grid, lds, st); break;
-    default: fused_launch_dt<NB, 1024>(dt, x, signs, codes, scales, biases, y, N, K, cfg, aux, grid, lds, st); break;
+    case 0:
+      fused_launch_dt<NB, 0>(mode, dt, x, signs, codes, scales, biases, y, N, K, cfg, aux, grid, lds, st);
+      break;
+    case 512:
+      fused_launch_dt<NB, 512>(mode, dt, x, signs, codes, scales, biases, y, N, K, cfg, aux, grid, lds, st);
+      break;
+    default:
+      fused_launch_dt<NB, 1024>(mode, dt, x, signs, codes, scales, biases, y, N, K, cfg, aux, grid, lds, st);
+      break;
   }
 }
 
@@ -538,15 +639,15 @@ void gemv_fused_launch(const void* x, int x_dtype, int64_t B, int64_t K, const i
                        const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, int64_t N,
                        float* y, hipStream_t st) {
   const FusedPlan p = fused_plan(B, K, N, fused_device_cus());
-  const int cfg = static_cast<int>(B) | (p.split ? 16 : 0) | (p.tsub << 5) | (p.grid << 8);
+  const int cfg = static_cast<int>(B) | (p.tsub << 5) | (p.grid << 8);
   const int n = static_cast<int>(N), k = static_cast<int>(K);
   const size_t lds = static_cast<size_t>(p.lds);
   if (B == 1)
-    fused_launch_l<1>(block, x_dtype, x, signs, codes, scales, biases, y, n, k, cfg, p.aux, p.grid, lds, st);
+    fused_launch_l<1>(p.mode, block, x_dtype, x, signs, codes, scales, biases, y, n, k, cfg, p.aux, p.grid, lds, st);
   else if (B <= 4)
-    fused_launch_l<4>(block, x_dtype, x, signs, codes, scales, biases, y, n, k, cfg, p.aux, p.grid, lds, st);
+    fused_launch_l<4>(p.mode, block, x_dtype, x, signs, codes, scales, biases, y, n, k, cfg, p.aux, p.grid, lds, st);
   else
-    fused_launch_l<8>(block, x_dtype, x, signs, codes, scales, biases, y, n, k, cfg, p.aux, p.grid, lds, st);
+    fused_launch_l<8>(p.mode, block, x_dtype, x, signs, codes, scales, biases, y, n, k, cfg, p.aux, p.grid, lds, st);
 }
 
 }  // namespace tb

@@ -414,6 +414,8 @@ TWO_PATHS = [
     (250, 2304, 3, 0, "bf16"),       # partial last chunk, 18 groups (2 padding)
     (5000, 640, 2, 0, "f32"),
     (9000, 1024, 1, 1024, "bf16"),   # 563 tiles: 4 waves per tile
+    (45, 640, 1, 0, "f32"),          # 5 groups (3 padding), last band of 13 rows
+    (1000, 384, 2, 0, "bf16"),       # 6-byte scale rows: band ends mid 16 bytes
 ]
 
 
