@@ -42,6 +42,45 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# Sources whose change invalidates the hardware-counter traffic figure of the
+# single-launch GEMV kernel (its code, the headers it includes, its flags).
+_CSRC = os.path.join(ROOT, "hadamard_rotated_quantized_amd", "csrc")
+KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in ("tb_gemv_fused.hip", "tb_gemv.h", "tb_device.h", "tb_common.h")] + \
+    [os.path.join(ROOT, "hadamard_rotated_quantized_amd", "build.py")]
+COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "gemv_fused_kernel_q_proj_counters.txt")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the GEMV kernel from the committed rocprofv3
+    counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter
+    reads for a plain copy of known size), or None when no summary exists for
+    this workload or the kernel's sources changed after it was taken."""
+    if workload != "q_proj" or not os.path.exists(COUNTER_SUMMARY):
+        return None
+    kv = {}
+    with open(COUNTER_SUMMARY) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        log("counter summary is stale (kernel sources changed): traffic = null")
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline_gemv(p, codes, scales, biases, budget_s=12.0):
     """Time the fp64 oracle on the same workload (bounded number of calls)."""
     import oracle
@@ -59,6 +98,44 @@ def cpu_baseline_gemv(p, codes, scales, biases, budget_s=12.0):
         oracle.packed_linear(p.x64, p.signs, p.block, codes, scales, biases)
     per = (time.perf_counter() - t0) / reps
     return per, reps + 1, blas_threads
+
+
+def run_counter_pass(args):
+    """Eager launches only, no timing: the command that rocprofv3 --pmc passes
+    wrap.  `--workload copy` runs plain device copies of a known size (the
+    calibration of the FETCH_SIZE / WRITE_SIZE counters)."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    if args.workload == "copy":
+        nbytes = 64 << 20
+        bufs = [torch.empty(nbytes // 4, dtype=torch.float32, device=dev).uniform_() for _ in range(4)]
+        dst = torch.empty_like(bufs[0])
+        for i in range(40):
+            dst.copy_(bufs[i % 4])
+        torch.cuda.synchronize()
+        print(json.dumps({"counter_pass": "copy", "bytes_per_copy": nbytes, "copies": 40}), flush=True)
+        return
+    import hadamard_rotated_quantized_amd as tb
+    from hadamard_rotated_quantized_amd import synth
+
+    p = synth.config_problem(args.workload)
+    codes, s, b = tb.tb_pack(p.t, p.scales)
+    c0 = torch.from_numpy(codes.view(np.int32)).to(dev)
+    s0 = torch.from_numpy(s).to(dev)
+    b0 = torch.from_numpy(b).to(dev)
+    R = args.replicas or max(1, math.ceil((1 << 30) / (p.N * p.K * 9 // 32)))
+    reps = [(c0, s0, b0)] + [(c0.clone(), s0.clone(), b0.clone()) for _ in range(R - 1)]
+    x = (torch.from_numpy(p.x_store.view(np.int16)).view(torch.bfloat16) if p.xdtype == "bf16"
+         else torch.from_numpy(p.x_store)).to(dev)
+    sg = torch.from_numpy(p.signs).to(dev)
+    ws = torch.empty(tb.tb_ternary_gemv_workspace_size(p.B, p.K), dtype=torch.uint8, device=dev)
+    y = torch.empty((p.B, p.N), dtype=torch.float32, device=dev)
+    for i in range(3 * R):
+        tb.tb_ternary_gemv(x, sg, p.block, *reps[i % R], out=y, workspace=ws)
+    torch.cuda.synchronize()
+    print(json.dumps({"counter_pass": args.workload, "launches": 3 * R, "replicas": R,
+                      "weight_bytes": p.N * p.K * 9 // 32}), flush=True)
 
 
 def run_q_proj(args):
@@ -187,7 +264,7 @@ def run_q_proj(args):
                                f"2.25 bpw packed weights, {R} rotating weight replicas",
                    "N": N, "K": K, "batch": B, "block": p.block, "replicas": R},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload)},
         "cpu_baseline": cpu,
         "detail": {"kernel": "gemv_fused_kernel", "kernel_us_mean": round(main_us, 3),
                    "timing": "HIP graph of back-to-back steps over the replica ring; one step is one "
@@ -205,15 +282,22 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=12200)
     ap.add_argument("--warmup", type=int, default=1220)
-    ap.add_argument("--workload", default="q_proj", choices=["q_proj", "tiny"])
+    ap.add_argument("--workload", default="q_proj", choices=["q_proj", "tiny", "copy"])
     ap.add_argument("--replicas", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counters-only", action="store_true",
+                    help="eager launches without timing, for rocprofv3 --pmc passes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
-    run_q_proj(args)
+    if args.counters_only:
+        run_counter_pass(args)
+    elif args.workload == "copy":
+        raise SystemExit("--workload copy is a counter-calibration pass: use it with --counters-only")
+    else:
+        run_q_proj(args)
 
 
 if __name__ == "__main__":
