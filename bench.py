@@ -138,14 +138,15 @@ def run_counter_pass(args):
                       "weight_bytes": p.N * p.K * 9 // 32}), flush=True)
 
 
-def run_q_proj(args):
+def run_gemv(args):
+    """Decode GEMV workloads: q_proj (default), tiny, down_proj (--batch 1..8)."""
     import torch
 
     import hadamard_rotated_quantized_amd as tb
     import oracle
     from hadamard_rotated_quantized_amd import synth
 
-    p = synth.config_problem(args.workload)
+    p = synth.config_problem(args.workload, args.batch)
     N, K, B = p.N, p.K, p.B
     wbytes = N * K * 9 // 32
     log(f"workload {args.workload}: N={N} K={K} B={B} weight bytes {wbytes}")
@@ -260,7 +261,7 @@ def run_q_proj(args):
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload} decode GEMV N={N} K={K} batch {B} bf16 activations, "
+        "config": {"workload": f"{args.workload} decode GEMV N={N} K={K} batch {B} {p.xdtype} activations, "
                                f"2.25 bpw packed weights, {R} rotating weight replicas",
                    "N": N, "K": K, "batch": B, "block": p.block, "replicas": R},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -277,12 +278,241 @@ def run_q_proj(args):
     print(json.dumps(out), flush=True)
 
 
+def _time_graph(torch, g, n_replays):
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n_replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3  # seconds
+
+
+def _parity(got, want):
+    got = np.asarray(got, dtype=np.float64)
+    rel = float(np.linalg.norm(got - want) / np.linalg.norm(want))
+    mabs = float(np.abs(got - want).max() / np.abs(want).max())
+    return rel, mabs
+
+
+def run_prefill(args):
+    """Prefill GEMM gate/up_proj: M=2048, K=5120, N=17408, bf16 x.  One step =
+    one tb_ternary_gemm call (rotation + hi/lo split kernel, then the bf16
+    MFMA matmul).  value = algorithmic TFLOP/s (2 M N K per step)."""
+    import torch
+
+    import hadamard_rotated_quantized_amd as tb
+    import oracle
+    from hadamard_rotated_quantized_amd import synth
+
+    p = synth.config_problem("prefill_gate_up")
+    M, N, K = p.B, p.N, p.K
+    flops = 2.0 * M * N * K
+    dev = torch.device("cuda:0")
+    codes, s, b = tb.tb_pack(p.t, p.scales)
+    c0 = torch.from_numpy(codes.view(np.int32)).to(dev)
+    s0 = torch.from_numpy(s).to(dev)
+    b0 = torch.from_numpy(b).to(dev)
+    x = torch.from_numpy(p.x_store.view(np.int16)).view(torch.bfloat16).to(dev)
+    sg = torch.from_numpy(p.signs).to(dev)
+    ws = torch.empty(tb.tb_ternary_gemm_workspace_size(M, K), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    tb.tb_ternary_gemm(x, sg, p.block, c0, s0, b0, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 1023, M - 1],
+                                     np.random.default_rng(44).integers(0, M, 26)]))
+    oc, osc, ob = oracle.pack(p.t, p.scales)
+    want = oracle.packed_linear(p.x64[rows], p.signs, p.block, oc, osc, ob)
+    rel, mabs = _parity(y[torch.from_numpy(rows).to(dev)].cpu().numpy(), want)
+    log(f"parity (sampled rows) rel L2 {rel:.2e} max-abs {mabs:.2e}")
+    if not (rel <= 1e-4 and mabs <= 1e-3):
+        raise SystemExit("parity check failed; refusing to report a number")
+
+    steps = max(1, min(args.steps, 200))
+    warm = max(1, min(args.warmup, 20))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(10):
+            tb.tb_ternary_gemm(x, sg, p.block, c0, s0, b0, out=y, workspace=ws)
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2):
+        for _ in range(10):
+            tb.tb_ternary_gemm_run(ws, M, K, c0, s0, b0, out=y)
+    for _ in range(max(1, warm // 10)):
+        g.replay()
+    torch.cuda.synchronize()
+    nrep = max(1, steps // 10)
+    t = _time_graph(torch, g, nrep) / (nrep * 10)
+    t_run = _time_graph(torch, g2, nrep) / (nrep * 10)
+    tflops = flops / t / 1e12
+    run_tflops = flops / t_run / 1e12
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        sample = 16
+        t0 = time.perf_counter()
+        oracle.packed_linear(p.x64[:sample], p.signs, p.block, oc, osc, ob)
+        per = time.perf_counter() - t0
+        cpu = {"value": round(2.0 * sample * N * K / per / 1e12, 6), "unit": "TFLOP/s", "cores": _blas_threads(),
+               "kind": "oracle",
+               "sample": f"{sample} of the {M} activation rows against the whole {N}x{K} pack, {per:.1f} s, numpy fp64"}
+
+    out = {
+        "metric": "algorithmic TFLOP/s of the prefill Packed linear (bf16 MFMA path); % of bf16 dense MFMA peak",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": nrep * 10, "warmup": warm,
+        "ms_per_step": round(t * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"prefill gate/up_proj GEMM M={M} K={K} N={N}, bf16 activations, 2.25 bpw packed "
+                               "weights", "M": M, "N": N, "K": K, "block": p.block},
+        "roofline": {"bound": "mfma", "achieved": round(run_tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(run_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "detail": {"kernel": "gemm_main_kernel", "main_kernel_ms": round(t_run * 1e3, 4),
+                   "step_ms_prepare_and_run": round(t * 1e3, 4),
+                   "issued_mfma_frac": round(2 * run_tflops / BF16_PEAK_TFLOPS, 4),
+                   "note": "the activation enters MFMA as an exact bf16 hi + lo pair, so the issued MFMA work "
+                           "is twice the algorithmic 2 M N K",
+                   "parity_rel_l2": rel, "parity_max_abs_rel": mabs, "parity_rows": int(len(rows))},
+    }
+    print(json.dumps(out), flush=True)
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        return 1
+
+
+def run_sweep(args):
+    """The full decode sweep at batch 1: the 401 packed linears of the
+    64-layer model (3:1 linear:full attention layers, MLP 17408, lm_head
+    248320) and one embedding row with the inverse transform.  Every module
+    has its own synthetic pack and input (modules are not chained).  One step
+    = all 402 calls, captured once as a HIP graph."""
+    import torch
+
+    import hadamard_rotated_quantized_amd as tb
+    import oracle
+    from hadamard_rotated_quantized_amd import synth
+
+    dev = torch.device("cuda:0")
+    mods = synth.sweep_modules()
+    signs_h = synth.sweep_signs()
+    signs = {k: torch.from_numpy(v).to(dev) for k, v in signs_h.items()}
+    packs, xs, ys = [], [], []
+    t0 = time.perf_counter()
+    for i, (name, N, K, kind) in enumerate(mods):
+        t, sc, x = synth.device_module_draw(i, N, K, 1, dev)
+        codes, so, bo = tb.tb_pack_device(t, sc, check=False)
+        del t, sc
+        packs.append((codes, so, bo))
+        xs.append(x)
+        ys.append(torch.empty((1, N) if kind == "linear" else (1, K), dtype=torch.float32, device=dev))
+    torch.cuda.synchronize()
+    log(f"drew and packed {len(mods)} modules in {time.perf_counter() - t0:.1f} s")
+    embed_id = torch.tensor([int(np.random.default_rng(synth.SWEEP_SEED).integers(0, synth.VOCAB))],
+                            dtype=torch.int32, device=dev)
+    wsz = tb.tb_ternary_gemv_workspace_size(1, max(m[2] for m in mods))
+    ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
+
+    def call(i):
+        name, N, K, kind = mods[i]
+        c, sc, bi = packs[i]
+        if kind == "linear":
+            tb.tb_ternary_gemv(xs[i], signs[K], 1024, c, sc, bi, out=ys[i], workspace=ws)
+        else:
+            tb.tb_embed_inverse(embed_id, c, sc, bi, signs[K], 1024, out=ys[i])
+
+    for i in range(len(mods)):
+        call(i)
+    torch.cuda.synchronize()
+    # parity on one module of every shape (lm_head on sampled rows) and the embedding row
+    checked, worst = [], 0.0
+    seen = set()
+    for i, (name, N, K, kind) in enumerate(mods):
+        key = (N, K, kind)
+        if key in seen:
+            continue
+        seen.add(key)
+        t, sc, _ = synth.device_module_draw(i, N, K, 1, dev)
+        if kind == "linear":
+            rows = np.arange(N) if N <= 20000 else np.unique(np.concatenate(
+                [[0, N - 1], np.random.default_rng(i).integers(0, N, 2046)]))
+        else:
+            rows = np.array([int(embed_id.item())])
+        rt = torch.from_numpy(rows).to(dev)
+        oc, osc, ob = oracle.pack(t[rt].cpu().numpy(), sc[rt].cpu().numpy())
+        del t, sc
+        if kind == "linear":
+            xh = xs[i].float().cpu().numpy().astype(np.float64)
+            want = oracle.packed_linear(xh, signs_h[K], 1024, oc, osc, ob)
+            got = ys[i][:, rt].cpu().numpy()
+        else:
+            want = oracle.embed_inverse([0], oc, osc, ob, signs_h[K], 1024)
+            got = ys[i].cpu().numpy()
+        rel, mabs = _parity(got, want)
+        worst = max(worst, rel)
+        checked.append(f"{name}:{rel:.1e}")
+        if not (rel <= 1e-4 and mabs <= 1e-3):
+            raise SystemExit(f"parity check failed on {name}: rel {rel:.2e} max-abs {mabs:.2e}")
+    log("parity " + ", ".join(checked))
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(len(mods)):
+            call(i)
+    g.replay()
+    torch.cuda.synchronize()
+    nrep = max(3, min(args.steps, 30))
+    sec = _time_graph(torch, g, nrep) / nrep
+    wbytes = sum(N * K * 9 // 32 for (_, N, K, kind) in mods if kind == "linear") + 5120 * 9 // 32
+    value = wbytes / sec / 1e9
+
+    # per-shape timing: a graph of every module of one shape, back to back
+    per_shape = {}
+    for key in sorted({(m[1], m[2], m[3]) for m in mods}):
+        idx = [i for i, m in enumerate(mods) if (m[1], m[2], m[3]) == key]
+        gs = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gs):
+            for i in idx:
+                call(i)
+        gs.replay()
+        torch.cuda.synchronize()
+        r = max(3, min(20, 2000 // len(idx)))
+        us = _time_graph(torch, gs, r) / (r * len(idx)) * 1e6
+        N, K, kind = key
+        b = N * K * 9 // 32 if kind == "linear" else 5120 * 9 // 32
+        per_shape[f"{kind} {N}x{K}"] = {"count": len(idx), "us_each": round(us, 3),
+                                        "GB/s": round(b / (us * 1e-6) / 1e9, 1)}
+
+    out = {
+        "metric": "effective weight GB/s (2.25 bpw), full batch-1 decode sweep of 402 packed modules",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": nrep, "warmup": 1,
+        "ms_per_step": round(sec * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8", "data": "synthetic",
+        "config": {"workload": "decode sweep: 401 packed linears of a 64-layer hidden-5120 model (48 linear-"
+                               "attention + 16 full-attention layers, MLP 17408, lm_head 248320) + 1 embedding "
+                               "row, batch 1, one HIP graph of 402 calls", "modules": len(mods),
+                   "weight_bytes": wbytes},
+        "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
+        "detail": {"per_shape": per_shape, "parity_worst_rel_l2": worst, "parity": checked},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=12200)
     ap.add_argument("--warmup", type=int, default=1220)
-    ap.add_argument("--workload", default="q_proj", choices=["q_proj", "tiny", "copy"])
+    ap.add_argument("--workload", default="q_proj",
+                    choices=["q_proj", "tiny", "down_proj", "prefill_gate_up", "sweep", "copy"])
+    ap.add_argument("--batch", type=int, default=None, help="down_proj batch (1, 2, 4 or 8)")
     ap.add_argument("--replicas", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--counters-only", action="store_true",
@@ -296,8 +526,14 @@ def main():
         run_counter_pass(args)
     elif args.workload == "copy":
         raise SystemExit("--workload copy is a counter-calibration pass: use it with --counters-only")
+    elif args.workload == "prefill_gate_up":
+        run_prefill(args)
+    elif args.workload == "sweep":
+        run_sweep(args)
     else:
-        run_q_proj(args)
+        if args.workload == "down_proj" and args.batch is None:
+            args.batch = 1
+        run_gemv(args)
 
 
 if __name__ == "__main__":

@@ -169,6 +169,13 @@ struct Mfma {
 // True when one workgroup can transform the whole input itself: block in
 // {0, 512, 1024}, at most 3 chunk transforms per wave, and an LDS footprint
 // within the limit for this (B, K, N).
+// Host side of the batch-1 band path (tb_gemv_band.hip): true when one
+// workgroup per band of output rows can hold the band's packed weights and
+// the transformed input in LDS.
+bool gemv_band_eligible(int64_t B, int64_t K, int64_t N, int block);
+void gemv_band_launch(const void* x, int x_dtype, int64_t K, const int8_t* signs, int block, const uint32_t* codes,
+                      const uint16_t* scales, const uint16_t* biases, int64_t N, float* y, hipStream_t st);
+
 bool gemv_fused_eligible(int64_t B, int64_t K, int64_t N, int block);
 void gemv_fused_launch(const void* x, int x_dtype, int64_t B, int64_t K, const int8_t* signs, int block,
                        const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, int64_t N,

@@ -704,6 +704,11 @@ extern "C" int tb_ternary_gemv(const void* x, int x_dtype, int64_t B, int64_t K,
   TB_TRY(run_checks(N, K, codes, scales, biases, y, who));
   TB_TRY(gemv_ws_check(workspace, ws_bytes, B, K, who));
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (gemv_band_eligible(B, K, N, block)) {
+    gemv_band_launch(x, x_dtype, K, signs, block, codes, scales, biases, N, y, st);
+    TB_LAUNCH_CHECK(who);
+    return TB_OK;
+  }
   if (gemv_fused_eligible(B, K, N, block)) {
     gemv_fused_launch(x, x_dtype, B, K, signs, block, codes, scales, biases, N, y, st);
     TB_LAUNCH_CHECK(who);
