@@ -50,7 +50,16 @@ _SIGNATURES = {
     "tb_ternary_gemm_run": (_I, [_P, _SZ, _I64, _I64, _P, _P, _P, _I64, _P, _P]),
     "tb_ternary_gemm": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
     "tb_embed_inverse": (_I, [_P, _I64, _P, _P, _P, _I64, _I64, _P, _I, _P, _P]),
+    "tb_gemv_multi_plan_size": (_SZ, [_P, _I64]),
+    "tb_gemv_multi_plan": (_I, [_P, _I64, _I, _I, _P, _SZ, ctypes.POINTER(_SZ)]),
+    "tb_ternary_gemv_multi": (_I, [_P, _P, _P, _SZ, _P]),
 }
+
+
+class TbGemvModule(ctypes.Structure):
+    """tb_gemv_module of include/tb.h (device pointers, N, K)."""
+    _fields_ = [("x", _P), ("signs", _P), ("codes", _P), ("scales", _P), ("biases", _P), ("y", _P),
+                ("N", _I64), ("K", _I64)]
 
 
 class TBError(RuntimeError):
@@ -312,3 +321,43 @@ def tb_embed_inverse(ids, codes, scales, biases, signs, block: int, out=None):
     _check(lib().tb_embed_inverse(ids.data_ptr(), T, codes.data_ptr(), scales.data_ptr(),
                                   biases.data_ptr(), V, K, _ptr(signs), block, out.data_ptr(), _stream()))
     return out
+
+
+# ---------------------------------------------------------------------------
+# multi-module decode (batch 1)
+# ---------------------------------------------------------------------------
+def tb_gemv_multi_plan(modules, block: int, x_dtype: int = TB_BF16):
+    """Plan a multi-module decode call.  modules: sequence of (x, signs, codes,
+    scales, biases, y) tensors on the GPU (x: (K,) or (1, K); y: (N,) or
+    (1, N) float32, overwritten by each run).  Returns (plan, workspace_bytes)
+    with plan a host uint8 numpy array; the plan embeds the tensors' device
+    pointers, so they must stay alive (and in place) while it is used."""
+    torch = _torch()
+    arr = (TbGemvModule * len(modules))()
+    for i, (x, signs, codes, scales, biases, y) in enumerate(modules):
+        _dev(x, "x")
+        _container(codes, scales, biases)
+        _dev(y, "y", torch.float32)
+        if signs is not None:
+            _dev(signs, "signs", torch.int8)
+        K = x.shape[-1]
+        N = codes.shape[0]
+        arr[i] = TbGemvModule(x.data_ptr(), _ptr(signs), codes.data_ptr(), scales.data_ptr(), biases.data_ptr(),
+                              y.data_ptr(), N, K)
+    size = int(lib().tb_gemv_multi_plan_size(arr, len(modules)))
+    plan = np.zeros(max(size, 64), np.uint8)
+    ws = _SZ(0)
+    _check(lib().tb_gemv_multi_plan(arr, len(modules), x_dtype, block, plan.ctypes.data, plan.nbytes,
+                                    ctypes.byref(ws)))
+    return plan, int(ws.value)
+
+
+def tb_ternary_gemv_multi(plan, plan_device, workspace):
+    """Run a plan: plan (host numpy array from tb_gemv_multi_plan), plan_device
+    (uint8 tensor on the GPU holding the same bytes), workspace (uint8 tensor of
+    the reported size).  Enqueues on the current stream."""
+    torch = _torch()
+    _dev(plan_device, "plan_device", torch.uint8)
+    _dev(workspace, "workspace", torch.uint8)
+    _check(lib().tb_ternary_gemv_multi(plan.ctypes.data, plan_device.data_ptr(), workspace.data_ptr(),
+                                       workspace.numel(), _stream()))

@@ -1,0 +1,519 @@
+// Multi-module decode: many Packed linears of one decode step (batch 1) in
+// two launches [lpnh.cn/news/2438023, "text model loading" (every packed
+// module applies fwht(x, block, signs) and then the quantized matmul);
+// kwkr.cn/news/564617, "ternary weights + folded Hadamard rotation" and
+// "packing-format engineering"].
+//
+// A decode step runs hundreds of linears of 1.5 to 360 MB each; launched one
+// by one, each pays a kernel launch and its own ramp.  Here:
+//
+// 1. multi_prep_kernel: one wave per 1024-input chunk of every module's
+//    input, the in-register MFMA transform (tb_xform.h), writing each
+//    module's exact four-limb operand image and group sums to the workspace.
+//
+// 2. multi_stream_kernel: one persistent workgroup per CU.  The host splits
+//    the concatenated list of 16-row tiles (all modules, in order) into one
+//    contiguous range per workgroup, balanced by weight bytes.  For each
+//    module in its range a workgroup copies the module's operand image into
+//    LDS once; its 8 waves then take the range's tiles round robin.  A wave
+//    streams its tiles span by span (16 rows x 4 groups: 2 KB of codes, 128 B
+//    of scales, 128 B of biases) through a ring of P register slots: lane
+//    (lane group lg, row c) loads the 32 code bytes it multiplies straight
+//    into its B-operand registers, plus its group's scale and bias, so P spans
+//    per wave are in flight while one is multiplied, and a wave waits only
+//    for its own loads (no barrier inside a module).  A span is 8
+//    v_mfma_i32_16x16x64_i8 against the exact integer activation (4 balanced
+//    base-256 limbs, one A row each, read from LDS), with the fp16 scale and
+//    bias applied in fp32; a tile's rows are written once, after its last
+//    span.
+#include <algorithm>
+#include <vector>
+
+#include "tb_xform.h"
+
+namespace tb {
+
+// ---------------------------------------------------------------------------
+// the device plan (built on the host, copied to device memory by the caller)
+// ---------------------------------------------------------------------------
+constexpr int32_t kPlanMagic = 0x4D504254;  // "TBPM"
+constexpr int kMultiWaves = 8;
+constexpr int kMultiThreads = 64 * kMultiWaves;
+constexpr int kMultiArow = 144;          // LDS bytes per (group, limb) operand row
+constexpr int kMultiImgChunk = 8 * kXfLimbs * 128;  // workspace bytes of one chunk's operand image
+constexpr int kMultiRing = 8;                       // spans in flight per wave
+constexpr int kMultiYbuf = 32;                      // finished tiles a wave holds in LDS before writing them
+constexpr int64_t kMultiLdsMax = 150 * 1024;
+
+struct MultiHeader {  // 64 bytes
+  int32_t magic, count, tasks, grid;
+  int32_t block, x_dtype, max_nch, ring;
+  int64_t modules_off, tasks_off, ranges_off, total_bytes;
+};
+struct MultiModule {  // 64 bytes
+  const void* x;
+  const int8_t* signs;
+  const uint32_t* codes;
+  const uint16_t* scales;
+  const uint16_t* biases;
+  float* y;
+  int32_t N, K;
+  int32_t tile0;  // index of the module's first 16-row tile in the concatenated list
+  int32_t ws_off; // workspace byte offset of the module's operand image (group sums follow)
+};
+static_assert(sizeof(MultiHeader) == 64 && sizeof(MultiModule) == 64, "plan layout");
+
+__host__ __device__ inline int multi_nch(int K) { return (K + 1023) >> 10; }
+
+// LDS layout of the stream kernel: the operand image, the group sums, then
+// each wave's buffer of finished output rows
+__host__ __device__ inline int64_t multi_lds_xf(int max_nch) {
+  return static_cast<int64_t>(max_nch) * 8 * kXfLimbs * kMultiArow;
+}
+__host__ __device__ inline int64_t multi_lds_ybuf(int max_nch) { return multi_lds_xf(max_nch) + max_nch * 8 * 8; }
+__host__ __device__ inline int64_t multi_lds_total(int max_nch) {
+  return multi_lds_ybuf(max_nch) + kMultiWaves * kMultiYbuf * 16 * 4;
+}
+
+// ---------------------------------------------------------------------------
+// 1. transform every chunk of every module's input
+// ---------------------------------------------------------------------------
+template <int L, int DT>
+__global__ __launch_bounds__(256) void multi_prep_kernel(const char* __restrict__ plan, char* __restrict__ ws) {
+  const MultiHeader* hd = reinterpret_cast<const MultiHeader*>(plan);
+  const int lane = threadIdx.x & 63;
+  const int task = static_cast<int>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (task >= hd->tasks) return;  // whole wave; the kernel has no barrier
+  const int2 tk = reinterpret_cast<const int2*>(plan + hd->tasks_off)[task];
+  const MultiModule md = reinterpret_cast<const MultiModule*>(plan + hd->modules_off)[tk.x];
+  const int c = tk.y;
+  constexpr int ESZ = DT == TB_F32 ? 4 : 2;
+  const auto rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(md.x), 0, md.K * ESZ, kRsrcWord3);
+  const auto rsg = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(md.signs), 0, L > 0 ? md.K : 0, kRsrcWord3);
+  XformIn<DT> in;
+  xform_issue<L, DT>(rx, rsg, static_cast<int64_t>(c) * 1024, c * 1024, lane, in);
+  const v4u* cst = reinterpret_cast<const v4u*>(&kXformConst.w[xf_mode<L>()][0][lane][0]);
+  const v4u* cst2 = reinterpret_cast<const v4u*>(&kXformConst.w[xf_mode<L>()][1][lane][0]);
+  const v4u cf[2] = {cst[0], cst[1]};
+  const v4u cs[2] = {cst2[0], cst2[1]};
+  char* img = ws + md.ws_off;
+  float2* xf = reinterpret_cast<float2*>(img + static_cast<int64_t>(multi_nch(md.K)) * kMultiImgChunk);
+  xform_chunk<L, DT>(in, 8 * c, lane, cf, cs, img, xf, 128);
+}
+
+// ---------------------------------------------------------------------------
+// 2. stream every module's weights
+// ---------------------------------------------------------------------------
+struct MultiStep {
+  uint4 w0, w1;    // 8 code words of (row, group)
+  uint16_t s, b;   // fp16 bits of the group's scale and bias
+};
+
+template <int P>
+__global__ __launch_bounds__(kMultiThreads, 1) void multi_stream_kernel(const char* __restrict__ plan,
+                                                                        const char* __restrict__ ws) {
+  constexpr int M = 16, GPS = 4;
+  extern __shared__ uint4 lds_dyn[];
+  char* const lds = reinterpret_cast<char*>(lds_dyn);
+  const MultiHeader* hd = reinterpret_cast<const MultiHeader*>(plan);
+  const MultiModule* mods = reinterpret_cast<const MultiModule*>(plan + hd->modules_off);
+  const int4 rg = reinterpret_cast<const int4*>(plan + hd->ranges_off)[blockIdx.x];
+  const int max_nch = hd->max_nch;
+  char* const lds_a = lds;
+  const float2* const lds_xf = reinterpret_cast<const float2*>(lds + multi_lds_xf(max_nch));
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lg = lane >> 4, c = lane & 15;
+  const int ar = c & 3, alg = (c >> 2) & 3;
+  const bool a_lane = alg == lg;
+  float* const ybuf = reinterpret_cast<float*>(lds + multi_lds_ybuf(max_nch)) + wave * (kMultiYbuf * 16);
+
+  int T = rg.y;
+  const int T1 = rg.z;
+  for (int m = rg.x; T < T1; ++m) {
+    const MultiModule md = mods[m];
+    const int nt = (md.N + M - 1) / M;
+    const int ta = max(T, md.tile0), tb = min(T1, md.tile0 + nt);
+    if (ta >= tb) continue;
+    T = tb;
+    const int K = md.K, G = K / kGroup, RB = K / 4;
+    const int S = (G + GPS - 1) / GPS;
+    const int nch = multi_nch(K);
+    // the module's operand image and group sums into LDS
+    {
+      const char* img = ws + md.ws_off;
+      const int rows = nch * 8 * kXfLimbs;
+      for (int i = tid; i < rows * 8; i += kMultiThreads) {
+        const int r = i >> 3, q = i & 7;
+        *reinterpret_cast<uint4*>(lds_a + r * kMultiArow + q * 16) =
+            *reinterpret_cast<const uint4*>(img + r * 128 + q * 16);
+      }
+      const float2* xfg = reinterpret_cast<const float2*>(img + static_cast<int64_t>(nch) * kMultiImgChunk);
+      for (int i = tid; i < nch * 8; i += kMultiThreads) const_cast<float2*>(lds_xf)[i] = xfg[i];
+    }
+    __syncthreads();
+
+    // this wave's tiles: ta + wave + 8 j, j < ntw; steps k = j * S + s
+    const int ntw = ta + wave < tb ? (tb - ta - wave + kMultiWaves - 1) / kMultiWaves : 0;
+    const int nsteps = ntw * S;
+    const auto rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(md.codes), 0, md.N * RB, kRsrcWord3);
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(md.scales), 0, md.N * G * 2, kRsrcWord3);
+    const auto rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(md.biases), 0, md.N * G * 2, kRsrcWord3);
+    const auto ry = __builtin_amdgcn_make_buffer_rsrc(md.y, 0, md.N * 4, kRsrcWord3);
+    // Finished rows wait in the wave's LDS buffer and are written in bursts:
+    // a store in the stream would make the compiler drain every load before
+    // the next use of one.  Tile j0 + i of the wave sits at ybuf[16 i + c].
+    int j0 = 0;
+    auto flush = [&](int upto) {  // write tiles j0 .. upto - 1 of this wave
+      for (int i = lane; i < (upto - j0) * 16; i += 64) {
+        const int row = (ta - md.tile0 + wave + kMultiWaves * (j0 + (i >> 4))) * M + (i & 15);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ybuf[i]), ry, row * 4, 0, 0);  // rows past N: dropped
+      }
+      j0 = upto;
+    };
+    // Lane (lg, c) loads, for step (tile, span s), the 8 code words of row
+    // tile*16 + c, group 4 s + lg (32 bytes) and that group's scale and bias.
+    // A step past the end loads nothing useful: its offsets lie beyond every
+    // buffer and read as zero, so every ring slot is refilled unconditionally
+    // and the loads stay in one static order.
+    int is = 0, it = 0;  // span and tile of the next step to load
+    const int lane_c = (ta - md.tile0 + wave) * M * RB + c * RB + lg * 32;
+    const int lane_s = ((ta - md.tile0 + wave) * M + c) * G * 2 + lg * 2;
+    auto load = [&](int k, MultiStep& st) {
+      const bool live = k < nsteps;
+      const int oc = live ? lane_c + it * (kMultiWaves * M * RB) + is * 128 : kOob;
+      const int os = live ? lane_s + it * (kMultiWaves * M * G * 2) + is * (GPS * 2) : kOob;
+      const v4u u0 = __builtin_amdgcn_raw_buffer_load_b128(rc, oc, 0, 0);
+      const v4u u1 = __builtin_amdgcn_raw_buffer_load_b128(rc, oc + 16, 0, 0);
+      st.w0 = make_uint4(u0.x, u0.y, u0.z, u0.w);
+      st.w1 = make_uint4(u1.x, u1.y, u1.z, u1.w);
+      st.s = __builtin_amdgcn_raw_buffer_load_b16(rs, os, 0, 0);
+      st.b = __builtin_amdgcn_raw_buffer_load_b16(rb, os, 0, 0);
+      if (++is == S) {
+        is = 0;
+        ++it;
+      }
+    };
+    MultiStep ring[P];
+#pragma unroll
+    for (int k = 0; k < P; ++k) load(k, ring[k]);
+
+    uint4 av[kWordsPerGroup];
+#pragma unroll
+    for (int w = 0; w < kWordsPerGroup; ++w) av[w] = make_uint4(0, 0, 0, 0);
+    float yacc = 0.f;
+    int s = 0, j = 0;  // span and tile of the step being consumed
+    for (int base = 0; base < nsteps; base += P) {
+#pragma unroll
+      for (int sl = 0; sl < P; ++sl) {
+        if (base + sl < nsteps) {
+          const MultiStep cur = ring[sl];
+          const float2 xf = lds_xf[s * GPS + lg];
+          if (a_lane) {
+            const uint4* ap = reinterpret_cast<const uint4*>(lds_a + ((s * GPS + alg) * kXfLimbs + ar) * kMultiArow);
+#pragma unroll
+            for (int w = 0; w < kWordsPerGroup; ++w) av[w] = ap[w];
+          }
+          v4i bop[kWordsPerGroup];
+          bop[0] = decode_word(cur.w0.x);
+          bop[1] = decode_word(cur.w0.y);
+          bop[2] = decode_word(cur.w0.z);
+          bop[3] = decode_word(cur.w0.w);
+          bop[4] = decode_word(cur.w1.x);
+          bop[5] = decode_word(cur.w1.y);
+          bop[6] = decode_word(cur.w1.z);
+          bop[7] = decode_word(cur.w1.w);
+          v4i acc0 = {}, acc1 = {};
+#pragma unroll
+          for (int w = 0; w < kWordsPerGroup; w += 2) {
+            acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)av[w].x, (int)av[w].y, (int)av[w].z, (int)av[w].w},
+                                                         bop[w], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                v4i{(int)av[w + 1].x, (int)av[w + 1].y, (int)av[w + 1].z, (int)av[w + 1].w}, bop[w + 1], acc1, 0, 0, 0);
+          }
+          const v4i acc = acc0 + acc1;
+          const bool gin = s * GPS + lg < G;
+          const float sc = gin ? half_bits_to_float(cur.s) : 0.f;
+          const float bi = gin ? half_bits_to_float(cur.b) : 0.f;
+          const float v = static_cast<float>(acc[3]) * 16777216.f + static_cast<float>(acc[2]) * 65536.f +
+                          static_cast<float>(acc[1]) * 256.f + static_cast<float>(acc[0]);
+          yacc += sc * (v * xf.y) + bi * xf.x;
+          if (++s == S) {
+            // tile done: add the 4 lane groups and park its rows
+            float t = yacc + xor_lane(yacc, 4, lane);
+            t += xor_lane(t, 5, lane);
+            if (lg == 0) ybuf[(j - j0) * 16 + c] = t;
+            yacc = 0.f;
+            s = 0;
+            if (++j - j0 == kMultiYbuf) flush(j);
+          }
+        }
+        load(base + sl + P, ring[sl]);
+      }
+    }
+    flush(j);
+    __syncthreads();  // the next module's image replaces this one
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+static int multi_device_cus() {
+  int dev = 0, cus = 256;
+  (void)hipGetDevice(&dev);
+  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  return cus;
+}
+
+
+static inline int64_t align64(int64_t v) { return (v + 63) & ~int64_t(63); }
+
+// byte offsets of the plan's sections (each 64-byte aligned: the kernels read
+// them with vector and scalar loads of up to 16 bytes)
+struct PlanOffsets {
+  int64_t modules, tasks, ranges, total;
+};
+static PlanOffsets plan_offsets(int64_t count, int64_t ntasks, int64_t grid) {
+  PlanOffsets o;
+  o.modules = sizeof(MultiHeader);
+  o.tasks = align64(o.modules + count * static_cast<int64_t>(sizeof(MultiModule)));
+  o.ranges = align64(o.tasks + ntasks * 8);
+  o.total = align64(o.ranges + grid * 16);
+  return o;
+}
+
+static int64_t multi_total_tasks(const tb_gemv_module* mods, int64_t count) {
+  int64_t t = 0;
+  for (int64_t i = 0; i < count; ++i)
+    if (mods[i].N > 0) t += multi_nch(static_cast<int>(mods[i].K));
+  return t;
+}
+
+}  // namespace tb
+
+using namespace tb;
+
+extern "C" size_t tb_gemv_multi_plan_size(const tb_gemv_module* mods, int64_t count) {
+  if (!mods || count <= 0) return 0;
+  return static_cast<size_t>(plan_offsets(count, multi_total_tasks(mods, count), multi_device_cus()).total);
+}
+
+extern "C" int tb_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int x_dtype, int block, void* plan,
+                                  size_t plan_bytes, size_t* workspace_bytes) {
+  const char* who = "tb_gemv_multi_plan";
+  if (!mods || count <= 0 || !plan || !workspace_bytes) {
+    set_error("%s: null argument or empty module list", who);
+    return TB_ERR_ARG;
+  }
+  if (!(block == 0 || block == 512 || block == 1024)) {
+    set_error("%s: block %d: the multi-module path takes 0, 512 or 1024", who, block);
+    return block_known(block) ? TB_ERR_UNSUPPORTED : TB_ERR_BLOCK;
+  }
+  if (x_dtype != TB_F32 && x_dtype != TB_BF16) {
+    set_error("%s: x_dtype %d is not TB_F32 or TB_BF16", who, x_dtype);
+    return TB_ERR_DTYPE;
+  }
+  if (count > (1 << 20)) {
+    set_error("%s: %lld modules is more than the plan format takes", who, (long long)count);
+    return TB_ERR_ARG;
+  }
+  int max_nch = 1;
+  int64_t tiles = 0, ws = 0, cost = 0;
+  for (int64_t i = 0; i < count; ++i) {
+    const tb_gemv_module& m = mods[i];
+    if (m.N < 0 || m.K <= 0) {
+      set_error("%s: module %lld: N=%lld K=%lld", who, (long long)i, (long long)m.N, (long long)m.K);
+      return TB_ERR_ARG;
+    }
+    if (m.K % 256 != 0 || (block > 0 && m.K % block != 0)) {
+      set_error("%s: module %lld: K=%lld must be a multiple of 256 and of the block", who, (long long)i,
+                (long long)m.K);
+      return TB_ERR_SHAPE;
+    }
+    if (m.N == 0) continue;
+    if (!m.x || !m.codes || !m.scales || !m.biases || !m.y || (block > 0) != (m.signs != nullptr)) {
+      set_error("%s: module %lld: null pointer (signs must be given exactly when block > 0)", who, (long long)i);
+      return TB_ERR_ARG;
+    }
+    if (!aligned(m.x, 16) || !aligned(m.codes, 16) || !aligned(m.scales, 4) || !aligned(m.biases, 4) ||
+        !aligned(m.y, 4) || (m.signs && !aligned(m.signs, 4))) {
+      set_error("%s: module %lld: x and codes need 16-byte, scales, biases, y and signs 4-byte alignment", who,
+                (long long)i);
+      return TB_ERR_ALIGN;
+    }
+    if (m.N > (1 << 26) || m.K > (1 << 20) || m.N * (m.K / 4) > INT32_MAX) {
+      set_error("%s: module %lld: N=%lld K=%lld is too large for one module", who, (long long)i, (long long)m.N,
+                (long long)m.K);
+      return TB_ERR_SHAPE;
+    }
+    const int nch = multi_nch(static_cast<int>(m.K));
+    max_nch = std::max(max_nch, nch);
+    tiles += (m.N + 15) / 16;
+    ws += static_cast<int64_t>(nch) * (kMultiImgChunk + 64);
+    cost += (m.N + 15) / 16 * (m.K / 128 + 2);
+  }
+  const int ring = kMultiRing;
+  if (multi_lds_total(max_nch) > kMultiLdsMax) {
+    set_error("%s: K up to %d takes too much LDS for the stream kernel", who, max_nch * 1024);
+    return TB_ERR_UNSUPPORTED;
+  }
+  if (tiles >= INT32_MAX || ws >= INT32_MAX) {
+    set_error("%s: the module list is too large for one plan", who);
+    return TB_ERR_SHAPE;
+  }
+  const int grid = multi_device_cus();
+  const int64_t ntasks = multi_total_tasks(mods, count);
+  const PlanOffsets po = plan_offsets(count, ntasks, grid);
+  const size_t need = static_cast<size_t>(po.total);
+  if (plan_bytes < need) {
+    set_error("%s: plan buffer of %zu bytes, %zu needed", who, plan_bytes, need);
+    return TB_ERR_WORKSPACE;
+  }
+  char* p = static_cast<char*>(plan);
+  std::memset(p, 0, need);
+  MultiHeader hd{};
+  hd.magic = kPlanMagic;
+  hd.count = static_cast<int32_t>(count);
+  hd.tasks = static_cast<int32_t>(ntasks);
+  hd.grid = grid;
+  hd.block = block;
+  hd.x_dtype = x_dtype;
+  hd.max_nch = max_nch;
+  hd.ring = ring;
+  hd.modules_off = po.modules;
+  hd.tasks_off = po.tasks;
+  hd.ranges_off = po.ranges;
+  hd.total_bytes = static_cast<int64_t>(need);
+  std::memcpy(p, &hd, sizeof hd);
+  MultiModule* md = reinterpret_cast<MultiModule*>(p + hd.modules_off);
+  int32_t* tk = reinterpret_cast<int32_t*>(p + hd.tasks_off);
+  std::vector<int64_t> tile_cost;  // per module: cost of one tile
+  int64_t t0 = 0, off = 0, nt = 0;
+  for (int64_t i = 0; i < count; ++i) {
+    const tb_gemv_module& m = mods[i];
+    MultiModule d{};
+    d.x = m.x;
+    d.signs = m.signs;
+    d.codes = m.codes;
+    d.scales = m.scales;
+    d.biases = m.biases;
+    d.y = m.y;
+    d.N = static_cast<int32_t>(m.N);
+    d.K = static_cast<int32_t>(m.K);
+    d.tile0 = static_cast<int32_t>(t0);
+    d.ws_off = static_cast<int32_t>(off);
+    std::memcpy(md + i, &d, sizeof d);
+    if (m.N == 0) continue;
+    const int nch = multi_nch(static_cast<int>(m.K));
+    for (int c = 0; c < nch; ++c) {
+      tk[2 * nt] = static_cast<int32_t>(i);
+      tk[2 * nt + 1] = c;
+      ++nt;
+    }
+    t0 += (m.N + 15) / 16;
+    off += static_cast<int64_t>(nch) * (kMultiImgChunk + 64);
+  }
+  // contiguous tile ranges of about equal weight bytes: workgroup g takes the
+  // tiles whose cumulative cost starts in [g C / grid, (g + 1) C / grid)
+  int32_t* rg = reinterpret_cast<int32_t*>(p + hd.ranges_off);
+  {
+    int64_t acc = 0, tile = 0;
+    int g = 0;
+    int64_t m_of_g = 0;
+    rg[0] = 0;
+    rg[1] = 0;
+    for (int64_t i = 0; i < count && g < grid; ++i) {
+      const tb_gemv_module& m = mods[i];
+      if (m.N == 0) continue;
+      const int64_t ntm = (m.N + 15) / 16, tc = m.K / 128 + 2;
+      for (int64_t t = 0; t < ntm; ++t, ++tile) {
+        // tile starts at cost acc: move to the workgroup that owns acc
+        while (g + 1 < grid && acc * grid >= (g + 1) * cost) {
+          rg[4 * g + 2] = static_cast<int32_t>(tile);
+          rg[4 * g + 3] = 0;
+          ++g;
+          rg[4 * g] = static_cast<int32_t>(i);
+          rg[4 * g + 1] = static_cast<int32_t>(tile);
+        }
+        acc += tc;
+      }
+      m_of_g = i;
+    }
+    (void)m_of_g;
+    rg[4 * g + 2] = static_cast<int32_t>(tiles);
+    rg[4 * g + 3] = 0;
+    for (int h = g + 1; h < grid; ++h) {  // workgroups without tiles
+      rg[4 * h] = 0;
+      rg[4 * h + 1] = static_cast<int32_t>(tiles);
+      rg[4 * h + 2] = static_cast<int32_t>(tiles);
+      rg[4 * h + 3] = 0;
+    }
+  }
+  *workspace_bytes = static_cast<size_t>(std::max<int64_t>(ws, 256));
+  return TB_OK;
+}
+
+template <int L, int DT>
+static void multi_prep_launch(const void* plan, void* ws, int tasks, hipStream_t st) {
+  hipLaunchKernelGGL((multi_prep_kernel<L, DT>), dim3((tasks + 3) / 4), dim3(256), 0, st,
+                     static_cast<const char*>(plan), static_cast<char*>(ws));
+}
+
+template <int P>
+static void multi_stream_launch(const void* plan, const void* ws, int grid, size_t lds, hipStream_t st) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(multi_stream_kernel<P>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kMultiLdsMax));
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(multi_stream_kernel<P>, dim3(grid), dim3(kMultiThreads), lds, st,
+                     static_cast<const char*>(plan), static_cast<const char*>(ws));
+}
+
+extern "C" int tb_ternary_gemv_multi(const void* plan_host, const void* plan_device, void* workspace,
+                                     size_t ws_bytes, void* stream) {
+  const char* who = "tb_ternary_gemv_multi";
+  if (!plan_host || !plan_device || !workspace) {
+    set_error("%s: null plan or workspace", who);
+    return TB_ERR_ARG;
+  }
+  MultiHeader hd;
+  std::memcpy(&hd, plan_host, sizeof hd);
+  if (hd.magic != kPlanMagic || hd.count <= 0 || hd.grid <= 0 || hd.ring != kMultiRing) {
+    set_error("%s: the host plan was not built by tb_gemv_multi_plan", who);
+    return TB_ERR_ARG;
+  }
+  if (!aligned(plan_device, 16) || !aligned(workspace, 16)) {
+    set_error("%s: plan and workspace need 16-byte alignment", who);
+    return TB_ERR_ALIGN;
+  }
+  // the workspace size the plan needs: the last module's image end
+  const MultiModule* md = reinterpret_cast<const MultiModule*>(static_cast<const char*>(plan_host) + hd.modules_off);
+  int64_t need = 256;
+  for (int i = 0; i < hd.count; ++i)
+    if (md[i].N > 0) need = std::max<int64_t>(need, md[i].ws_off + static_cast<int64_t>(multi_nch(md[i].K)) * (kMultiImgChunk + 64));
+  if (ws_bytes < static_cast<size_t>(need)) {
+    set_error("%s: workspace of %zu bytes, %lld needed", who, ws_bytes, (long long)need);
+    return TB_ERR_WORKSPACE;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hd.tasks > 0) {
+    const int L = hd.block;
+    if (hd.x_dtype == TB_F32) {
+      if (L == 0) multi_prep_launch<0, TB_F32>(plan_device, workspace, hd.tasks, st);
+      else if (L == 512) multi_prep_launch<512, TB_F32>(plan_device, workspace, hd.tasks, st);
+      else multi_prep_launch<1024, TB_F32>(plan_device, workspace, hd.tasks, st);
+    } else {
+      if (L == 0) multi_prep_launch<0, TB_BF16>(plan_device, workspace, hd.tasks, st);
+      else if (L == 512) multi_prep_launch<512, TB_BF16>(plan_device, workspace, hd.tasks, st);
+      else multi_prep_launch<1024, TB_BF16>(plan_device, workspace, hd.tasks, st);
+    }
+    TB_LAUNCH_CHECK(who);
+    const size_t lds = static_cast<size_t>(multi_lds_total(hd.max_nch));
+    multi_stream_launch<kMultiRing>(plan_device, workspace, hd.grid, lds, st);
+    TB_LAUNCH_CHECK(who);
+  }
+  return TB_OK;
+}

@@ -190,6 +190,56 @@ int tb_ternary_gemm_run(const void* workspace, size_t ws_bytes, int64_t M, int64
                         const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
                         int64_t N, float* y, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Multi-module decode [P3 "text model loading": every packed module of the
+ * model applies fwht(x, block, signs) and the quantized matmul; a decode step
+ * runs all of them].  Many batch-1 Packed linears in two launches: one
+ * transforms every module's input, one persistent kernel streams every
+ * module's weights.  Each module is the single-row case of tb_ternary_gemv:
+ *   y_i[n] = sum_k W~_i[n][k] (R_i x_i)[k]
+ * ------------------------------------------------------------------------ */
+
+/* One module (all pointers are device pointers).  x: K activations of the
+ * call's x_dtype, 16-byte aligned; signs: K int8 (+-1), 4-byte aligned, or
+ * NULL when block = 0; codes: N x K/16 uint32, 16-byte aligned; scales,
+ * biases: N x K/128 fp16 bits, 4-byte aligned; y: N fp32, overwritten.
+ * K % 256 == 0 and K % block == 0; N may be 0 (the module is skipped). */
+typedef struct tb_gemv_module {
+  const void* x;
+  const int8_t* signs;
+  const uint32_t* codes;
+  const uint16_t* scales;
+  const uint16_t* biases;
+  float* y;
+  int64_t N;
+  int64_t K;
+} tb_gemv_module;
+
+/* Bytes of the plan for this module list on the current device (0 for an
+ * empty list). */
+size_t tb_gemv_multi_plan_size(const tb_gemv_module* mods, int64_t count);
+
+/* Build the plan (host memory, plan_bytes >= tb_gemv_multi_plan_size) for the
+ * modules (host array), all sharing x_dtype and block (0, 512 or 1024), and
+ * report the workspace the run needs.  The plan holds the module table, the
+ * transform tasks and a split of all modules' 16-row output tiles into one
+ * range per workgroup of about equal weight bytes; it embeds the device
+ * pointers of the modules, so it stays valid while those buffers do.  Errors:
+ * TB_ERR_ARG, TB_ERR_SHAPE (K % 256 or K % block), TB_ERR_BLOCK /
+ * TB_ERR_UNSUPPORTED (block 2048/4096, or K too large for the kernel's LDS),
+ * TB_ERR_DTYPE, TB_ERR_ALIGN, TB_ERR_WORKSPACE (plan buffer too small). */
+int tb_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int x_dtype, int block,
+                       void* plan, size_t plan_bytes, size_t* workspace_bytes);
+
+/* Run a plan: plan_host is the buffer tb_gemv_multi_plan filled (read on the
+ * host for the launch sizes), plan_device a copy of it in device memory
+ * (16-byte aligned, read by the kernels; the caller owns both).  workspace:
+ * device scratch of the reported size, 16-byte aligned, needing no
+ * initialisation, not shared with a concurrent call.  Enqueues two kernels
+ * on the stream; every module's y is overwritten. */
+int tb_ternary_gemv_multi(const void* plan_host, const void* plan_device,
+                          void* workspace, size_t ws_bytes, void* stream);
+
 /* Embedding lookup with the inverse transform [P3 "text model loading"]:
  *   out[t] = signs .* (H_L W~[ids[t]]) / sqrt(L)   blockwise  (block > 0)
  *   out[t] = W~[ids[t]]                                      (block = 0)

@@ -1,0 +1,89 @@
+"""Parity of the multi-module decode path (tb_gemv_multi_plan +
+tb_ternary_gemv_multi) with the fp64 oracle, module by module, on the GPU."""
+import numpy as np
+import pytest
+
+import hadamard_rotated_quantized_amd as tb
+import oracle
+from hadamard_rotated_quantized_amd import synth
+from gpu_util import announce, compare, cuda_available, pack_to_device, signs_to_device, torch, x_to_device
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not cuda_available(), reason="needs a GPU")]
+
+
+def _run_multi(shapes, block, xd, seed):
+    T = torch()
+    probs, mods, keep = [], [], []
+    for i, (N, K) in enumerate(shapes):
+        p = synth.make_problem("multi", N, K, 1, [seed, i, N, K], xd, block)
+        codes, s, b = pack_to_device(p.t, p.scales)
+        x = x_to_device(p)
+        sg = signs_to_device(p.signs)
+        y = T.full((1, N), float("nan"), dtype=T.float32, device="cuda")
+        mods.append((x, sg, codes, s, b, y))
+        probs.append(p)
+    plan, wsb = tb.tb_gemv_multi_plan(mods, block, tb.TB_F32 if xd == "f32" else tb.TB_BF16)
+    pd = T.from_numpy(plan).cuda()
+    ws = T.empty(wsb, dtype=T.uint8, device="cuda")
+    tb.tb_ternary_gemv_multi(plan, pd, ws)
+    T.cuda.synchronize()
+    return probs, mods, plan, pd, ws
+
+
+CASES = [
+    ("bf16", 1024, [(1, 1024), (45, 2048), (300, 5120), (1000, 6144), (16, 17408), (0, 1024), (4099, 1024),
+                    (31, 3072)]),
+    ("f32", 512, [(17, 1024), (33, 1536), (200, 512)]),
+    ("bf16", 0, [(45, 256), (300, 768), (16, 1024)]),
+]
+
+
+@pytest.mark.parametrize("xd,block,shapes", CASES)
+def test_multi_matches_oracle(xd, block, shapes):
+    announce(f"multi x={xd} block={block} shapes={shapes}")
+    probs, mods, *_ = _run_multi(shapes, block, xd, 70)
+    for p, m in zip(probs, mods):
+        if p.N == 0:
+            continue
+        oc, osc, ob = oracle.pack(p.t, p.scales)
+        want = oracle.packed_linear(p.x64, p.signs, block, oc, osc, ob)
+        compare(m[5].cpu().numpy(), want, f"multi module N={p.N} K={p.K}")
+
+
+def test_multi_rerun_is_bitwise_stable_and_matches_single_calls():
+    announce("multi rerun + single-call agreement")
+    T = torch()
+    shapes = [(300, 5120), (1024, 5120), (77, 6144), (513, 17408)]
+    probs, mods, plan, pd, ws = _run_multi(shapes, 1024, "bf16", 71)
+    first = [m[5].clone() for m in mods]
+    for m in mods:
+        m[5].fill_(float("nan"))
+    tb.tb_ternary_gemv_multi(plan, pd, ws)
+    T.cuda.synchronize()
+    for f, m in zip(first, mods):
+        assert T.equal(f, m[5])
+    for p, m in zip(probs, mods):
+        x, sg, codes, s, b, y = m
+        y1 = tb.tb_ternary_gemv(x, sg, 1024, codes, s, b)
+        T.cuda.synchronize()
+        d = (y1.double() - y.double()).abs().max().item()
+        assert d <= 1e-6 * y1.abs().max().item(), (p.N, p.K, d)
+
+
+def test_multi_graph_replays_match_eager():
+    announce("multi graph replay")
+    T = torch()
+    shapes = [(600, 5120), (100, 17408)]
+    probs, mods, plan, pd, ws = _run_multi(shapes, 1024, "bf16", 72)
+    eager = [m[5].clone() for m in mods]
+    g = T.cuda.CUDAGraph()
+    with T.cuda.graph(g):
+        tb.tb_ternary_gemv_multi(plan, pd, ws)
+    for r in range(3):
+        for m in mods:
+            m[5].zero_()
+        T.cuda.synchronize()
+        g.replay()
+        T.cuda.synchronize()
+        for e, m in zip(eager, mods):
+            assert T.equal(e, m[5]), r
