@@ -37,11 +37,10 @@ namespace tb {
 // the device plan (built on the host, copied to device memory by the caller)
 // ---------------------------------------------------------------------------
 constexpr int32_t kPlanMagic = 0x4D504254;  // "TBPM"
-constexpr int kMultiWaves = 8;
-constexpr int kMultiThreads = 64 * kMultiWaves;
+constexpr int kMultiWaves = 8;                      // waves per streaming workgroup
 constexpr int kMultiArow = 144;          // LDS bytes per (group, limb) operand row
 constexpr int kMultiImgChunk = 8 * kXfLimbs * 128;  // workspace bytes of one chunk's operand image
-constexpr int kMultiRing = 8;                       // spans in flight per wave
+constexpr int kMultiRing = 4;                       // span pairs in flight per wave
 constexpr int kMultiYbuf = 32;                      // finished tiles a wave holds in LDS before writing them
 constexpr int64_t kMultiLdsMax = 150 * 1024;
 
@@ -104,14 +103,15 @@ __global__ __launch_bounds__(256) void multi_prep_kernel(const char* __restrict_
 // ---------------------------------------------------------------------------
 // 2. stream every module's weights
 // ---------------------------------------------------------------------------
-struct MultiStep {
-  uint4 w0, w1;    // 8 code words of (row, group)
-  uint16_t s, b;   // fp16 bits of the group's scale and bias
+struct MultiPair {
+  uint4 w[4];  // 8 code words of (row, group) in each of the pair's two spans
+  uint4 s, b;  // 8 fp16 scales / biases of the row's 8 groups of the pair
 };
 
-template <int P>
-__global__ __launch_bounds__(kMultiThreads, 1) void multi_stream_kernel(const char* __restrict__ plan,
-                                                                        const char* __restrict__ ws) {
+template <int NW, int P>
+__global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __restrict__ plan,
+                                                                  const char* __restrict__ ws) {
+  constexpr int kMultiThreads = 64 * NW;
   constexpr int M = 16, GPS = 4;
   extern __shared__ uint4 lds_dyn[];
   char* const lds = reinterpret_cast<char*>(lds_dyn);
@@ -153,9 +153,12 @@ __global__ __launch_bounds__(kMultiThreads, 1) void multi_stream_kernel(const ch
     }
     __syncthreads();
 
-    // this wave's tiles: ta + wave + 8 j, j < ntw; steps k = j * S + s
-    const int ntw = ta + wave < tb ? (tb - ta - wave + kMultiWaves - 1) / kMultiWaves : 0;
-    const int nsteps = ntw * S;
+    // this wave's tiles: ta + wave + NW j, j < ntw.  The unit of the ring is
+    // a pair of spans (2 p, 2 p + 1) of one tile: P2 = ceil(S / 2) pairs per
+    // tile, pair steps k = j * P2 + p.
+    const int P2 = (S + 1) >> 1;
+    const int ntw = ta + wave < tb ? (tb - ta - wave + NW - 1) / NW : 0;
+    const int nsteps = ntw * P2;
     const auto rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(md.codes), 0, md.N * RB, kRsrcWord3);
     const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(md.scales), 0, md.N * G * 2, kRsrcWord3);
     const auto rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(md.biases), 0, md.N * G * 2, kRsrcWord3);
@@ -166,35 +169,40 @@ __global__ __launch_bounds__(kMultiThreads, 1) void multi_stream_kernel(const ch
     int j0 = 0;
     auto flush = [&](int upto) {  // write tiles j0 .. upto - 1 of this wave
       for (int i = lane; i < (upto - j0) * 16; i += 64) {
-        const int row = (ta - md.tile0 + wave + kMultiWaves * (j0 + (i >> 4))) * M + (i & 15);
+        const int row = (ta - md.tile0 + wave + NW * (j0 + (i >> 4))) * M + (i & 15);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ybuf[i]), ry, row * 4, 0, 0);  // rows past N: dropped
       }
       j0 = upto;
     };
-    // Lane (lg, c) loads, for step (tile, span s), the 8 code words of row
-    // tile*16 + c, group 4 s + lg (32 bytes) and that group's scale and bias.
-    // A step past the end loads nothing useful: its offsets lie beyond every
-    // buffer and read as zero, so every ring slot is refilled unconditionally
-    // and the loads stay in one static order.
-    int is = 0, it = 0;  // span and tile of the next step to load
+    // Lane (lg, c) loads, for pair (tile, p), the 8 code words of row
+    // tile*16 + c in groups 8 p + lg and 8 p + 4 + lg (2 x 32 bytes), and the
+    // 8 consecutive fp16 scales (and biases) of groups 8 p .. 8 p + 7 of that
+    // row -- one 16-byte load each, shared by the row's 4 lane groups.  A pair
+    // past the end loads nothing useful: its offsets lie beyond every buffer
+    // and read as zero, so every ring slot is refilled unconditionally and the
+    // loads stay in one static order.
+    int ip = 0, it = 0;  // pair and tile of the next step to load
     const int lane_c = (ta - md.tile0 + wave) * M * RB + c * RB + lg * 32;
-    const int lane_s = ((ta - md.tile0 + wave) * M + c) * G * 2 + lg * 2;
-    auto load = [&](int k, MultiStep& st) {
+    const int lane_s = ((ta - md.tile0 + wave) * M + c) * G * 2;
+    auto load = [&](int k, MultiPair& st) {
       const bool live = k < nsteps;
-      const int oc = live ? lane_c + it * (kMultiWaves * M * RB) + is * 128 : kOob;
-      const int os = live ? lane_s + it * (kMultiWaves * M * G * 2) + is * (GPS * 2) : kOob;
-      const v4u u0 = __builtin_amdgcn_raw_buffer_load_b128(rc, oc, 0, 0);
-      const v4u u1 = __builtin_amdgcn_raw_buffer_load_b128(rc, oc + 16, 0, 0);
-      st.w0 = make_uint4(u0.x, u0.y, u0.z, u0.w);
-      st.w1 = make_uint4(u1.x, u1.y, u1.z, u1.w);
-      st.s = __builtin_amdgcn_raw_buffer_load_b16(rs, os, 0, 0);
-      st.b = __builtin_amdgcn_raw_buffer_load_b16(rb, os, 0, 0);
-      if (++is == S) {
-        is = 0;
+      const int oc = live ? lane_c + it * (NW * M * RB) + ip * 256 : kOob;
+      const int os = live ? lane_s + it * (NW * M * G * 2) + ip * 16 : kOob;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const v4u u = __builtin_amdgcn_raw_buffer_load_b128(rc, oc + (h >> 1) * 128 + (h & 1) * 16, 0, 0);
+        st.w[h] = make_uint4(u.x, u.y, u.z, u.w);
+      }
+      const v4u us = __builtin_amdgcn_raw_buffer_load_b128(rs, os, 0, 0);
+      const v4u ub = __builtin_amdgcn_raw_buffer_load_b128(rb, os, 0, 0);
+      st.s = make_uint4(us.x, us.y, us.z, us.w);
+      st.b = make_uint4(ub.x, ub.y, ub.z, ub.w);
+      if (++ip == P2) {
+        ip = 0;
         ++it;
       }
     };
-    MultiStep ring[P];
+    MultiPair ring[P];
 #pragma unroll
     for (int k = 0; k < P; ++k) load(k, ring[k]);
 
@@ -202,53 +210,63 @@ __global__ __launch_bounds__(kMultiThreads, 1) void multi_stream_kernel(const ch
 #pragma unroll
     for (int w = 0; w < kWordsPerGroup; ++w) av[w] = make_uint4(0, 0, 0, 0);
     float yacc = 0.f;
-    int s = 0, j = 0;  // span and tile of the step being consumed
+    int p = 0, j = 0;  // pair and tile of the step being consumed
+    // one span: 8 MFMAs of the lane's (row, group) words against the A rows
+    // of groups 4 s .. 4 s + 3, then the fp16 scale and bias in fp32
+    auto span = [&](int s, const uint4& w0, const uint4& w1, uint32_t sdw, uint32_t bdw) {
+      const float2 xf = lds_xf[s * GPS + lg];
+      if (a_lane) {
+        const uint4* ap = reinterpret_cast<const uint4*>(lds_a + ((s * GPS + alg) * kXfLimbs + ar) * kMultiArow);
+#pragma unroll
+        for (int w = 0; w < kWordsPerGroup; ++w) av[w] = ap[w];
+      }
+      v4i bop[kWordsPerGroup];
+      bop[0] = decode_word(w0.x);
+      bop[1] = decode_word(w0.y);
+      bop[2] = decode_word(w0.z);
+      bop[3] = decode_word(w0.w);
+      bop[4] = decode_word(w1.x);
+      bop[5] = decode_word(w1.y);
+      bop[6] = decode_word(w1.z);
+      bop[7] = decode_word(w1.w);
+      v4i acc0 = {}, acc1 = {};
+#pragma unroll
+      for (int w = 0; w < kWordsPerGroup; w += 2) {
+        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)av[w].x, (int)av[w].y, (int)av[w].z, (int)av[w].w},
+                                                     bop[w], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+            v4i{(int)av[w + 1].x, (int)av[w + 1].y, (int)av[w + 1].z, (int)av[w + 1].w}, bop[w + 1], acc1, 0, 0, 0);
+      }
+      const v4i acc = acc0 + acc1;
+      // the lane's fp16 scale / bias: half (lg & 1) of the dword it was given
+      const float sc = half_bits_to_float(static_cast<uint16_t>(sdw >> (16 * (lg & 1))));
+      const float bi = half_bits_to_float(static_cast<uint16_t>(bdw >> (16 * (lg & 1))));
+      const float v = static_cast<float>(acc[3]) * 16777216.f + static_cast<float>(acc[2]) * 65536.f +
+                      static_cast<float>(acc[1]) * 256.f + static_cast<float>(acc[0]);
+      // groups past K (padding of the last span) contribute nothing
+      yacc += s * GPS + lg < G ? sc * (v * xf.y) + bi * xf.x : 0.f;
+    };
     for (int base = 0; base < nsteps; base += P) {
 #pragma unroll
       for (int sl = 0; sl < P; ++sl) {
+        const MultiPair cur = ring[sl];
+        load(base + sl + P, ring[sl]);  // refill the slot before computing on its data
         if (base + sl < nsteps) {
-          const MultiStep cur = ring[sl];
-          const float2 xf = lds_xf[s * GPS + lg];
-          if (a_lane) {
-            const uint4* ap = reinterpret_cast<const uint4*>(lds_a + ((s * GPS + alg) * kXfLimbs + ar) * kMultiArow);
-#pragma unroll
-            for (int w = 0; w < kWordsPerGroup; ++w) av[w] = ap[w];
-          }
-          v4i bop[kWordsPerGroup];
-          bop[0] = decode_word(cur.w0.x);
-          bop[1] = decode_word(cur.w0.y);
-          bop[2] = decode_word(cur.w0.z);
-          bop[3] = decode_word(cur.w0.w);
-          bop[4] = decode_word(cur.w1.x);
-          bop[5] = decode_word(cur.w1.y);
-          bop[6] = decode_word(cur.w1.z);
-          bop[7] = decode_word(cur.w1.w);
-          v4i acc0 = {}, acc1 = {};
-#pragma unroll
-          for (int w = 0; w < kWordsPerGroup; w += 2) {
-            acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)av[w].x, (int)av[w].y, (int)av[w].z, (int)av[w].w},
-                                                         bop[w], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                v4i{(int)av[w + 1].x, (int)av[w + 1].y, (int)av[w + 1].z, (int)av[w + 1].w}, bop[w + 1], acc1, 0, 0, 0);
-          }
-          const v4i acc = acc0 + acc1;
-          const bool gin = s * GPS + lg < G;
-          const float sc = gin ? half_bits_to_float(cur.s) : 0.f;
-          const float bi = gin ? half_bits_to_float(cur.b) : 0.f;
-          const float v = static_cast<float>(acc[3]) * 16777216.f + static_cast<float>(acc[2]) * 65536.f +
-                          static_cast<float>(acc[1]) * 256.f + static_cast<float>(acc[0]);
-          yacc += sc * (v * xf.y) + bi * xf.x;
-          if (++s == S) {
+          // dwords (lg >> 1) and 2 + (lg >> 1) of the 8 halves hold the
+          // lane's group in the pair's first and second span
+          const bool hi = lg >= 2;
+          span(2 * p, cur.w[0], cur.w[1], hi ? cur.s.y : cur.s.x, hi ? cur.b.y : cur.b.x);
+          if (2 * p + 1 < S) span(2 * p + 1, cur.w[2], cur.w[3], hi ? cur.s.w : cur.s.z, hi ? cur.b.w : cur.b.z);
+          if (++p == P2) {
             // tile done: add the 4 lane groups and park its rows
             float t = yacc + xor_lane(yacc, 4, lane);
             t += xor_lane(t, 5, lane);
             if (lg == 0) ybuf[(j - j0) * 16 + c] = t;
             yacc = 0.f;
-            s = 0;
+            p = 0;
             if (++j - j0 == kMultiYbuf) flush(j);
           }
         }
-        load(base + sl + P, ring[sl]);
       }
     }
     flush(j);
@@ -460,15 +478,15 @@ static void multi_prep_launch(const void* plan, void* ws, int tasks, hipStream_t
                      static_cast<const char*>(plan), static_cast<char*>(ws));
 }
 
-template <int P>
+template <int NW, int P>
 static void multi_stream_launch(const void* plan, const void* ws, int grid, size_t lds, hipStream_t st) {
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(multi_stream_kernel<P>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(multi_stream_kernel<NW, P>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kMultiLdsMax));
     attr_set = true;
   }
-  hipLaunchKernelGGL(multi_stream_kernel<P>, dim3(grid), dim3(kMultiThreads), lds, st,
+  hipLaunchKernelGGL((multi_stream_kernel<NW, P>), dim3(grid), dim3(64 * NW), lds, st,
                      static_cast<const char*>(plan), static_cast<const char*>(ws));
 }
 
@@ -512,7 +530,7 @@ extern "C" int tb_ternary_gemv_multi(const void* plan_host, const void* plan_dev
     }
     TB_LAUNCH_CHECK(who);
     const size_t lds = static_cast<size_t>(multi_lds_total(hd.max_nch));
-    multi_stream_launch<kMultiRing>(plan_device, workspace, hd.grid, lds, st);
+    multi_stream_launch<kMultiWaves, kMultiRing>(plan_device, workspace, hd.grid, lds, st);
     TB_LAUNCH_CHECK(who);
   }
   return TB_OK;
