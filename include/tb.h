@@ -171,16 +171,20 @@ size_t tb_ternary_gemm_workspace_size(int64_t M, int64_t K);
 
 /* Packed linear for prefill (any M >= 1), same definition as the GEMV:
  *   y[m][n] = sum_k W~[n][k] (R x[m])[k]   (fp32 out, M x N)
- * Codes are expanded to exact bf16 tiles in LDS and multiplied on bf16 MFMA
- * against a bf16 hi + lo split of the rotated activation; the per-group scale
- * and bias are applied in fp32.  Same argument rules as tb_ternary_gemv;
- * equivalent to tb_ternary_gemm_prepare then tb_ternary_gemm_run. */
+ * Runs on the block-scaled fp6 x fp4 MFMA: the 2-bit codes are fp4 operands
+ * as stored, the rotated activation enters as four signed base-16 fp6 digits
+ * per input with one power-of-two exponent per run of 32 inputs (16-bit
+ * fixed point relative to the run's largest magnitude); products accumulate
+ * in fp32 and the per-group scale and bias are applied in fp32.  Same
+ * argument rules as tb_ternary_gemv; equivalent to tb_ternary_gemm_prepare
+ * then tb_ternary_gemm_run. */
 int tb_ternary_gemm(const void* x, int x_dtype, int64_t M, int64_t K,
                     const int8_t* signs, int block,
                     const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
                     int64_t N, float* y, void* workspace, size_t ws_bytes, void* stream);
 
-/* Rotate the M x K activation into the workspace (bf16 hi/lo + group sums). */
+/* Rotate the M x K activation into the workspace (fp6 digit records, scaled
+ * fp16 hi/lo group sums; format private to the library). */
 int tb_ternary_gemm_prepare(const void* x, int x_dtype, int64_t M, int64_t K,
                             const int8_t* signs, int block, void* workspace, size_t ws_bytes,
                             void* stream);
