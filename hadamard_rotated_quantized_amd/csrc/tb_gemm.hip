@@ -32,6 +32,8 @@
 //    exact-sum fp16 hi + lo pair.  Workgroups are mapped so that each XCD
 //    walks contiguous output tiles in M-major order: the XCD's workgroups
 //    share one activation row tile in that XCD's L2 while the codes stream.
+#include <type_traits>
+
 #include "tb_device.h"
 
 namespace tb {
@@ -53,14 +55,16 @@ constexpr int kScaleOff = 4 * kRunBytes;      // 384
 constexpr int kRecBytes = kScaleOff + 16;     // 400
 constexpr int kRecUnits = kRecBytes / 16;     // 25
 
-constexpr int kMxBM = 128, kMxBN = 256;       // workgroup tile
-constexpr int kMxThreads = 512;               // 8 waves: 4 along M x 2 along N
-constexpr int kStageA = kMxBM * kRecBytes;    // 51200 B of activation records
-constexpr int kStageC = kMxBN * 32;           // 8192 B of code words (8 per row)
-constexpr int kStageBytes = kStageA + kStageC;
-constexpr int kMxLds = 2 * kStageBytes;       // double-buffered: 118784 B
-constexpr int kAUnits = kMxBM * kRecUnits;    // 3200 16-byte units per stage
-constexpr int kAUnitLoads = (kAUnits + kMxThreads - 1) / kMxThreads;  // 7
+constexpr int kMxBM = 64, kMxBN = 512;        // workgroup tile
+constexpr int kMxThreads = 512;               // 8 waves: 2 along M x 4 along N, 32 x 128 each
+constexpr int kStageA = kMxBM * kRecBytes;    // 25600 B of activation records
+constexpr int kStageC = kMxBN * 32;           // 16384 B of code words (8 per row)
+constexpr int kStageS = kMxBN * 4;            // 2048 B: per column the dword holding its scale
+constexpr int kStageBytes = kStageA + kStageC + kStageS;  // 44032 B per stage, three stages
+constexpr int kADma = kStageA / 1024;         // 25 direct-to-LDS loads of 1 KB (64 lanes x 16 B)
+constexpr int kCDma = kADma + kStageC / 1024; // codes: loads 25 .. 40
+constexpr int kSDma = kCDma + kStageS / 256;  // scales: loads 41 .. 48 (64 lanes x 4 B)
+constexpr int kDmaSlots = 7;                  // per wave and fill (56 slots, 7 of them padding)
 constexpr int kXcds = 8;
 constexpr uint32_t kFp4Codes = 0x33333333u;
 constexpr int kScaleB = 128;                  // E8M0 of 2^1
@@ -237,24 +241,79 @@ __global__ __launch_bounds__(kThreads) void gemm_prep_kernel(const void* __restr
 
 __device__ __forceinline__ v8h_g as_v8h(v4u_g u) { return __builtin_bit_cast(v8h_g, u); }
 
-// Digits 2 JP and 2 JP + 1 of one run (48 B of the record at rp) against the
-// four column blocks' fp4 codes; digit j takes byte j of the scale dword.
-template <int JP>
-__device__ __forceinline__ void mx_digit_pair(const uint8_t* rp, const v8i_g* bop, int sc, bool first,
-                                              v16f_g* acc) {
-  const v4u_g* ap = reinterpret_cast<const v4u_g*>(rp + 48 * JP);
-  const v4u_g u0 = ap[0], u1 = ap[1], u2 = ap[2];
-  const v8i_g alo = v8i_g{static_cast<int>(u0.x), static_cast<int>(u0.y), static_cast<int>(u0.z),
-                          static_cast<int>(u0.w), static_cast<int>(u1.x), static_cast<int>(u1.y), 0, 0};
-  const v8i_g ahi = v8i_g{static_cast<int>(u1.z), static_cast<int>(u1.w), static_cast<int>(u2.x),
-                          static_cast<int>(u2.y), static_cast<int>(u2.z), static_cast<int>(u2.w), 0, 0};
+// The three LDS stages of the matmul ring.
+__shared__ __attribute__((aligned(16))) uint8_t mx_stage0[kStageBytes];
+__shared__ __attribute__((aligned(16))) uint8_t mx_stage1[kStageBytes];
+__shared__ __attribute__((aligned(16))) uint8_t mx_stage2[kStageBytes];
+__shared__ __attribute__((aligned(16))) uint8_t mx_sink[1024];  // target of the padding loads
+
+template <int ST>
+__device__ __forceinline__ uint8_t* mx_stage() {
+  if constexpr (ST == 0) return mx_stage0;
+  else if constexpr (ST == 1) return mx_stage1;
+  else return mx_stage2;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint8_t*)(p)));
+}
+
+// Raw buffer resource (stride 0, range checked against `bytes`) as the four
+// scalar words the buffer instructions take.
+typedef int v4i_rs __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4i_rs rsrc_words(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return v4i_rs{static_cast<int>(static_cast<uint32_t>(a)), static_cast<int>(static_cast<uint32_t>(a >> 32)), bytes,
+                kRsrcW3};
+}
+
+// Direct-to-LDS buffer loads: lane l's 16 (or 4) bytes at voff land at LDS
+// address lds + 16 l (4 l).  Written as assembly so that the stage ring's
+// waits are the kernel's own s_waitcnt vmcnt(n): the ring keeps one fill in
+// flight across the barrier, which the compiler's conservative LDS tracking
+// would otherwise drain.  M0 holds the LDS base; nothing else in these
+// kernels uses M0.
+__device__ __forceinline__ void dma16(v4i_rs r, uint32_t lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff),
+               "s"(r)
+               : "memory");
+}
+__device__ __forceinline__ void dma4(v4i_rs r, uint32_t lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds), "v"(voff),
+               "s"(r)
+               : "memory");
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone
+__host__ __device__ constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// Operands of one k-step for one wave, read from a stage: the run's 6 units
+// (4 digits x 24 B), its scale dword, the two code words of each column
+// block, and (second k-step only) the scale dwords of the lane's columns.
+struct MxOps {
+  v4u_g a[6];
+  v2u_g c[4];
+  int sc;
+  uint32_t sd[4];
+};
+
+// Digit J of a run as an fp6 operand: dwords 6 J .. 6 J + 5 of the run.
+template <int J>
+__device__ __forceinline__ v8i_g digit_operand(const v4u_g* u) {
+  int d[6];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const v16f_g c_in = first ? v16f_g{} : acc[nb];
-    acc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(alo, bop[nb], c_in, 2, 4, 2 * JP, sc, 0, kScaleB);
-    acc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ahi, bop[nb], acc[nb], 2, 4, 2 * JP + 1, sc, 0,
-                                                              kScaleB);
-  }
+  for (int i = 0; i < 6; ++i) d[i] = static_cast<int>(u[(6 * J + i) / 4][(6 * J + i) % 4]);
+  return v8i_g{d[0], d[1], d[2], d[3], d[4], d[5], 0, 0};
+}
+
+// Digit J against the four column blocks; the A scale is byte J of sc.
+template <int J>
+__device__ __forceinline__ void mx_digit(const v4u_g* u, const v8i_g* bop, int sc, bool zero, v16f_g* acc) {
+  const v8i_g a = digit_operand<J>(u);
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+    acc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop[nb], zero ? v16f_g{} : acc[nb], 2, 4, J, sc,
+                                                              0, kScaleB);
 }
 
 __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
@@ -262,8 +321,6 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
     const float* __restrict__ p2, const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, float* __restrict__ y, int M, int N, int G, int Gp, int MT, int NT,
     int per_xcd) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t mx_lds[];
-
   // XCD-aware tile order: workgroup w runs on XCD w % 8; XCD x owns the
   // contiguous M-major tile range [x * per_xcd, (x + 1) * per_xcd).
   const int wg = blockIdx.x;
@@ -274,107 +331,197 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
   const int n0 = (tile % NT) * kMxBN;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave & 3, wn = wave >> 2;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int wm = wave & 1, wn = wave >> 1;
   const int r32 = lane & 31, h = lane >> 5;
   const int W = G * 8;  // code words per weight row
 
   // Rows past M or N read as zeros through the buffer range checks (sizes
-  // computed in 32-bit scalar arithmetic: one tile spans at most 128 / 256 rows).
+  // computed in 32-bit scalar arithmetic: one tile spans kMxBM / kMxBN rows).
   const int mrows = min(M - m0, kMxBM), nrows = min(N - n0, kMxBN);
-  const auto ra = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(rec + static_cast<int64_t>(m0) * G * kRecBytes), 0, mrows * G * kRecBytes, kRsrcW3);
-  const auto rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(codes + static_cast<int64_t>(n0) * W), 0,
-                                                    nrows * W * 4, kRsrcW3);
-  const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(scales + static_cast<int64_t>(n0) * G), 0,
-                                                    nrows * G * 2, kRsrcW3);
+  const v4i_rs ra = rsrc_words(rec + static_cast<int64_t>(m0) * G * kRecBytes, mrows * G * kRecBytes);
+  const v4i_rs rc = rsrc_words(codes + static_cast<int64_t>(n0) * W, nrows * W * 4);
+  // scales: the aligned dword holding s[n][g]; the resource starts at the
+  // dword holding s[n0][0] and ends with the dword holding s[N-1][G-1]
+  const uint64_t sp = reinterpret_cast<uint64_t>(scales) + static_cast<uint64_t>(n0) * G * 2;
+  const uint64_t sbase = sp & ~uint64_t(3);
+  const int shalf0 = static_cast<int>((sp - sbase) >> 1);  // 0 or 1
+  const v4i_rs rs = rsrc_words(reinterpret_cast<const void*>(sbase), ((shalf0 + (N - n0) * G) * 2 + 3) & ~3);
 
-  // staging: 4 threads per activation row of the tile, thread t taking the
-  // 16-byte units (t % 4) + 4 i of row t / 4; code unit tid is (row tid / 2,
-  // half tid % 2).  Offsets differ per unit by constants.
-  const int arow_t = tid >> 2, au0 = tid & 3;
-  const int aoff = arow_t * G * kRecBytes + au0 * 16;
-  const int apos = arow_t * kRecBytes + au0 * 16;
-  const bool a_last = au0 + 4 * (kAUnitLoads - 1) < kRecUnits;  // unit 24 exists for au0 == 0 only
-  const int crow = tid >> 1, chalf = tid & 1;
-  const int coff = crow * W * 4 + chalf * 16;
-  const int cpos = 2 * crow + (chalf ^ ((crow >> 2) & 1));  // swizzled LDS unit
-  const int soff = (wn * 128 + r32) * G * 2;                 // + 64 G per column block
-
-  v4u_g sa[kAUnitLoads], scw;
-  uint32_t sraw[4];
-  // g == G loads zeros (every offset out of range): the loop body has no branch
-  auto gload = [&](int g) {
-    const bool in = g < G;
+  // Stage fill: 49 direct-to-LDS loads; wave w issues loads w + 8 i, i < 7.
+  // Load q < 25 brings activation units 64 q + lane (unit p is record row
+  // p / 25, unit p % 25); loads 25 .. 40 bring code units, LDS unit
+  // pos = 64 (q - 25) + lane holding row pos / 2, half (pos & 1) ^ bit 2 of
+  // the row; loads 41 .. 48 bring the scale dword of column 64 (q - 41) + lane;
+  // loads 49 .. 55 are padding (out of range: zeros into mx_sink).
+  int voff[kDmaSlots];
+  int slot_kind[kDmaSlots];  // 0 activation, 1 codes, 2 scales, 3 padding (uniform)
 #pragma unroll
-    for (int i = 0; i < kAUnitLoads; ++i) {
-      const bool ok = in && (i < kAUnitLoads - 1 || a_last);
-      sa[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? aoff + g * kRecBytes + 64 * i : kOobOff, 0, 0);
+  for (int i = 0; i < kDmaSlots; ++i) {
+    const int q = wave + 8 * i;
+    if (q < kADma) {
+      const int p = 64 * q + lane;
+      voff[i] = (p / kRecUnits) * G * kRecBytes + (p % kRecUnits) * 16;
+      slot_kind[i] = 0;
+    } else if (q < kCDma) {
+      const int pos = 64 * (q - kADma) + lane, n = pos >> 1;
+      voff[i] = n * W * 4 + (((pos & 1) ^ ((n >> 2) & 1)) * 16);
+      slot_kind[i] = 1;
+    } else if (q < kSDma) {
+      voff[i] = shalf0 + (64 * (q - kCDma) + lane) * G;  // half index of s[n][0] from the resource base
+      slot_kind[i] = 2;
+    } else {
+      voff[i] = kOobOff;
+      slot_kind[i] = 3;
     }
-    scw = __builtin_amdgcn_raw_buffer_load_b128(rc, in ? coff + g * 32 : kOobOff, 0, 0);
+  }
+  // lane's own columns: which half of the staged dword is s[n][g] (flips with g)
+  int spar[4];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-      sraw[nb] = __builtin_amdgcn_raw_buffer_load_b16(rs, in ? soff + nb * 64 * G + 2 * g : kOobOff, 0, 0);
-  };
-  auto lstore = [&](int st) {
-    uint8_t* S = mx_lds + st * kStageBytes;
+  for (int nb = 0; nb < 4; ++nb) spar[nb] = (shalf0 + (wn * 128 + 32 * nb + r32) * G) & 1;
+
+  // Every wave issues exactly kDmaSlots loads per fill (padding included), so
+  // one s_waitcnt vmcnt(kDmaSlots) leaves exactly the newest fill in flight.
+  // A fill past the last group loads zeros (offsets out of range).
+  auto fill = [&](auto stage_tag, int g) {
+    constexpr int ST = decltype(stage_tag)::value;
+    const uint32_t dst = lds_addr(mx_stage<ST>());
+    const bool live = g < G;
 #pragma unroll
-    for (int i = 0; i < kAUnitLoads; ++i)
-      if (i < kAUnitLoads - 1 || a_last) *reinterpret_cast<v4u_g*>(S + apos + 64 * i) = sa[i];
-    *reinterpret_cast<v4u_g*>(S + kStageA + cpos * 16) = scw;
+    for (int i = 0; i < kDmaSlots; ++i) {
+      const int q = wave + 8 * i;
+      if (slot_kind[i] == 0) {
+        dma16(ra, dst + q * 1024, live ? voff[i] + g * kRecBytes : kOobOff);
+      } else if (slot_kind[i] == 1) {
+        dma16(rc, dst + q * 1024, live ? voff[i] + g * 32 : kOobOff);
+      } else if (slot_kind[i] == 2) {
+        dma4(rs, dst + kStageA + kStageC + (q - kCDma) * 256, live ? ((voff[i] + g) >> 1) * 4 : kOobOff);
+      } else {
+        dma4(rs, lds_addr(mx_sink), kOobOff);
+      }
+    }
   };
 
-  // LDS read positions of this lane: record row, and the code unit of
-  // column block 0 (bit 2 of the column is that of r32 in every block)
+  // LDS read positions of this lane: record row, and the code unit of column
+  // block 0 (bit 2 of the column is that of r32 in every block)
   const int arow = (wm * 32 + r32) * kRecBytes;
   const int cread = kStageA + (2 * (wn * 128 + r32) + (h ^ ((r32 >> 2) & 1))) * 16;  // + 1024 per block
 
   v16f_g yv[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) yv[nb] = v16f_g{};
-  float s_cur[4];
 
-  gload(0);
-  lstore(0);
+  // Reads of k-step s of the group held by stage ST, in three parts so that
+  // they can be spread between the MFMAs of the k-step before.
+  auto read_a = [&](auto stage_tag, int s, MxOps& o, int part) {
+    constexpr int ST = decltype(stage_tag)::value;
+    const uint8_t* S = mx_stage<ST>();
+    const int run = 2 * h + s;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) s_cur[nb] = half_bits_to_float(static_cast<uint16_t>(sraw[nb]));
-  __syncthreads();
-
-  for (int g = 0; g < G; ++g) {
-    const uint8_t* S = mx_lds + (g & 1) * kStageBytes;
-    gload(g + 1);
-
-    v16f_g acc[4];
+    for (int u = 3 * part; u < 3 * part + 3; ++u)
+      o.a[u] = *reinterpret_cast<const v4u_g*>(S + arow + run * kRunBytes + 16 * u);
+    if (part == 1) o.sc = *reinterpret_cast<const int*>(S + arow + kScaleOff + 4 * run);
+  };
+  auto read_c = [&](auto stage_tag, int s, MxOps& o, bool with_scales) {
+    constexpr int ST = decltype(stage_tag)::value;
+    const uint8_t* S = mx_stage<ST>();
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int run = 2 * h + s;
-      const int sc = *reinterpret_cast<const int*>(S + arow + kScaleOff + 4 * run);
-      v8i_g bop[4];
+    for (int nb = 0; nb < 4; ++nb) o.c[nb] = *reinterpret_cast<const v2u_g*>(S + cread + 1024 * nb + 8 * s);
+    if (with_scales) {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const v2u_g cw = *reinterpret_cast<const v2u_g*>(S + cread + 1024 * nb + 8 * s);
-        const uint32_t wa = cw.x, wb = cw.y;
-        bop[nb] = v8i_g{static_cast<int>(wa & kFp4Codes), static_cast<int>((wa >> 2) & kFp4Codes),
-                        static_cast<int>(wb & kFp4Codes), static_cast<int>((wb >> 2) & kFp4Codes), 0, 0, 0, 0};
-      }
-      mx_digit_pair<0>(S + arow + run * kRunBytes, bop, sc, s == 0, acc);
-      mx_digit_pair<1>(S + arow + run * kRunBytes, bop, sc, false, acc);
-      // keep the next k-step's LDS reads after these MFMAs (register budget)
-      __builtin_amdgcn_sched_barrier(0);
+      for (int nb = 0; nb < 4; ++nb)
+        o.sd[nb] = *reinterpret_cast<const uint32_t*>(S + kStageA + kStageC + 4 * (wn * 128 + 32 * nb + r32));
     }
+  };
+  auto decode = [&](const MxOps& o, v8i_g* bop) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const uint32_t wa = o.c[nb].x, wb = o.c[nb].y;
+      bop[nb] = v8i_g{static_cast<int>(wa & kFp4Codes), static_cast<int>((wa >> 2) & kFp4Codes),
+                      static_cast<int>(wb & kFp4Codes), static_cast<int>((wb >> 2) & kFp4Codes), 0, 0, 0, 0};
+    }
+  };
+
+  // Software pipeline at k-step granularity, one barrier per group placed
+  // between the group's two k-steps.  Per group g:
+  //   MFMAs of k-step 0, with the reads of k-step 1 and the refill of the
+  //   stage of group g + 2 issued between them; wait for this wave's part of
+  //   the fill of group g + 1 and for its reads; barrier;
+  //   MFMAs of k-step 1, with the reads of k-step 0 of group g + 1 between
+  //   them; fold group g.
+  // The matrix core works through each digit's MFMAs while the reads and
+  // loads placed after them are issued.  The refill overwrites the stage of
+  // group g - 1, whose reads all completed before the previous barrier.
+  fill(std::integral_constant<int, 0>{}, 0);
+  fill(std::integral_constant<int, 1>{}, 1);
+  __builtin_amdgcn_s_waitcnt(wait_vm(kDmaSlots));
+  __builtin_amdgcn_s_barrier();
+  MxOps r0;
+  read_a(std::integral_constant<int, 0>{}, 0, r0, 0);
+  read_a(std::integral_constant<int, 0>{}, 0, r0, 1);
+  read_c(std::integral_constant<int, 0>{}, 0, r0, false);
+
+  auto step = [&](auto stage_tag, int g) {
+    constexpr int ST = decltype(stage_tag)::value;
+    constexpr auto next = std::integral_constant<int, (ST + 1) % 3>{};
+    MxOps r1;
+    v8i_g bop[4];
+    v16f_g acc[4];
+    decode(r0, bop);
+    mx_digit<0>(r0.a, bop, r0.sc, true, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    read_a(stage_tag, 1, r1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_digit<1>(r0.a, bop, r0.sc, false, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    read_a(stage_tag, 1, r1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_digit<2>(r0.a, bop, r0.sc, false, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    read_c(stage_tag, 1, r1, true);
+    fill(std::integral_constant<int, (ST + 2) % 3>{}, g + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_digit<3>(r0.a, bop, r0.sc, false, acc);
+    // keep this k-step's MFMAs ahead of the barrier: the matrix core works
+    // through them while the waves synchronize
+    asm volatile("" ::"v"(acc[0]), "v"(acc[1]), "v"(acc[2]), "v"(acc[3]));
+    // every read of this wave done (the refill of the next-but-one group
+    // targets what other waves read before this barrier) and this wave's
+    // part of the next group's stage landed
+    __builtin_amdgcn_s_waitcnt(wait_vm(kDmaSlots) & ~(0xF << 8));
+    __builtin_amdgcn_s_barrier();
+    decode(r1, bop);
+    mx_digit<0>(r1.a, bop, r1.sc, false, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    read_a(next, 0, r0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_digit<1>(r1.a, bop, r1.sc, false, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    read_a(next, 0, r0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_digit<2>(r1.a, bop, r1.sc, false, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    read_c(next, 0, r0, false);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_digit<3>(r1.a, bop, r1.sc, false, acc);
     // per-group scale fold in fp32
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < 4; ++nb) {
+      const uint32_t sd = r1.sd[nb];
+      const float sv = half_bits_to_float(static_cast<uint16_t>((spar[nb] ^ (g & 1)) ? sd >> 16 : sd));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) yv[nb][r] = fmaf(s_cur[nb], acc[nb][r], yv[nb][r]);
-
-    // the stage refill waits for this group's loads: keep it after the MFMAs
-    asm volatile("" ::"v"(yv[0]), "v"(yv[1]), "v"(yv[2]), "v"(yv[3]) : "memory");
-    lstore((g + 1) & 1);
-    __syncthreads();
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) s_cur[nb] = half_bits_to_float(static_cast<uint16_t>(sraw[nb]));
+      for (int r = 0; r < 16; ++r) yv[nb][r] = fmaf(sv, acc[nb][r], yv[nb][r]);
+    }
+  };
+  for (int g = 0; g < G; g += 3) {
+    step(std::integral_constant<int, 0>{}, g);
+    if (g + 1 >= G) break;
+    step(std::integral_constant<int, 1>{}, g + 1);
+    if (g + 2 >= G) break;
+    step(std::integral_constant<int, 2>{}, g + 2);
   }
+
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));  // the ring's trailing (zero) fills
 
   // bias term: y += 2^t[m] * sum_g Xs[m][g] * b[n][g] on fp16 MFMA
   const auto rxh = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(xh + static_cast<int64_t>(m0) * Gp), 0,
@@ -532,14 +679,8 @@ static void gemm_run_launch(const void* workspace, int64_t M, int64_t K, const u
   const float* p2 = reinterpret_cast<const float*>(ws + lay.p2_off);
   const int64_t MT = (M + kMxBM - 1) / kMxBM, NT = (N + kMxBN - 1) / kMxBN;
   const int64_t per_xcd = (MT * NT + kXcds - 1) / kXcds;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_mx_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(gemm_mx_kernel, dim3(static_cast<unsigned>(per_xcd * kXcds)), dim3(kMxThreads),
-                     static_cast<size_t>(kMxLds), st, rec, xh, xl, p2, codes, scales, biases, y,
+  hipLaunchKernelGGL(gemm_mx_kernel, dim3(static_cast<unsigned>(per_xcd * kXcds)), dim3(kMxThreads), 0,
+                     st, rec, xh, xl, p2, codes, scales, biases, y,
                      static_cast<int>(M), static_cast<int>(N), static_cast<int>(lay.G), static_cast<int>(lay.Gp),
                      static_cast<int>(MT), static_cast<int>(NT), static_cast<int>(per_xcd));
 }
