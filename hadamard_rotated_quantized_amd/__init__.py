@@ -42,6 +42,7 @@ _SIGNATURES = {
     "tb_pack_device": (_I, [_P, _P, _I64, _I64, _P, _P, _P, _P, _P]),
     "tb_fwht_signed": (_I, [_P, _I, _P, _P, _I64, _I64, _I, _I, _P]),
     "tb_ternary_gemv_workspace_size": (_SZ, [_I64, _I64]),
+    "tb_ternary_gemv_workspace_size_n": (_SZ, [_I64, _I64, _I64]),
     "tb_ternary_gemv": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
     "tb_ternary_gemv_prepare": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _SZ, _P]),
     "tb_ternary_gemv_run": (_I, [_P, _SZ, _I64, _I64, _P, _P, _P, _I64, _P, _P]),
@@ -194,6 +195,10 @@ def tb_ternary_gemv_workspace_size(B: int, K: int) -> int:
     return int(lib().tb_ternary_gemv_workspace_size(B, K))
 
 
+def tb_ternary_gemv_workspace_size_n(B: int, K: int, N: int) -> int:
+    return int(lib().tb_ternary_gemv_workspace_size_n(B, K, N))
+
+
 def tb_ternary_gemm_workspace_size(M: int, K: int) -> int:
     return int(lib().tb_ternary_gemm_workspace_size(M, K))
 
@@ -219,7 +224,7 @@ def tb_ternary_gemv(x, signs, block: int, codes, scales, biases, out=None, works
     if out is None:
         out = torch.empty((B, N), dtype=torch.float32, device=x.device)
     _dev(out, "out", torch.float32)
-    need = tb_ternary_gemv_workspace_size(B, K)
+    need = tb_ternary_gemv_workspace_size_n(B, K, N)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     _check(lib().tb_ternary_gemv(x.data_ptr(), _xdtype(x), B, K, _ptr(signs), block, codes.data_ptr(),

@@ -173,6 +173,12 @@ struct Mfma {
 // workgroup per band of output rows can hold the band's packed weights and
 // the transformed input in LDS.
 bool gemv_band_eligible(int64_t B, int64_t K, int64_t N, int block);
+// decode batches of 2 to 8 rows: prepare + K-split streaming (+ slice sum)
+bool gemv_batch_eligible(int64_t B, int64_t K, int64_t N, int block);
+size_t gemv_batch_workspace(int64_t B, int64_t K, int64_t N);
+void gemv_batch_launch(const void* x, int x_dtype, int64_t B, int64_t K, const int8_t* signs, int block,
+                       const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, int64_t N, float* y,
+                       void* workspace, hipStream_t st);
 void gemv_band_launch(const void* x, int x_dtype, int64_t K, const int8_t* signs, int block, const uint32_t* codes,
                       const uint16_t* scales, const uint16_t* biases, int64_t N, float* y, hipStream_t st);
 

@@ -663,6 +663,13 @@ extern "C" size_t tb_ternary_gemv_workspace_size(int64_t B, int64_t K) {
   return static_cast<size_t>(gemv_ws_layout(B, K).total);
 }
 
+extern "C" size_t tb_ternary_gemv_workspace_size_n(int64_t B, int64_t K, int64_t N) {
+  const size_t base = tb_ternary_gemv_workspace_size(B, K);
+  if (base == 0 || N <= 0 || B < 2 || B > TB_GEMV_MAX_BATCH || N > (int64_t(1) << 30) || K > (int64_t(1) << 24))
+    return base;
+  return std::max(base, gemv_batch_workspace(B, K, N));
+}
+
 extern "C" int tb_ternary_gemv_prepare(const void* x, int x_dtype, int64_t B, int64_t K,
                                        const int8_t* signs, int block, void* workspace,
                                        size_t ws_bytes, void* stream) {
@@ -702,8 +709,14 @@ extern "C" int tb_ternary_gemv(const void* x, int x_dtype, int64_t B, int64_t K,
   TB_TRY(check_dtype(x_dtype, x, who));
   TB_TRY(prep_align_checks(x, signs, who));
   TB_TRY(run_checks(N, K, codes, scales, biases, y, who));
-  TB_TRY(gemv_ws_check(workspace, ws_bytes, B, K, who));
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (gemv_batch_eligible(B, K, N, block) && workspace && aligned(workspace, 16) &&
+      ws_bytes >= gemv_batch_workspace(B, K, N)) {
+    gemv_batch_launch(x, x_dtype, B, K, signs, block, codes, scales, biases, N, y, workspace, st);
+    TB_LAUNCH_CHECK(who);
+    return TB_OK;
+  }
+  TB_TRY(gemv_ws_check(workspace, ws_bytes, B, K, who));
   if (gemv_band_eligible(B, K, N, block)) {
     gemv_band_launch(x, x_dtype, K, signs, block, codes, scales, biases, N, y, st);
     TB_LAUNCH_CHECK(who);

@@ -1,0 +1,359 @@
+// Decode batches of 2 to 8 rows against one packed weight matrix
+// [lpnh.cn/news/2438023, "text model loading" (fwht(x, block, signs), then
+// the quantized matmul); kwkr.cn/news/564617, "ternary weights + folded
+// Hadamard rotation" and "packing-format engineering"]:
+//   y[b][n] = sum_g s[n][g] (sum_{k in g} c[n][k] xr[b][k]) + bias[n][g] X[b][g]
+//
+// The weights must stream from HBM once for all batch rows, and a decode
+// layer is often narrow (N = 5120) but deep (K = 17408): 320 row tiles of 16
+// cannot keep 256 CUs streaming, and the exact activation operand of 8 rows
+// (4 base-256 limbs each, 557 KB at K = 17408) does not fit one CU's LDS.
+// So the contraction is split along K as well:
+//
+// 1. batch_prep_kernel: one wave per (batch row, 1024-input chunk), the
+//    in-register MFMA transform (tb_xform.h) writing the row's exact
+//    four-limb operand image and group terms to the workspace.
+// 2. batch_stream_kernel: one workgroup per (128-row block, K slice of whole
+//    chunks).  The workgroup first issues its code loads, then copies the
+//    slice's operand rows of every batch row into LDS; each of its 8 waves
+//    streams one 16-row tile through a ring of per-group register slots.  A
+//    group is 2 v_mfma_i32_16x16x64_i8 per 4 batch rows: A row 4 b' + l holds
+//    limb l of batch row b', the 4 k-blocks hold 4 of the group's 8 code
+//    words, so the accumulator of lane (lane group j, row c) is the 4 limbs of
+//    batch row j (+4 for the second set) at output row c.  The limbs are
+//    recombined in fp32 and the fp16 scale and bias applied per group.
+// 3. batch_reduce_kernel (more than one K slice): the slices' partial rows
+//    summed in slice order, so results do not depend on scheduling.
+#include <algorithm>
+
+#include "tb_xform.h"
+
+namespace tb {
+
+constexpr int kBatWaves = 8;
+constexpr int kBatThreads = 64 * kBatWaves;
+constexpr int kBatTile = 16;                    // output rows per wave
+constexpr int kBatRows = kBatTile * kBatWaves;  // output rows per work unit
+constexpr int kBatArow = 144;                   // LDS bytes per (batch row, group, limb) operand row
+constexpr int kBatGroupBytes = kXfLimbs * 128;  // workspace bytes per (batch row, group)
+constexpr int kBatRing = 2;                     // octets of groups in flight per wave (10 loads each)
+constexpr int kBatStageUnits = 19;              // 16-byte LDS units per thread: 19 x 512 x 16 B >= kBatLdsMax
+constexpr int64_t kBatLdsMax = 150 * 1024;
+
+// LDS stride between batch rows: 16 mod 32 dwords, so that the two batch rows
+// read by lanes 0-3 and 4-7 of an A-operand read land on disjoint banks.
+__host__ __device__ inline int batch_bstride(int gps) { return gps * kXfLimbs * kBatArow + ((gps & 1) ? 0 : 64); }
+__host__ __device__ inline int64_t batch_lds_bytes(int B, int gps) {
+  return static_cast<int64_t>(B) * batch_bstride(gps) + static_cast<int64_t>(B) * gps * 8;
+}
+
+struct BatchPlan {
+  int nch, cps, S, rbn, grid;
+  int64_t lds;
+  bool ok;
+};
+
+static int batch_device_cus() {
+  int dev = 0, cus = 256;
+  (void)hipGetDevice(&dev);
+  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  return cus;
+}
+
+// Work units: ceil(N / 128) row blocks x S slices of cps chunks, about one
+// per CU; a slice's operand rows must fit the LDS.
+static BatchPlan batch_plan(int64_t B, int64_t K, int64_t N, int cus) {
+  BatchPlan p{};
+  p.nch = static_cast<int>((K + 1023) / 1024);
+  p.rbn = static_cast<int>((N + kBatRows - 1) / kBatRows);
+  int cps_max = 0;
+  while (batch_lds_bytes(static_cast<int>(B), 8 * (cps_max + 1)) <= kBatLdsMax) ++cps_max;
+  const int target = std::max(1, (cus + p.rbn / 2) / p.rbn);
+  p.cps = std::min(std::max(1, (p.nch + target - 1) / target), std::max(cps_max, 1));
+  p.S = (p.nch + p.cps - 1) / p.cps;
+  p.lds = batch_lds_bytes(static_cast<int>(B), 8 * p.cps);
+  p.ok = cps_max >= 1 && static_cast<int64_t>(p.rbn) * p.S < (int64_t(1) << 31);
+  p.grid = p.rbn * p.S;
+  return p;
+}
+
+struct BatchWs {
+  int64_t img, xf, part, total;
+};
+static inline int64_t bat_align256(int64_t v) { return (v + 255) & ~int64_t(255); }
+static BatchWs batch_ws_layout(int64_t B, int64_t K, int64_t N, const BatchPlan& p) {
+  const int64_t Gc = static_cast<int64_t>(p.nch) * 8;
+  BatchWs w;
+  w.img = 0;
+  w.xf = bat_align256(B * Gc * kBatGroupBytes);
+  w.part = w.xf + bat_align256(B * Gc * 8);
+  w.total = w.part + (p.S > 1 ? bat_align256(static_cast<int64_t>(p.S) * B * N * 4) : 0);
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// 1. transform: one wave per (batch row, chunk)
+// ---------------------------------------------------------------------------
+template <int L, int DT>
+__global__ __launch_bounds__(256) void batch_prep_kernel(const void* __restrict__ x, const int8_t* __restrict__ signs,
+                                                         int B, int K, int nch, char* __restrict__ img,
+                                                         float2* __restrict__ xf) {
+  const int lane = threadIdx.x & 63;
+  const int task = static_cast<int>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (task >= B * nch) return;  // whole wave; the kernel has no barrier
+  const int b = task / nch, c = task - b * nch;
+  constexpr int ESZ = DT == TB_F32 ? 4 : 2;
+  const auto rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(static_cast<const char*>(x) + static_cast<int64_t>(b) * K * ESZ), 0, K * ESZ, kRsrcWord3);
+  const auto rsg = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(signs), 0, L > 0 ? K : 0, kRsrcWord3);
+  XformIn<DT> in;
+  xform_issue<L, DT>(rx, rsg, static_cast<int64_t>(c) * 1024, c * 1024, lane, in);
+  const v4u* cst = reinterpret_cast<const v4u*>(&kXformConst.w[xf_mode<L>()][0][lane][0]);
+  const v4u* cst2 = reinterpret_cast<const v4u*>(&kXformConst.w[xf_mode<L>()][1][lane][0]);
+  const v4u cf[2] = {cst[0], cst[1]};
+  const v4u cs[2] = {cst2[0], cst2[1]};
+  xform_chunk<L, DT>(in, 8 * c, lane, cf, cs, img + static_cast<int64_t>(b) * nch * 8 * kBatGroupBytes,
+                     xf + static_cast<int64_t>(b) * nch * 8, 128);
+}
+
+// ---------------------------------------------------------------------------
+// 2. stream: one workgroup per (row block, K slice)
+// ---------------------------------------------------------------------------
+// One ring slot: 8 consecutive groups (an octet) of the lane's row
+struct BatchSlot {
+  uint2 w[8];  // code words 2 j and 2 j + 1 of (row c, group) for lane group j
+  uint4 s, b;  // the 8 fp16 scales / biases of (row c, octet), one 16-byte load each
+};
+
+template <int NS>
+__global__ __launch_bounds__(kBatThreads, 1) void batch_stream_kernel(
+    const char* __restrict__ img, const float2* __restrict__ xf, const uint32_t* __restrict__ codes,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases, float* __restrict__ out, int B, int N,
+    int K, int nch, int cps, int S) {
+  extern __shared__ uint4 bat_lds_dyn[];
+  char* const lds = reinterpret_cast<char*>(bat_lds_dyn);
+  const int unit = blockIdx.x;
+  const int rb = unit / S, sl = unit - rb * S;
+  const int G = K / kGroup, RBy = K / 4;  // groups, code bytes per weight row
+  const int gps = 8 * cps;
+  const int g0 = sl * gps;
+  const int ng = min(G, g0 + gps) - g0;  // groups of this slice (>= 1)
+  const int bstride = batch_bstride(gps);
+  float2* const lxf = reinterpret_cast<float2*>(lds + static_cast<int64_t>(B) * bstride);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lg = lane >> 4, c = lane & 15;
+
+  // 1. this wave's tile: rows trow0 .. trow0 + 15; its first code loads
+  // (wave-uniform values, kept in scalar registers for the buffer resources)
+  const int trow0 = __builtin_amdgcn_readfirstlane(rb * kBatRows + kBatTile * wave);
+  const int base_row = __builtin_amdgcn_readfirstlane(min(trow0, N));
+  const int nrows = __builtin_amdgcn_readfirstlane(max(0, min(kBatTile, N - trow0)));
+  const auto rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(codes + static_cast<int64_t>(base_row) * (K / 16)),
+                                                    0, nrows * RBy, kRsrcWord3);
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(scales + static_cast<int64_t>(base_row) * G), 0,
+                                                    nrows * G * 2, kRsrcWord3);
+  const auto rbi = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(biases + static_cast<int64_t>(base_row) * G), 0,
+                                                     nrows * G * 2, kRsrcWord3);
+  // a slot past the slice loads nothing useful: its offsets lie beyond every
+  // buffer and read as zero, so every slot is refilled in one static order.
+  // The scale and bias rows are read 8 groups at a time (K % 256 == 0 keeps
+  // those 16-byte loads dword aligned).
+  auto load = [&](int o, BatchSlot& st) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int gl = 8 * o + j;
+      const int oc = gl < ng ? c * RBy + (g0 + gl) * 32 + lg * 8 : kOob;
+      const v2u w = __builtin_amdgcn_raw_buffer_load_b64(rc, oc, 0, 0);
+      st.w[j] = make_uint2(w.x, w.y);
+    }
+    const int os = 8 * o < ng ? (c * G + g0 + 8 * o) * 2 : kOob;
+    const v4u us = __builtin_amdgcn_raw_buffer_load_b128(rs, os, 0, 0);
+    const v4u ub = __builtin_amdgcn_raw_buffer_load_b128(rbi, os, 0, 0);
+    st.s = make_uint4(us.x, us.y, us.z, us.w);
+    st.b = make_uint4(ub.x, ub.y, ub.z, ub.w);
+  };
+
+  // 2. the slice's operand rows of every batch row (16-byte units, all of a
+  //    thread's loads in flight at once; indices past the end repeat the last
+  //    unit: same value, same place), then the ring's first code loads, then
+  //    the stores, which wait for the older operand loads only
+  const int units = B * ng * kXfLimbs * 8;
+  const int rows_b = ng * kXfLimbs;
+  const int njs = (units + kBatThreads - 1) / kBatThreads;  // uniform: rounds of the copy
+  uint4 sv[kBatStageUnits];
+  int sdst[kBatStageUnits];
+#pragma unroll
+  for (int j = 0; j < kBatStageUnits; ++j) {
+    sv[j] = make_uint4(0u, 0u, 0u, 0u);
+    sdst[j] = 0;
+    if (j < njs) {
+      const int i = min(j * kBatThreads + tid, units - 1);
+      const int r = i >> 3, q = i & 7;
+      const int b = r / rows_b, rem = r - b * rows_b;
+      sv[j] = *reinterpret_cast<const uint4*>(img + (static_cast<int64_t>(b) * nch * 8 + g0) * kBatGroupBytes +
+                                              rem * 128 + q * 16);
+      sdst[j] = b * bstride + rem * kBatArow + q * 16;
+    }
+  }
+  float2 sxf = make_float2(0.f, 0.f);
+  if (tid < B * ng) {
+    const int b = tid / ng, gl = tid - b * ng;
+    sxf = xf[static_cast<int64_t>(b) * nch * 8 + g0 + gl];
+  }
+  BatchSlot ring[kBatRing];
+#pragma unroll
+  for (int k = 0; k < kBatRing; ++k) load(k, ring[k]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < kBatStageUnits; ++j)
+    if (j < njs) *reinterpret_cast<uint4*>(lds + sdst[j]) = sv[j];
+  if (tid < B * ng) {
+    const int b = tid / ng, gl = tid - b * ng;
+    lxf[b * gps + gl] = sxf;
+  }
+  __syncthreads();
+  if (nrows == 0) return;  // no barrier follows
+
+  // 3. stream the tile's groups
+  float yacc[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) yacc[s] = 0.f;
+  // lane (j, c) holds A row c = 4 b' + l (batch row b', limb l) of k-block j
+  const int ab = c >> 2, al = c & 3;
+  auto group = [&](int gl, uint2 w, uint32_t sdw, uint32_t bdw, int hi) {
+    const v4i bq0 = decode_word(w.x), bq1 = decode_word(w.y);
+    const float sc = half_bits_to_float(static_cast<uint16_t>(sdw >> (16 * hi)));
+    const float bi = half_bits_to_float(static_cast<uint16_t>(bdw >> (16 * hi)));
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      v4u a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
+      if (4 * s + ab < B) {
+        const char* ap = lds + (4 * s + ab) * bstride + (gl * kXfLimbs + al) * kBatArow + 2 * lg * 16;
+        a0 = *reinterpret_cast<const v4u*>(ap);
+        a1 = *reinterpret_cast<const v4u*>(ap + 16);
+      }
+      v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, a0), bq0, v4i{0, 0, 0, 0}, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, a1), bq1, acc, 0, 0, 0);
+      // lane (j, c): limbs 0..3 of batch row 4 s + j at output row c
+      const int bo = 4 * s + lg;
+      if (bo < B) {
+        const float2 t = lxf[bo * gps + gl];
+        const float v = static_cast<float>(acc[3]) * 16777216.f + static_cast<float>(acc[2]) * 65536.f +
+                        static_cast<float>(acc[1]) * 256.f + static_cast<float>(acc[0]);
+        yacc[s] += sc * (v * t.y) + bi * t.x;
+      }
+    }
+  };
+  const int nocts = (ng + 7) >> 3;
+  for (int base = 0; base < nocts; base += kBatRing) {
+#pragma unroll
+    for (int k = 0; k < kBatRing; ++k) {
+      const BatchSlot cur = ring[k];
+      load(base + k + kBatRing, ring[k]);  // refill the slot before computing on its data
+      const int o = base + k;
+      if (o < nocts) {
+        const uint32_t sd[4] = {cur.s.x, cur.s.y, cur.s.z, cur.s.w};
+        const uint32_t bd[4] = {cur.b.x, cur.b.y, cur.b.z, cur.b.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (8 * o + j < ng) group(8 * o + j, cur.w[j], sd[j >> 1], bd[j >> 1], j & 1);
+      }
+    }
+  }
+
+  // 4. the tile's rows: partial sums of this slice, or y itself
+  if (c < nrows) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int bo = 4 * s + lg;
+      if (bo < B) {
+        const int64_t n = trow0 + c;
+        float* dst = S > 1 ? out + (static_cast<int64_t>(sl) * B + bo) * N + n : out + static_cast<int64_t>(bo) * N + n;
+        *dst = yacc[s];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. the slices' partial rows, summed in slice order
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void batch_reduce_kernel(const float* __restrict__ part, float* __restrict__ y,
+                                                           int64_t BN, int S) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= BN) return;
+  // eight slices' loads in flight, added in slice order
+  float s = 0.f;
+  for (int k0 = 0; k0 < S; k0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = k0 + j < S ? part[static_cast<int64_t>(k0 + j) * BN + i] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += v[j];
+  }
+  y[i] = s;
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+bool gemv_batch_eligible(int64_t B, int64_t K, int64_t N, int block) {
+  if (B < 2 || B > TB_GEMV_MAX_BATCH || !(block == 0 || block == 512 || block == 1024) || K % 256) return false;
+  if (N <= 0 || N > (int64_t(1) << 30) || K > (int64_t(1) << 24)) return false;
+  return batch_plan(B, K, N, batch_device_cus()).ok;
+}
+
+size_t gemv_batch_workspace(int64_t B, int64_t K, int64_t N) {
+  const BatchPlan p = batch_plan(B, K, N, batch_device_cus());
+  return static_cast<size_t>(batch_ws_layout(B, K, N, p).total);
+}
+
+template <int L>
+static void batch_prep_launch(const void* x, int dt, const int8_t* signs, int B, int K, int nch, char* img,
+                              float2* xf, hipStream_t st) {
+  const dim3 grid((B * nch + 3) / 4);
+  if (dt == TB_F32)
+    hipLaunchKernelGGL((batch_prep_kernel<L, TB_F32>), grid, dim3(256), 0, st, x, signs, B, K, nch, img, xf);
+  else
+    hipLaunchKernelGGL((batch_prep_kernel<L, TB_BF16>), grid, dim3(256), 0, st, x, signs, B, K, nch, img, xf);
+}
+
+template <int NS>
+static void batch_stream_launch(const BatchPlan& p, const char* img, const float2* xf, const uint32_t* codes,
+                                const uint16_t* scales, const uint16_t* biases, float* out, int B, int N, int K,
+                                hipStream_t st) {
+  auto kern = batch_stream_kernel<NS>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              static_cast<int>(kBatLdsMax));
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(p.grid), dim3(kBatThreads), static_cast<size_t>(p.lds), st, img, xf, codes, scales,
+                     biases, out, B, N, K, p.nch, p.cps, p.S);
+}
+
+void gemv_batch_launch(const void* x, int x_dtype, int64_t B, int64_t K, const int8_t* signs, int block,
+                       const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, int64_t N, float* y,
+                       void* workspace, hipStream_t st) {
+  const BatchPlan p = batch_plan(B, K, N, batch_device_cus());
+  const BatchWs lay = batch_ws_layout(B, K, N, p);
+  char* ws = static_cast<char*>(workspace);
+  char* img = ws + lay.img;
+  float2* xf = reinterpret_cast<float2*>(ws + lay.xf);
+  const int b = static_cast<int>(B), k = static_cast<int>(K), n = static_cast<int>(N);
+  if (block == 0) batch_prep_launch<0>(x, x_dtype, signs, b, k, p.nch, img, xf, st);
+  else if (block == 512) batch_prep_launch<512>(x, x_dtype, signs, b, k, p.nch, img, xf, st);
+  else batch_prep_launch<1024>(x, x_dtype, signs, b, k, p.nch, img, xf, st);
+  float* out = p.S > 1 ? reinterpret_cast<float*>(ws + lay.part) : y;
+  if (b <= 4) batch_stream_launch<1>(p, img, xf, codes, scales, biases, out, b, n, k, st);
+  else batch_stream_launch<2>(p, img, xf, codes, scales, biases, out, b, n, k, st);
+  if (p.S > 1) {
+    const int64_t BN = B * N;
+    hipLaunchKernelGGL(batch_reduce_kernel, dim3(static_cast<unsigned>((BN + 255) / 256)), dim3(256), 0, st, out, y,
+                       BN, p.S);
+  }
+}
+
+}  // namespace tb
