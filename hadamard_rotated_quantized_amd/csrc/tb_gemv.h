@@ -173,7 +173,9 @@ struct Mfma {
 // workgroup per band of output rows can hold the band's packed weights and
 // the transformed input in LDS.
 bool gemv_band_eligible(int64_t B, int64_t K, int64_t N, int block);
-// decode batches of 2 to 8 rows: prepare + K-split streaming (+ slice sum)
+// decode batches of 2 to 8 rows: in-workgroup transform + K-split streaming
+// (+ slice sum); the workspace holds the slices' partial rows (0 bytes when
+// one slice covers K)
 bool gemv_batch_eligible(int64_t B, int64_t K, int64_t N, int block);
 size_t gemv_batch_workspace(int64_t B, int64_t K, int64_t N);
 void gemv_batch_launch(const void* x, int x_dtype, int64_t B, int64_t K, const int8_t* signs, int block,

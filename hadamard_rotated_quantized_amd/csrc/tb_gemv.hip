@@ -710,8 +710,9 @@ extern "C" int tb_ternary_gemv(const void* x, int x_dtype, int64_t B, int64_t K,
   TB_TRY(prep_align_checks(x, signs, who));
   TB_TRY(run_checks(N, K, codes, scales, biases, y, who));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (gemv_batch_eligible(B, K, N, block) && workspace && aligned(workspace, 16) &&
-      ws_bytes >= gemv_batch_workspace(B, K, N)) {
+  const size_t batch_ws = gemv_batch_eligible(B, K, N, block) ? gemv_batch_workspace(B, K, N) : 0;
+  if (gemv_batch_eligible(B, K, N, block) &&
+      (batch_ws == 0 || (workspace && aligned(workspace, 16) && ws_bytes >= batch_ws))) {
     gemv_batch_launch(x, x_dtype, B, K, signs, block, codes, scales, biases, N, y, workspace, st);
     TB_LAUNCH_CHECK(who);
     return TB_OK;

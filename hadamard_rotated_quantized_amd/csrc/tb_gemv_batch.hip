@@ -10,19 +10,21 @@
 // (4 base-256 limbs each, 557 KB at K = 17408) does not fit one CU's LDS.
 // So the contraction is split along K as well:
 //
-// 1. batch_prep_kernel: one wave per (batch row, 1024-input chunk), the
-//    in-register MFMA transform (tb_xform.h) writing the row's exact
-//    four-limb operand image and group terms to the workspace.
-// 2. batch_stream_kernel: one workgroup per (128-row block, K slice of whole
-//    chunks).  The workgroup first issues its code loads, then copies the
-//    slice's operand rows of every batch row into LDS; each of its 8 waves
-//    streams one 16-row tile through a ring of per-group register slots.  A
-//    group is 2 v_mfma_i32_16x16x64_i8 per 4 batch rows: A row 4 b' + l holds
-//    limb l of batch row b', the 4 k-blocks hold 4 of the group's 8 code
-//    words, so the accumulator of lane (lane group j, row c) is the 4 limbs of
-//    batch row j (+4 for the second set) at output row c.  The limbs are
-//    recombined in fp32 and the fp16 scale and bias applied per group.
-// 3. batch_reduce_kernel (more than one K slice): the slices' partial rows
+// 1. batch_stream_kernel: one workgroup per (128-row block, K slice of whole
+//    chunks).  Its waves first issue the loads of the slice's activation
+//    chunks (every batch row), then the first code loads of their tiles, and
+//    transform the chunks on the matrix cores (tb_xform.h) straight into the
+//    LDS operand image of the slice -- the exact four-limb split and the
+//    group terms -- while the codes are in flight.  Each of the 8 waves then
+//    streams one 16-row tile through a ring of register slots of 8 groups
+//    (8-byte code loads, one 16-byte load for the 8 scales and one for the 8
+//    biases of a row).  A group is 2 v_mfma_i32_16x16x64_i8 per 4 batch rows:
+//    A row 4 b' + l holds limb l of batch row b', the 4 k-blocks hold 4 of
+//    the group's 8 code words, so the accumulator of lane (lane group j, row
+//    c) is the 4 limbs of batch row j (+4 for the second set) at output row
+//    c.  The limbs are recombined in fp32 and the fp16 scale and bias applied
+//    per group.
+// 2. batch_reduce_kernel (more than one K slice): the slices' partial rows
 //    summed in slice order, so results do not depend on scheduling.
 #include <algorithm>
 
@@ -35,9 +37,8 @@ constexpr int kBatThreads = 64 * kBatWaves;
 constexpr int kBatTile = 16;                    // output rows per wave
 constexpr int kBatRows = kBatTile * kBatWaves;  // output rows per work unit
 constexpr int kBatArow = 144;                   // LDS bytes per (batch row, group, limb) operand row
-constexpr int kBatGroupBytes = kXfLimbs * 128;  // workspace bytes per (batch row, group)
 constexpr int kBatRing = 2;                     // octets of groups in flight per wave (10 loads each)
-constexpr int kBatStageUnits = 19;              // 16-byte LDS units per thread: 19 x 512 x 16 B >= kBatLdsMax
+constexpr int kBatMaxTasks = 4;                 // chunk transforms per wave
 constexpr int64_t kBatLdsMax = 150 * 1024;
 
 // LDS stride between batch rows: 16 mod 32 dwords, so that the two batch rows
@@ -67,7 +68,10 @@ static BatchPlan batch_plan(int64_t B, int64_t K, int64_t N, int cus) {
   p.nch = static_cast<int>((K + 1023) / 1024);
   p.rbn = static_cast<int>((N + kBatRows - 1) / kBatRows);
   int cps_max = 0;
-  while (batch_lds_bytes(static_cast<int>(B), 8 * (cps_max + 1)) <= kBatLdsMax) ++cps_max;
+  // a slice's chunks are transformed by the 8 waves, kBatMaxTasks each at most
+  while (batch_lds_bytes(static_cast<int>(B), 8 * (cps_max + 1)) <= kBatLdsMax &&
+         B * (cps_max + 1) <= kBatWaves * kBatMaxTasks)
+    ++cps_max;
   const int target = std::max(1, (cus + p.rbn / 2) / p.rbn);
   p.cps = std::min(std::max(1, (p.nch + target - 1) / target), std::max(cps_max, 1));
   p.S = (p.nch + p.cps - 1) / p.cps;
@@ -77,47 +81,14 @@ static BatchPlan batch_plan(int64_t B, int64_t K, int64_t N, int cus) {
   return p;
 }
 
-struct BatchWs {
-  int64_t img, xf, part, total;
-};
 static inline int64_t bat_align256(int64_t v) { return (v + 255) & ~int64_t(255); }
-static BatchWs batch_ws_layout(int64_t B, int64_t K, int64_t N, const BatchPlan& p) {
-  const int64_t Gc = static_cast<int64_t>(p.nch) * 8;
-  BatchWs w;
-  w.img = 0;
-  w.xf = bat_align256(B * Gc * kBatGroupBytes);
-  w.part = w.xf + bat_align256(B * Gc * 8);
-  w.total = w.part + (p.S > 1 ? bat_align256(static_cast<int64_t>(p.S) * B * N * 4) : 0);
-  return w;
+// workspace: the slices' partial rows (none for a single slice)
+static int64_t batch_ws_bytes(int64_t B, int64_t N, const BatchPlan& p) {
+  return p.S > 1 ? bat_align256(static_cast<int64_t>(p.S) * B * N * 4) : 0;
 }
 
 // ---------------------------------------------------------------------------
-// 1. transform: one wave per (batch row, chunk)
-// ---------------------------------------------------------------------------
-template <int L, int DT>
-__global__ __launch_bounds__(256) void batch_prep_kernel(const void* __restrict__ x, const int8_t* __restrict__ signs,
-                                                         int B, int K, int nch, char* __restrict__ img,
-                                                         float2* __restrict__ xf) {
-  const int lane = threadIdx.x & 63;
-  const int task = static_cast<int>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (task >= B * nch) return;  // whole wave; the kernel has no barrier
-  const int b = task / nch, c = task - b * nch;
-  constexpr int ESZ = DT == TB_F32 ? 4 : 2;
-  const auto rx = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(static_cast<const char*>(x) + static_cast<int64_t>(b) * K * ESZ), 0, K * ESZ, kRsrcWord3);
-  const auto rsg = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(signs), 0, L > 0 ? K : 0, kRsrcWord3);
-  XformIn<DT> in;
-  xform_issue<L, DT>(rx, rsg, static_cast<int64_t>(c) * 1024, c * 1024, lane, in);
-  const v4u* cst = reinterpret_cast<const v4u*>(&kXformConst.w[xf_mode<L>()][0][lane][0]);
-  const v4u* cst2 = reinterpret_cast<const v4u*>(&kXformConst.w[xf_mode<L>()][1][lane][0]);
-  const v4u cf[2] = {cst[0], cst[1]};
-  const v4u cs[2] = {cst2[0], cst2[1]};
-  xform_chunk<L, DT>(in, 8 * c, lane, cf, cs, img + static_cast<int64_t>(b) * nch * 8 * kBatGroupBytes,
-                     xf + static_cast<int64_t>(b) * nch * 8, 128);
-}
-
-// ---------------------------------------------------------------------------
-// 2. stream: one workgroup per (row block, K slice)
+// 1. transform + stream: one workgroup per (row block, K slice)
 // ---------------------------------------------------------------------------
 // One ring slot: 8 consecutive groups (an octet) of the lane's row
 struct BatchSlot {
@@ -125,11 +96,11 @@ struct BatchSlot {
   uint4 s, b;  // the 8 fp16 scales / biases of (row c, octet), one 16-byte load each
 };
 
-template <int NS>
+template <int NS, int L, int DT>
 __global__ __launch_bounds__(kBatThreads, 1) void batch_stream_kernel(
-    const char* __restrict__ img, const float2* __restrict__ xf, const uint32_t* __restrict__ codes,
+    const void* __restrict__ x, const int8_t* __restrict__ signs, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases, float* __restrict__ out, int B, int N,
-    int K, int nch, int cps, int S) {
+    int K, int cps, int S) {
   extern __shared__ uint4 bat_lds_dyn[];
   char* const lds = reinterpret_cast<char*>(bat_lds_dyn);
   const int unit = blockIdx.x;
@@ -174,43 +145,40 @@ __global__ __launch_bounds__(kBatThreads, 1) void batch_stream_kernel(
     st.b = make_uint4(ub.x, ub.y, ub.z, ub.w);
   };
 
-  // 2. the slice's operand rows of every batch row (16-byte units, all of a
-  //    thread's loads in flight at once; indices past the end repeat the last
-  //    unit: same value, same place), then the ring's first code loads, then
-  //    the stores, which wait for the older operand loads only
-  const int units = B * ng * kXfLimbs * 8;
-  const int rows_b = ng * kXfLimbs;
-  const int njs = (units + kBatThreads - 1) / kBatThreads;  // uniform: rounds of the copy
-  uint4 sv[kBatStageUnits];
-  int sdst[kBatStageUnits];
+  // 2. the slice's activation chunks: loads first (they complete before the
+  //    code loads issued after them), then the transforms into LDS
+  const int ncs = (ng + 7) >> 3;  // chunks of this slice
+  const int ntask = B * ncs;      // <= 8 waves x kBatMaxTasks (plan)
+  constexpr int ESZ = DT == TB_F32 ? 4 : 2;
+  const auto rsg = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(signs), 0, L > 0 ? K : 0, kRsrcWord3);
+  // the transform's lane constants are loaded first: the waits for them
+  // then do not cover the code loads issued later
+  const v4u* cst = reinterpret_cast<const v4u*>(&kXformConst.w[xf_mode<L>()][0][lane][0]);
+  const v4u* cst2 = reinterpret_cast<const v4u*>(&kXformConst.w[xf_mode<L>()][1][lane][0]);
+  const v4u cf[2] = {cst[0], cst[1]};
+  const v4u cs[2] = {cst2[0], cst2[1]};
+  XformIn<DT> xin[kBatMaxTasks];
 #pragma unroll
-  for (int j = 0; j < kBatStageUnits; ++j) {
-    sv[j] = make_uint4(0u, 0u, 0u, 0u);
-    sdst[j] = 0;
-    if (j < njs) {
-      const int i = min(j * kBatThreads + tid, units - 1);
-      const int r = i >> 3, q = i & 7;
-      const int b = r / rows_b, rem = r - b * rows_b;
-      sv[j] = *reinterpret_cast<const uint4*>(img + (static_cast<int64_t>(b) * nch * 8 + g0) * kBatGroupBytes +
-                                              rem * 128 + q * 16);
-      sdst[j] = b * bstride + rem * kBatArow + q * 16;
+  for (int r = 0; r < kBatMaxTasks; ++r) {
+    const int t = wave + kBatWaves * r;
+    if (t < ntask) {
+      const int b = t / ncs, cg = (g0 >> 3) + (t - b * ncs);
+      const auto rx = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(static_cast<const char*>(x) + static_cast<int64_t>(b) * K * ESZ), 0, K * ESZ, kRsrcWord3);
+      xform_issue<L, DT>(rx, rsg, static_cast<int64_t>(cg) * 1024, cg * 1024, lane, xin[r]);
     }
-  }
-  float2 sxf = make_float2(0.f, 0.f);
-  if (tid < B * ng) {
-    const int b = tid / ng, gl = tid - b * ng;
-    sxf = xf[static_cast<int64_t>(b) * nch * 8 + g0 + gl];
   }
   BatchSlot ring[kBatRing];
 #pragma unroll
   for (int k = 0; k < kBatRing; ++k) load(k, ring[k]);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int j = 0; j < kBatStageUnits; ++j)
-    if (j < njs) *reinterpret_cast<uint4*>(lds + sdst[j]) = sv[j];
-  if (tid < B * ng) {
-    const int b = tid / ng, gl = tid - b * ng;
-    lxf[b * gps + gl] = sxf;
+  for (int r = 0; r < kBatMaxTasks; ++r) {
+    const int t = wave + kBatWaves * r;
+    if (t < ntask) {
+      const int b = t / ncs, j = t - b * ncs;
+      xform_chunk<L, DT>(xin[r], 8 * j, lane, cf, cs, lds + b * bstride, lxf + b * gps, kBatArow);
+    }
   }
   __syncthreads();
   if (nrows == 0) return;  // no barrier follows
@@ -306,49 +274,49 @@ bool gemv_batch_eligible(int64_t B, int64_t K, int64_t N, int block) {
 
 size_t gemv_batch_workspace(int64_t B, int64_t K, int64_t N) {
   const BatchPlan p = batch_plan(B, K, N, batch_device_cus());
-  return static_cast<size_t>(batch_ws_layout(B, K, N, p).total);
+  return static_cast<size_t>(batch_ws_bytes(B, N, p));
 }
 
-template <int L>
-static void batch_prep_launch(const void* x, int dt, const int8_t* signs, int B, int K, int nch, char* img,
-                              float2* xf, hipStream_t st) {
-  const dim3 grid((B * nch + 3) / 4);
-  if (dt == TB_F32)
-    hipLaunchKernelGGL((batch_prep_kernel<L, TB_F32>), grid, dim3(256), 0, st, x, signs, B, K, nch, img, xf);
-  else
-    hipLaunchKernelGGL((batch_prep_kernel<L, TB_BF16>), grid, dim3(256), 0, st, x, signs, B, K, nch, img, xf);
-}
-
-template <int NS>
-static void batch_stream_launch(const BatchPlan& p, const char* img, const float2* xf, const uint32_t* codes,
+template <int NS, int L, int DT>
+static void batch_stream_launch(const BatchPlan& p, const void* x, const int8_t* signs, const uint32_t* codes,
                                 const uint16_t* scales, const uint16_t* biases, float* out, int B, int N, int K,
                                 hipStream_t st) {
-  auto kern = batch_stream_kernel<NS>;
+  auto kern = batch_stream_kernel<NS, L, DT>;
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                               static_cast<int>(kBatLdsMax));
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(p.grid), dim3(kBatThreads), static_cast<size_t>(p.lds), st, img, xf, codes, scales,
-                     biases, out, B, N, K, p.nch, p.cps, p.S);
+  hipLaunchKernelGGL(kern, dim3(p.grid), dim3(kBatThreads), static_cast<size_t>(p.lds), st, x, signs, codes, scales,
+                     biases, out, B, N, K, p.cps, p.S);
+}
+
+template <int NS, int L>
+static void batch_launch_dt(int dt, const BatchPlan& p, const void* x, const int8_t* signs, const uint32_t* codes,
+                            const uint16_t* scales, const uint16_t* biases, float* out, int B, int N, int K,
+                            hipStream_t st) {
+  if (dt == TB_F32) batch_stream_launch<NS, L, TB_F32>(p, x, signs, codes, scales, biases, out, B, N, K, st);
+  else batch_stream_launch<NS, L, TB_BF16>(p, x, signs, codes, scales, biases, out, B, N, K, st);
+}
+
+template <int NS>
+static void batch_launch_l(int block, int dt, const BatchPlan& p, const void* x, const int8_t* signs,
+                           const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, float* out, int B,
+                           int N, int K, hipStream_t st) {
+  if (block == 0) batch_launch_dt<NS, 0>(dt, p, x, signs, codes, scales, biases, out, B, N, K, st);
+  else if (block == 512) batch_launch_dt<NS, 512>(dt, p, x, signs, codes, scales, biases, out, B, N, K, st);
+  else batch_launch_dt<NS, 1024>(dt, p, x, signs, codes, scales, biases, out, B, N, K, st);
 }
 
 void gemv_batch_launch(const void* x, int x_dtype, int64_t B, int64_t K, const int8_t* signs, int block,
                        const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, int64_t N, float* y,
                        void* workspace, hipStream_t st) {
   const BatchPlan p = batch_plan(B, K, N, batch_device_cus());
-  const BatchWs lay = batch_ws_layout(B, K, N, p);
-  char* ws = static_cast<char*>(workspace);
-  char* img = ws + lay.img;
-  float2* xf = reinterpret_cast<float2*>(ws + lay.xf);
   const int b = static_cast<int>(B), k = static_cast<int>(K), n = static_cast<int>(N);
-  if (block == 0) batch_prep_launch<0>(x, x_dtype, signs, b, k, p.nch, img, xf, st);
-  else if (block == 512) batch_prep_launch<512>(x, x_dtype, signs, b, k, p.nch, img, xf, st);
-  else batch_prep_launch<1024>(x, x_dtype, signs, b, k, p.nch, img, xf, st);
-  float* out = p.S > 1 ? reinterpret_cast<float*>(ws + lay.part) : y;
-  if (b <= 4) batch_stream_launch<1>(p, img, xf, codes, scales, biases, out, b, n, k, st);
-  else batch_stream_launch<2>(p, img, xf, codes, scales, biases, out, b, n, k, st);
+  float* out = p.S > 1 ? static_cast<float*>(workspace) : y;
+  if (b <= 4) batch_launch_l<1>(block, x_dtype, p, x, signs, codes, scales, biases, out, b, n, k, st);
+  else batch_launch_l<2>(block, x_dtype, p, x, signs, codes, scales, biases, out, b, n, k, st);
   if (p.S > 1) {
     const int64_t BN = B * N;
     hipLaunchKernelGGL(batch_reduce_kernel, dim3(static_cast<unsigned>((BN + 255) / 256)), dim3(256), 0, st, out, y,
