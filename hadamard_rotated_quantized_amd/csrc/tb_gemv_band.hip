@@ -48,8 +48,12 @@
 // * One barrier.  Once the transform waves have written the operand image
 //   and every wave's staging loads have landed, all 8 waves run the matmul
 //   from LDS: items of (16-row subtile, span of 4 groups), dealt round robin,
-//   with all of a wave's LDS reads issued before its MFMAs.  Partial sums
-//   meet in LDS and every row of y is written once.
+//   with all of a wave's LDS reads issued before its MFMAs.  The item count
+//   per wave is a template parameter, so the items carry no branches (only
+//   the last one can be missing; a wave without it skips its reads, since an
+//   LDS instruction costs the same whatever its active lanes) and their MFMA
+//   chains interleave.  Partial sums meet in LDS and every row of y is
+//   written once.
 //
 // Used for batch 1, blocks 0 / 512 / 1024, at most 3 chunk transforms per
 // wave, bands of at most 7 subtiles and an LDS footprint within the limit;
@@ -93,7 +97,7 @@ __host__ __device__ inline BandLds band_lds_layout(int64_t nch, int64_t tsub, in
 
 // rows: output rows per band (the last band may be short); tsub: 16-row
 // subtiles per band.
-template <int L, int DT>
+template <int L, int DT, int MI>
 __global__ __launch_bounds__(kBandThreads, 1) void gemv_band_kernel(
     const void* __restrict__ x, const int8_t* __restrict__ signs, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases, int N, int K, int rows,
@@ -212,83 +216,94 @@ __global__ __launch_bounds__(kBandThreads, 1) void gemv_band_kernel(
   const uint32_t lane_c = static_cast<uint32_t>(c * RB + lg * 32);
   auto stage_at = [](uint32_t off) { return off + (off >> 10) * (kBandSlot - 1024); };
 
+  // The wave's items are wave + 8 j, j < MI (MI = ceil(items / 8)); only the
+  // last can be past the end (it then aliases item 0 and is skipped), so the
+  // first MI - 1 items have no branches and their MFMA chains interleave.
+  int tt[MI], ss[MI];
+  bool iv[MI];
+#pragma unroll
+  for (int j = 0; j < MI; ++j) {
+    const int i = wave + kBandWaves * j;
+    iv[j] = i < items;
+    const int ic = iv[j] ? i : 0;
+    tt[j] = ic / S;
+    ss[j] = ic - tt[j] * S;
+  }
   // all LDS reads of the wave's items first: codes, scale, bias, the
   // group's (sum, f), and the A operand -- read only by the 16 lanes whose A
   // row is non-zero (the others keep zeros)
-  uint4 cw[kBandMaxItems][2];
-  uint4 av[kBandMaxItems][kWordsPerGroup];
-  float2 xfv[kBandMaxItems];
-  uint16_t sraw[kBandMaxItems], braw[kBandMaxItems];
-  int tt[kBandMaxItems], ss[kBandMaxItems];
-  {
-    int t = wave / S, s = wave - (wave / S) * S;  // item wave = t * S + s
+  uint4 cw[MI][2];
+  uint4 av[MI][kWordsPerGroup];
+  float2 xfv[MI];
+  uint16_t sraw[MI], braw[MI];
 #pragma unroll
-    for (int j = 0; j < kBandMaxItems; ++j) {
-      tt[j] = t;
-      ss[j] = s;
-      if (wave + kBandWaves * j < items) {
-        const uint32_t so = stage_at(lane_c + static_cast<uint32_t>(t * M * RB + s * 128));
-        cw[j][0] = *reinterpret_cast<const uint4*>(st_codes + so);
-        cw[j][1] = *reinterpret_cast<const uint4*>(st_codes + so + 16);
-        const int si = (t * M + c) * G + s * GPS + lg;
-        sraw[j] = st_sc[si];
-        braw[j] = st_bi[si];
-        xfv[j] = lds_xf[s * GPS + lg];
+  for (int j = 0; j < MI; ++j) {
+    cw[j][0] = cw[j][1] = make_uint4(0, 0, 0, 0);
+    sraw[j] = braw[j] = 0;
+    xfv[j] = make_float2(0.f, 0.f);
 #pragma unroll
-        for (int w = 0; w < kWordsPerGroup; ++w) av[j][w] = make_uint4(0, 0, 0, 0);
-        if (a_lane) {
-          const uint4* ap = reinterpret_cast<const uint4*>(lds_a + ((s * GPS + alg) * kXfLimbs + ar) * kBandArow);
+    for (int w = 0; w < kWordsPerGroup; ++w) av[j][w] = make_uint4(0, 0, 0, 0);
+    // LDS instructions cost the same whatever the active lanes: a wave
+    // without a last item skips its reads
+    if (j < MI - 1 || iv[j]) {
+      const int t = tt[j], s = ss[j];
+      const uint32_t so = stage_at(lane_c + static_cast<uint32_t>(t * M * RB + s * 128));
+      cw[j][0] = *reinterpret_cast<const uint4*>(st_codes + so);
+      cw[j][1] = *reinterpret_cast<const uint4*>(st_codes + so + 16);
+      const int si = (t * M + c) * G + s * GPS + lg;
+      sraw[j] = st_sc[si];
+      braw[j] = st_bi[si];
+      xfv[j] = lds_xf[s * GPS + lg];
+      if (a_lane) {
+        const uint4* ap = reinterpret_cast<const uint4*>(lds_a + ((s * GPS + alg) * kXfLimbs + ar) * kBandArow);
 #pragma unroll
-          for (int w = 0; w < kWordsPerGroup; ++w) av[j][w] = ap[w];
-        }
-      }
-      // next item of this wave: 8 items further
-      s += kBandWaves;
-      while (s >= S) {
-        s -= S;
-        ++t;
+        for (int w = 0; w < kWordsPerGroup; ++w) av[j][w] = ap[w];
       }
     }
   }
-  float part[kBandMaxItems];
+  float part[MI];
 #pragma unroll
-  for (int j = 0; j < kBandMaxItems; ++j) {
+  for (int j = 0; j < MI; ++j) {
     part[j] = 0.f;
-    if (wave + kBandWaves * j < items) {
-      v4i bop[kWordsPerGroup];
-      bop[0] = decode_word(cw[j][0].x);
-      bop[1] = decode_word(cw[j][0].y);
-      bop[2] = decode_word(cw[j][0].z);
-      bop[3] = decode_word(cw[j][0].w);
-      bop[4] = decode_word(cw[j][1].x);
-      bop[5] = decode_word(cw[j][1].y);
-      bop[6] = decode_word(cw[j][1].z);
-      bop[7] = decode_word(cw[j][1].w);
-      v4i acc0 = {}, acc1 = {};
+    // only the last item can be invalid; a wave without it skips its work
+    if (j < MI - 1 || iv[j]) {
+    v4i bop[kWordsPerGroup];
+    bop[0] = decode_word(cw[j][0].x);
+    bop[1] = decode_word(cw[j][0].y);
+    bop[2] = decode_word(cw[j][0].z);
+    bop[3] = decode_word(cw[j][0].w);
+    bop[4] = decode_word(cw[j][1].x);
+    bop[5] = decode_word(cw[j][1].y);
+    bop[6] = decode_word(cw[j][1].z);
+    bop[7] = decode_word(cw[j][1].w);
+    v4i acc0 = {}, acc1 = {};
 #pragma unroll
-      for (int w = 0; w < kWordsPerGroup; w += 2) {
-        const uint4 u0 = av[j][w], u1 = av[j][w + 1];
-        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w}, bop[w], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w}, bop[w + 1], acc1, 0, 0, 0);
-      }
-      const v4i acc = acc0 + acc1;
-      // lane (lg, c): limb sums of row t*16 + c, group s*4 + lg
-      const bool gin = ss[j] * GPS + lg < G;
-      const float sc = gin ? half_bits_to_float(sraw[j]) : 0.f;
-      const float bi = gin ? half_bits_to_float(braw[j]) : 0.f;
-      const float v = static_cast<float>(acc[3]) * 16777216.f + static_cast<float>(acc[2]) * 65536.f +
-                      static_cast<float>(acc[1]) * 256.f + static_cast<float>(acc[0]);
-      part[j] = sc * (v * xfv[j].y) + bi * xfv[j].x;
+    for (int w = 0; w < kWordsPerGroup; w += 2) {
+      const uint4 u0 = av[j][w], u1 = av[j][w + 1];
+      acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w}, bop[w], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w}, bop[w + 1], acc1, 0, 0, 0);
+    }
+    const v4i acc = acc0 + acc1;
+    // lane (lg, c): limb sums of row t*16 + c, group s*4 + lg
+    const bool gin = iv[j] && ss[j] * GPS + lg < G;
+    const float sc = gin ? half_bits_to_float(sraw[j]) : 0.f;
+    const float bi = gin ? half_bits_to_float(braw[j]) : 0.f;
+    const float v = static_cast<float>(acc[3]) * 16777216.f + static_cast<float>(acc[2]) * 65536.f +
+                    static_cast<float>(acc[1]) * 256.f + static_cast<float>(acc[0]);
+    part[j] = sc * (v * xfv[j].y) + bi * xfv[j].x;
     }
   }
   // per subtile: add this wave's items in registers, then over the 4 lane
   // groups, and park the 16 row sums in red[t][wave] (one plain store)
-  for (int t = tt[0]; t < tsub && t <= tt[kBandMaxItems - 1]; ++t) {
+  int tend = tt[0];  // subtile of the wave's last valid item
+#pragma unroll
+  for (int j = 1; j < MI; ++j) tend = iv[j] ? tt[j] : tend;
+  for (int t = tt[0]; t < tsub && t <= tend; ++t) {
     float v = 0.f;
     bool any = false;
 #pragma unroll
-    for (int j = 0; j < kBandMaxItems; ++j) {
-      const bool mine = tt[j] == t && wave + kBandWaves * j < items;
+    for (int j = 0; j < MI; ++j) {
+      const bool mine = tt[j] == t && iv[j];
       v += mine ? part[j] : 0.f;
       any |= mine;
     }
@@ -321,7 +336,7 @@ static int band_device_cus() {
 }
 
 struct BandPlan {
-  int rows, tsub, grid;
+  int rows, tsub, grid, mi;
   int64_t lds;
   bool ok;
 };
@@ -336,6 +351,7 @@ static BandPlan band_plan(int64_t K, int64_t N, int cus) {
   p.rows = static_cast<int>(rows);
   p.tsub = static_cast<int>(tsub);
   p.grid = static_cast<int>((N + rows - 1) / rows);
+  p.mi = static_cast<int>((tsub * S + kBandWaves - 1) / kBandWaves);  // matmul items per wave
   const int64_t cslots = (tsub * 16 * RB + 96 + 1023) / 1024 + 1;
   const int64_t sbslots = (tsub * 16 * G * 2 + 64 + 1023) / 1024;
   const int64_t nss = (rows * G * 2 + 1023) / 1024;
@@ -354,10 +370,10 @@ bool gemv_band_eligible(int64_t B, int64_t K, int64_t N, int block) {
   return band_plan(K, N, band_device_cus()).ok;
 }
 
-template <int L, int DT>
+template <int L, int DT, int MI>
 static void band_launch_t(const void* x, const int8_t* signs, const uint32_t* codes, const uint16_t* scales,
                           const uint16_t* biases, float* y, int N, int K, const BandPlan& p, hipStream_t st) {
-  auto kern = gemv_band_kernel<L, DT>;
+  auto kern = gemv_band_kernel<L, DT, MI>;
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -368,11 +384,22 @@ static void band_launch_t(const void* x, const int8_t* signs, const uint32_t* co
                      biases, N, K, p.rows, p.tsub, y);
 }
 
+template <int L, int DT>
+static void band_launch_mi(const void* x, const int8_t* signs, const uint32_t* codes, const uint16_t* scales,
+                           const uint16_t* biases, float* y, int N, int K, const BandPlan& p, hipStream_t st) {
+  switch (p.mi) {
+    case 1: band_launch_t<L, DT, 1>(x, signs, codes, scales, biases, y, N, K, p, st); break;
+    case 2: band_launch_t<L, DT, 2>(x, signs, codes, scales, biases, y, N, K, p, st); break;
+    case 3: band_launch_t<L, DT, 3>(x, signs, codes, scales, biases, y, N, K, p, st); break;
+    default: band_launch_t<L, DT, 4>(x, signs, codes, scales, biases, y, N, K, p, st); break;
+  }
+}
+
 template <int L>
 static void band_launch_l(int dt, const void* x, const int8_t* signs, const uint32_t* codes, const uint16_t* scales,
                           const uint16_t* biases, float* y, int N, int K, const BandPlan& p, hipStream_t st) {
-  if (dt == TB_F32) band_launch_t<L, TB_F32>(x, signs, codes, scales, biases, y, N, K, p, st);
-  else band_launch_t<L, TB_BF16>(x, signs, codes, scales, biases, y, N, K, p, st);
+  if (dt == TB_F32) band_launch_mi<L, TB_F32>(x, signs, codes, scales, biases, y, N, K, p, st);
+  else band_launch_mi<L, TB_BF16>(x, signs, codes, scales, biases, y, N, K, p, st);
 }
 
 void gemv_band_launch(const void* x, int x_dtype, int64_t K, const int8_t* signs, int block, const uint32_t* codes,

@@ -151,18 +151,19 @@ __device__ __forceinline__ void xform_issue(__amdgpu_buffer_rsrc_t rx, __amdgpu_
   }
 }
 
-// Transform one chunk (groups g0 .. g0 + 7 of the operand image) and write
-// its limbs and (group sum, f).  lds_a: operand rows [group][limb] of
-// arow_bytes bytes (128 of data; LDS images pad them); lds_xf: float2 per
-// group.  Both may be LDS or global memory.
+// The rotated chunk U = H (signs .* x) (unnormalized) in the accumulator
+// layout of the second product: lane l, register 4 Q + t holds element
+//   e = (l & 3) | t << 2 | ((l >> 2) & 7) << 4 | (l >> 5) << 7 | Q << 8,
+// so group (128 inputs) h + 2 Q of the chunk with h = l >> 5.  v128: element
+// 128 c in lanes 4 c (c < 8), for the group sums.
 template <int L, int DT>
-__device__ __forceinline__ void xform_chunk(const XformIn<DT>& in, int g0, int lane, const v4u cfirst[2],
-                                            const v4u csecond[2], char* lds_a, float2* lds_xf, int arow_bytes) {
+__device__ __forceinline__ v16f xform_rotate(const XformIn<DT>& in, int lane, const v4u cfirst[2],
+                                             const v4u csecond[2], float& v128) {
   // 1. signs onto the activations, as bf16 operand pairs
   uint32_t xop[2][4];        // exact bf16 (bf16 input) or the hi piece of an fp32 input
   uint32_t xmid[2][4] = {};  // fp32 input: the mid and lo pieces
   uint32_t xlo[2][4] = {};
-  float v128 = 0.f;         // element 128 c of lanes 4 c (c < 8): for the group sums
+  v128 = 0.f;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int s = q >> 1, u = q & 1;
@@ -215,6 +216,48 @@ __device__ __forceinline__ void xform_chunk(const XformIn<DT>& in, int g0, int l
     U = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ha, as_v8bf(mid[0], mid[1], mid[2], mid[3]), U, 0, 0, 0);
     U = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ha, as_v8bf(lo[0], lo[1], lo[2], lo[3]), U, 0, 0, 0);
   }
+  return U;
+}
+
+// Group sums of the normalized transform and the chunk's dequantization
+// factor f, as float2 (sum, f) per group of the chunk (groups g0 .. g0 + 7).
+template <int L>
+__device__ __forceinline__ void xform_group_sums(const v16f& U, float v128, int g0, int lane, float f,
+                                                 float2* lds_xf) {
+  if constexpr (L > 0) {
+    // sum_{k in group m} (H v)_k = 128 sum_c (-1)^popcount(m & c) v[128 c]; v[128 c]
+    // is element 0 of lane 4 c.  Butterflies over lane bits 2, 3 (and 4 for 1024-blocks).
+    float g = v128;
+#pragma unroll
+    for (int j = 2; j < (L == 512 ? 4 : 5); ++j) {
+      const float sgn = ((lane >> j) & 1) ? -1.f : 1.f;
+      g = fmaf(sgn, g, xor_lane(g, j, lane));
+    }
+    if (lane < 32 && (lane & 3) == 0)
+      lds_xf[g0 + (lane >> 2)] = make_float2(g * (128.f * inv_sqrt_block_or_one<L>()), f);
+  } else {
+    // no rotation: sum the 4 values of each group held by the lane, then over
+    // the 32 lanes of the lane half
+    const int h = lane >> 5;
+#pragma unroll
+    for (int Q = 0; Q < 4; ++Q) {
+      float sm = (U[4 * Q] + U[4 * Q + 1]) + (U[4 * Q + 2] + U[4 * Q + 3]);
+#pragma unroll
+      for (int j = 0; j < 5; ++j) sm += xor_lane(sm, j, lane);
+      if ((lane & 31) == 0) lds_xf[g0 + h + 2 * Q] = make_float2(sm, f);
+    }
+  }
+}
+
+// Transform one chunk (groups g0 .. g0 + 7 of the operand image) and write
+// its limbs and (group sum, f).  lds_a: operand rows [group][limb] of
+// arow_bytes bytes (128 of data; LDS images pad them); lds_xf: float2 per
+// group.  Both may be LDS or global memory.
+template <int L, int DT>
+__device__ __forceinline__ void xform_chunk(const XformIn<DT>& in, int g0, int lane, const v4u cfirst[2],
+                                            const v4u csecond[2], char* lds_a, float2* lds_xf, int arow_bytes) {
+  float v128;
+  const v16f U = xform_rotate<L, DT>(in, lane, cfirst, csecond, v128);
   // 4. one power-of-two scale for the chunk: |q| < 2^30
   float m = 0.f;
 #pragma unroll
@@ -247,28 +290,7 @@ __device__ __forceinline__ void xform_chunk(const XformIn<DT>& in, int g0, int l
     *reinterpret_cast<uint32_t*>(row + 3 * arow_bytes) = l3;
   }
   // 6. group sums of the normalized transform
-  if constexpr (L > 0) {
-    // sum_{k in group m} (H v)_k = 128 sum_c (-1)^popcount(m & c) v[128 c]; v[128 c]
-    // is element 0 of lane 4 c.  Butterflies over lane bits 2, 3 (and 4 for 1024-blocks).
-    float g = v128;
-#pragma unroll
-    for (int j = 2; j < (L == 512 ? 4 : 5); ++j) {
-      const float sgn = ((lane >> j) & 1) ? -1.f : 1.f;
-      g = fmaf(sgn, g, xor_lane(g, j, lane));
-    }
-    if (lane < 32 && (lane & 3) == 0)
-      lds_xf[g0 + (lane >> 2)] = make_float2(g * (128.f * inv_sqrt_block_or_one<L>()), f);
-  } else {
-    // no rotation: sum the 4 values of each group held by the lane, then over
-    // the 32 lanes of the lane half
-#pragma unroll
-    for (int Q = 0; Q < 4; ++Q) {
-      float sm = (U[4 * Q] + U[4 * Q + 1]) + (U[4 * Q + 2] + U[4 * Q + 3]);
-#pragma unroll
-      for (int j = 0; j < 5; ++j) sm += xor_lane(sm, j, lane);
-      if ((lane & 31) == 0) lds_xf[g0 + h + 2 * Q] = make_float2(sm, f);
-    }
-  }
+  xform_group_sums<L>(U, v128, g0, lane, f, lds_xf);
 }
 
 }  // namespace tb
