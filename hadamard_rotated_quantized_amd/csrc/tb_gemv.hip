@@ -11,9 +11,11 @@
 // which is sum_k (s c + b) xr, i.e. W~ xr, regrouped per 128-weight group.
 //
 // Design for gfx950 (the weight stream is the cost: 9/32 byte per weight).
-// tb_ternary_gemv runs the single-launch kernel of tb_gemv_fused.hip when a
-// workgroup can afford to transform the input itself (short inputs, small
-// batches); otherwise, and always for the prepare/run pair, two kernels:
+// tb_ternary_gemv picks, in order: the K-split batch kernel of
+// tb_gemv_batch.hip (batches 2..8), the band kernel of tb_gemv_band.hip
+// (batch 1), the single-launch kernel of tb_gemv_fused.hip (a workgroup can
+// afford to transform the whole input); otherwise, and always for the
+// prepare/run pair, two kernels:
 //
 // 1. gemv_prep_kernel: one wave per 1024 inputs of one batch row.  Lane l
 //    holds inputs 16 l .. 16 l + 15 of the chunk in registers: the transform
