@@ -416,6 +416,10 @@ TWO_PATHS = [
     (9000, 1024, 1, 1024, "bf16"),   # 563 tiles: 4 waves per tile
     (45, 640, 1, 0, "f32"),          # 5 groups (3 padding), last band of 13 rows
     (1000, 384, 2, 0, "bf16"),       # 6-byte scale rows: band ends mid 16 bytes
+    (6000, 8192, 1, 1024, "bf16"),   # band kernel, 4 matmul items per wave
+    (6000, 4096, 1, 512, "f32"),     # band kernel, 2 items per wave, 512-blocks
+    (1500, 3072, 6, 512, "f32"),     # K-split batch kernel, two sets of 4 batch rows
+    (777, 17408, 3, 1024, "f32"),    # K-split batch kernel, several slices, ragged N
 ]
 
 
@@ -479,3 +483,57 @@ def test_gemv_one_call_graph_replays_match_eager():
         assert T.equal(y, eager), i
         tb.tb_ternary_gemv_run(tb.tb_ternary_gemv_prepare(x, sg, 1024), 1, 5120, codes, s, b)
         T.cuda.synchronize()
+
+
+def test_gemv_batch_graph_replays_match_eager():
+    """Decode batch on the down_proj shape (K split over several workgroups,
+    partial rows in the workspace, slice sums in a second launch), captured in
+    a HIP graph: every replay, with eager work in between, equals the eager
+    result bitwise."""
+    announce("gemv batch graph replay")
+    T = torch()
+    p = synth.make_problem("graphb", 5120, 17408, 4, 47, "bf16", 1024)
+    codes, s, b = pack_to_device(p.t, p.scales)
+    x = x_to_device(p)
+    sg = signs_to_device(p.signs)
+    ws = T.empty(tb.tb_ternary_gemv_workspace_size_n(4, 17408, 5120), dtype=T.uint8, device="cuda")
+    eager = tb.tb_ternary_gemv(x, sg, 1024, codes, s, b, workspace=ws)
+    T.cuda.synchronize()
+    oc, osc, ob = oracle_pack(p)
+    compare(eager.cpu().numpy(), oracle.packed_linear(p.x64, p.signs, 1024, oc, osc, ob), "batch eager")
+    y = T.empty_like(eager)
+    g = T.cuda.CUDAGraph()
+    with T.cuda.graph(g):
+        tb.tb_ternary_gemv(x, sg, 1024, codes, s, b, out=y, workspace=ws)
+    for i in range(4):
+        y.fill_(float("nan"))
+        g.replay()
+        T.cuda.synchronize()
+        assert T.equal(y, eager), i
+        tb.tb_ternary_gemv(x[:2].contiguous(), sg, 1024, codes, s, b)  # eager work between replays
+        T.cuda.synchronize()
+
+
+def test_gemv_batch_with_small_workspace_takes_another_path():
+    """A workspace sized for the prepare/run pair only (smaller than the
+    K-split partial rows) is still a valid call: tb_ternary_gemv then runs a
+    path that fits it, with the same result to 1e-6 relative."""
+    announce("gemv batch small workspace")
+    T = torch()
+    B, K, N = 4, 17408, 5120
+    small = tb.tb_ternary_gemv_workspace_size(B, K)
+    full = tb.tb_ternary_gemv_workspace_size_n(B, K, N)
+    assert full > small
+    p = synth.make_problem("smallws", N, K, B, 48, "bf16", 1024)
+    codes, s, b = pack_to_device(p.t, p.scales)
+    x = x_to_device(p)
+    sg = signs_to_device(p.signs)
+    y_small = tb.tb_ternary_gemv(x, sg, 1024, codes, s, b,
+                                 workspace=T.empty(small, dtype=T.uint8, device="cuda"))
+    y_full = tb.tb_ternary_gemv(x, sg, 1024, codes, s, b,
+                                workspace=T.empty(full, dtype=T.uint8, device="cuda"))
+    T.cuda.synchronize()
+    oc, osc, ob = oracle_pack(p)
+    compare(y_small.cpu().numpy(), oracle.packed_linear(p.x64, p.signs, 1024, oc, osc, ob), "small workspace")
+    d = (y_small.double() - y_full.double()).abs().max().item()
+    assert d <= 1e-6 * y_full.abs().max().item(), d
