@@ -11,11 +11,16 @@
 //    input, the in-register MFMA transform (tb_xform.h), writing each
 //    module's exact four-limb operand image and group sums to the workspace.
 //
-// 2. multi_stream_kernel: one persistent workgroup per CU.  The host splits
-//    the concatenated list of 16-row tiles (all modules, in order) into one
-//    contiguous range per workgroup, balanced by weight bytes.  For each
-//    module in its range a workgroup copies the module's operand image into
-//    LDS once; its 8 waves then take the range's tiles round robin.  A wave
+// 2. multi_stream_kernel: one persistent workgroup per CU.  The host cuts
+//    the concatenated list of 16-row tiles (all modules, in order) into
+//    pieces of one module each, large first and smaller toward the end of the
+//    list (each about 1 / workgroups of the weight bytes still left, down to
+//    a floor), and the workgroups take pieces in list order from a
+//    counter in the workspace (the transform kernel zeroes it), so a
+//    workgroup that streams slower than the others simply takes fewer pieces.
+//    For a piece of a module other than its last one a workgroup copies the
+//    module's operand image into LDS; its 8 waves then take the piece's tiles
+//    round robin.  A wave
 //    streams its tiles span by span (16 rows x 4 groups: 2 KB of codes, 128 B
 //    of scales, 128 B of biases) through a ring of P register slots: lane
 //    (lane group lg, row c) loads the 32 code bytes it multiplies straight
@@ -27,6 +32,7 @@
 //    bias applied in fp32; a tile's rows are written once, after its last
 //    span.
 #include <algorithm>
+#include <array>
 #include <vector>
 
 #include "tb_xform.h"
@@ -43,11 +49,13 @@ constexpr int kMultiImgChunk = 8 * kXfLimbs * 128;  // workspace bytes of one ch
 constexpr int kMultiRing = 4;                       // span pairs in flight per wave
 constexpr int kMultiYbuf = 32;                      // finished tiles a wave holds in LDS before writing them
 constexpr int64_t kMultiLdsMax = 150 * 1024;
+constexpr int kMultiWsHead = 256;                   // workspace bytes before the first image: the piece counter
+constexpr int kMultiPieceFloor = 16;                // smallest piece: 1 / 16 of a workgroup's mean share
 
 struct MultiHeader {  // 64 bytes
   int32_t magic, count, tasks, grid;
-  int32_t block, x_dtype, max_nch, ring;
-  int64_t modules_off, tasks_off, ranges_off, total_bytes;
+  int32_t block, x_dtype, max_nch, pieces;
+  int64_t modules_off, tasks_off, pieces_off, total_bytes;
 };
 struct MultiModule {  // 64 bytes
   const void* x;
@@ -82,6 +90,9 @@ __global__ __launch_bounds__(256) void multi_prep_kernel(const char* __restrict_
   const MultiHeader* hd = reinterpret_cast<const MultiHeader*>(plan);
   const int lane = threadIdx.x & 63;
   const int task = static_cast<int>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // the stream kernel's piece counter starts at zero (this kernel runs first
+  // on the stream)
+  if (blockIdx.x == 0 && threadIdx.x == 0) *reinterpret_cast<int*>(ws) = 0;
   if (task >= hd->tasks) return;  // whole wave; the kernel has no barrier
   const int2 tk = reinterpret_cast<const int2*>(plan + hd->tasks_off)[task];
   const MultiModule md = reinterpret_cast<const MultiModule*>(plan + hd->modules_off)[tk.x];
@@ -110,14 +121,17 @@ struct MultiPair {
 
 template <int NW, int P>
 __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __restrict__ plan,
-                                                                  const char* __restrict__ ws) {
+                                                                  char* __restrict__ ws) {
   constexpr int kMultiThreads = 64 * NW;
   constexpr int M = 16, GPS = 4;
   extern __shared__ uint4 lds_dyn[];
   char* const lds = reinterpret_cast<char*>(lds_dyn);
   const MultiHeader* hd = reinterpret_cast<const MultiHeader*>(plan);
   const MultiModule* mods = reinterpret_cast<const MultiModule*>(plan + hd->modules_off);
-  const int4 rg = reinterpret_cast<const int4*>(plan + hd->ranges_off)[blockIdx.x];
+  const int4* const pieces = reinterpret_cast<const int4*>(plan + hd->pieces_off);
+  const int npieces = hd->pieces;
+  int* const counter = reinterpret_cast<int*>(ws);
+  __shared__ int piece_next;
   const int max_nch = hd->max_nch;
   char* const lds_a = lds;
   const float2* const lds_xf = reinterpret_cast<const float2*>(lds + multi_lds_xf(max_nch));
@@ -128,19 +142,24 @@ __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __
   const bool a_lane = alg == lg;
   float* const ybuf = reinterpret_cast<float*>(lds + multi_lds_ybuf(max_nch)) + wave * (kMultiYbuf * 16);
 
-  int T = rg.y;
-  const int T1 = rg.z;
-  for (int m = rg.x; T < T1; ++m) {
+  int img_m = -1;  // module whose image is in LDS
+  for (;;) {
+    // the next piece, taken by one lane (a vector atomic) and shared in LDS
+    if (tid == 0) piece_next = atomicAdd(counter, 1);
+    __syncthreads();
+    const int pc = __builtin_amdgcn_readfirstlane(piece_next);
+    if (pc >= npieces) break;  // uniform: every wave leaves
+    const int4 pz = pieces[pc];
+    const int m = __builtin_amdgcn_readfirstlane(pz.x);
+    const int ta = __builtin_amdgcn_readfirstlane(pz.y), tb = __builtin_amdgcn_readfirstlane(pz.z);
     const MultiModule md = mods[m];
-    const int nt = (md.N + M - 1) / M;
-    const int ta = max(T, md.tile0), tb = min(T1, md.tile0 + nt);
-    if (ta >= tb) continue;
-    T = tb;
     const int K = md.K, G = K / kGroup, RB = K / 4;
     const int S = (G + GPS - 1) / GPS;
     const int nch = multi_nch(K);
-    // the module's operand image and group sums into LDS
-    {
+    // the module's operand image and group sums into LDS (unless they are
+    // there from the previous piece)
+    if (m != img_m) {
+      img_m = m;
       const char* img = ws + md.ws_off;
       const int rows = nch * 8 * kXfLimbs;
       for (int i = tid; i < rows * 8; i += kMultiThreads) {
@@ -150,8 +169,8 @@ __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __
       }
       const float2* xfg = reinterpret_cast<const float2*>(img + static_cast<int64_t>(nch) * kMultiImgChunk);
       for (int i = tid; i < nch * 8; i += kMultiThreads) const_cast<float2*>(lds_xf)[i] = xfg[i];
+      __syncthreads();
     }
-    __syncthreads();
 
     // this wave's tiles: ta + wave + NW j, j < ntw.  The unit of the ring is
     // a pair of spans (2 p, 2 p + 1) of one tile: P2 = ceil(S / 2) pairs per
@@ -270,7 +289,7 @@ __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __
       }
     }
     flush(j);
-    __syncthreads();  // the next module's image replaces this one
+    __syncthreads();  // the next piece's number and image replace this one's
   }
 }
 
@@ -290,15 +309,45 @@ static inline int64_t align64(int64_t v) { return (v + 63) & ~int64_t(63); }
 // byte offsets of the plan's sections (each 64-byte aligned: the kernels read
 // them with vector and scalar loads of up to 16 bytes)
 struct PlanOffsets {
-  int64_t modules, tasks, ranges, total;
+  int64_t modules, tasks, pieces, total;
 };
-static PlanOffsets plan_offsets(int64_t count, int64_t ntasks, int64_t grid) {
+static PlanOffsets plan_offsets(int64_t count, int64_t ntasks, int64_t npieces) {
   PlanOffsets o;
   o.modules = sizeof(MultiHeader);
   o.tasks = align64(o.modules + count * static_cast<int64_t>(sizeof(MultiModule)));
-  o.ranges = align64(o.tasks + ntasks * 8);
-  o.total = align64(o.ranges + grid * 16);
+  o.pieces = align64(o.tasks + ntasks * 8);
+  o.total = align64(o.pieces + npieces * 16);
   return o;
+}
+
+// The pieces of the concatenated tile list, as (module, first tile, end tile)
+// with global tile indices.  A tile costs its weight groups plus 2 (its
+// scale / bias rows and fixed work); a piece takes tiles of one module until
+// its cost reaches max(floor, left / grid), where left is the cost not yet
+// cut, so pieces shrink toward the end and the last ones even out the
+// workgroups' finishing times.
+static std::vector<std::array<int32_t, 3>> multi_pieces(const tb_gemv_module* mods, int64_t count, int grid) {
+  int64_t total = 0;
+  for (int64_t i = 0; i < count; ++i)
+    if (mods[i].N > 0) total += (mods[i].N + 15) / 16 * (mods[i].K / 128 + 2);
+  const int64_t floor_cost = std::max<int64_t>(1, total / (static_cast<int64_t>(grid) * kMultiPieceFloor));
+  std::vector<std::array<int32_t, 3>> out;
+  int64_t left = total, tile = 0;
+  for (int64_t i = 0; i < count; ++i) {
+    const tb_gemv_module& m = mods[i];
+    if (m.N <= 0) continue;
+    const int64_t ntm = (m.N + 15) / 16, tc = m.K / 128 + 2;
+    int64_t t = 0;
+    while (t < ntm) {
+      const int64_t want = std::max(floor_cost, left / static_cast<int64_t>(grid));
+      const int64_t take = std::min(ntm - t, std::max<int64_t>(1, (want + tc - 1) / tc));
+      out.push_back({static_cast<int32_t>(i), static_cast<int32_t>(tile + t), static_cast<int32_t>(tile + t + take)});
+      t += take;
+      left -= take * tc;
+    }
+    tile += ntm;
+  }
+  return out;
 }
 
 static int64_t multi_total_tasks(const tb_gemv_module* mods, int64_t count) {
@@ -314,7 +363,10 @@ using namespace tb;
 
 extern "C" size_t tb_gemv_multi_plan_size(const tb_gemv_module* mods, int64_t count) {
   if (!mods || count <= 0) return 0;
-  return static_cast<size_t>(plan_offsets(count, multi_total_tasks(mods, count), multi_device_cus()).total);
+  for (int64_t i = 0; i < count; ++i)
+    if (mods[i].N < 0 || mods[i].K <= 0) return 0;  // the plan call reports the error
+  const int64_t np = static_cast<int64_t>(multi_pieces(mods, count, multi_device_cus()).size());
+  return static_cast<size_t>(plan_offsets(count, multi_total_tasks(mods, count), np).total);
 }
 
 extern "C" int tb_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int x_dtype, int block, void* plan,
@@ -371,7 +423,6 @@ extern "C" int tb_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int
     ws += static_cast<int64_t>(nch) * (kMultiImgChunk + 64);
     cost += (m.N + 15) / 16 * (m.K / 128 + 2);
   }
-  const int ring = kMultiRing;
   if (multi_lds_total(max_nch) > kMultiLdsMax) {
     set_error("%s: K up to %d takes too much LDS for the stream kernel", who, max_nch * 1024);
     return TB_ERR_UNSUPPORTED;
@@ -382,7 +433,12 @@ extern "C" int tb_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int
   }
   const int grid = multi_device_cus();
   const int64_t ntasks = multi_total_tasks(mods, count);
-  const PlanOffsets po = plan_offsets(count, ntasks, grid);
+  const std::vector<std::array<int32_t, 3>> pcs = multi_pieces(mods, count, grid);
+  if (pcs.size() >= (size_t(1) << 30)) {
+    set_error("%s: the module list is too large for one plan", who);
+    return TB_ERR_SHAPE;
+  }
+  const PlanOffsets po = plan_offsets(count, ntasks, static_cast<int64_t>(pcs.size()));
   const size_t need = static_cast<size_t>(po.total);
   if (plan_bytes < need) {
     set_error("%s: plan buffer of %zu bytes, %zu needed", who, plan_bytes, need);
@@ -398,16 +454,16 @@ extern "C" int tb_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int
   hd.block = block;
   hd.x_dtype = x_dtype;
   hd.max_nch = max_nch;
-  hd.ring = ring;
+  hd.pieces = static_cast<int32_t>(pcs.size());
   hd.modules_off = po.modules;
   hd.tasks_off = po.tasks;
-  hd.ranges_off = po.ranges;
+  hd.pieces_off = po.pieces;
   hd.total_bytes = static_cast<int64_t>(need);
   std::memcpy(p, &hd, sizeof hd);
   MultiModule* md = reinterpret_cast<MultiModule*>(p + hd.modules_off);
   int32_t* tk = reinterpret_cast<int32_t*>(p + hd.tasks_off);
   std::vector<int64_t> tile_cost;  // per module: cost of one tile
-  int64_t t0 = 0, off = 0, nt = 0;
+  int64_t t0 = 0, off = kMultiWsHead, nt = 0;
   for (int64_t i = 0; i < count; ++i) {
     const tb_gemv_module& m = mods[i];
     MultiModule d{};
@@ -432,43 +488,14 @@ extern "C" int tb_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int
     t0 += (m.N + 15) / 16;
     off += static_cast<int64_t>(nch) * (kMultiImgChunk + 64);
   }
-  // contiguous tile ranges of about equal weight bytes: workgroup g takes the
-  // tiles whose cumulative cost starts in [g C / grid, (g + 1) C / grid)
-  int32_t* rg = reinterpret_cast<int32_t*>(p + hd.ranges_off);
-  {
-    int64_t acc = 0, tile = 0;
-    int g = 0;
-    int64_t m_of_g = 0;
-    rg[0] = 0;
-    rg[1] = 0;
-    for (int64_t i = 0; i < count && g < grid; ++i) {
-      const tb_gemv_module& m = mods[i];
-      if (m.N == 0) continue;
-      const int64_t ntm = (m.N + 15) / 16, tc = m.K / 128 + 2;
-      for (int64_t t = 0; t < ntm; ++t, ++tile) {
-        // tile starts at cost acc: move to the workgroup that owns acc
-        while (g + 1 < grid && acc * grid >= (g + 1) * cost) {
-          rg[4 * g + 2] = static_cast<int32_t>(tile);
-          rg[4 * g + 3] = 0;
-          ++g;
-          rg[4 * g] = static_cast<int32_t>(i);
-          rg[4 * g + 1] = static_cast<int32_t>(tile);
-        }
-        acc += tc;
-      }
-      m_of_g = i;
-    }
-    (void)m_of_g;
-    rg[4 * g + 2] = static_cast<int32_t>(tiles);
-    rg[4 * g + 3] = 0;
-    for (int h = g + 1; h < grid; ++h) {  // workgroups without tiles
-      rg[4 * h] = 0;
-      rg[4 * h + 1] = static_cast<int32_t>(tiles);
-      rg[4 * h + 2] = static_cast<int32_t>(tiles);
-      rg[4 * h + 3] = 0;
-    }
+  int32_t* pq = reinterpret_cast<int32_t*>(p + hd.pieces_off);
+  for (size_t k = 0; k < pcs.size(); ++k) {
+    pq[4 * k] = pcs[k][0];
+    pq[4 * k + 1] = pcs[k][1];
+    pq[4 * k + 2] = pcs[k][2];
+    pq[4 * k + 3] = 0;
   }
-  *workspace_bytes = static_cast<size_t>(std::max<int64_t>(ws, 256));
+  *workspace_bytes = static_cast<size_t>(kMultiWsHead + ws);
   return TB_OK;
 }
 
@@ -479,7 +506,7 @@ static void multi_prep_launch(const void* plan, void* ws, int tasks, hipStream_t
 }
 
 template <int NW, int P>
-static void multi_stream_launch(const void* plan, const void* ws, int grid, size_t lds, hipStream_t st) {
+static void multi_stream_launch(const void* plan, void* ws, int grid, size_t lds, hipStream_t st) {
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(multi_stream_kernel<NW, P>),
@@ -487,7 +514,7 @@ static void multi_stream_launch(const void* plan, const void* ws, int grid, size
     attr_set = true;
   }
   hipLaunchKernelGGL((multi_stream_kernel<NW, P>), dim3(grid), dim3(64 * NW), lds, st,
-                     static_cast<const char*>(plan), static_cast<const char*>(ws));
+                     static_cast<const char*>(plan), static_cast<char*>(ws));
 }
 
 extern "C" int tb_ternary_gemv_multi(const void* plan_host, const void* plan_device, void* workspace,
@@ -499,7 +526,7 @@ extern "C" int tb_ternary_gemv_multi(const void* plan_host, const void* plan_dev
   }
   MultiHeader hd;
   std::memcpy(&hd, plan_host, sizeof hd);
-  if (hd.magic != kPlanMagic || hd.count <= 0 || hd.grid <= 0 || hd.ring != kMultiRing) {
+  if (hd.magic != kPlanMagic || hd.count <= 0 || hd.grid <= 0 || hd.pieces < 0) {
     set_error("%s: the host plan was not built by tb_gemv_multi_plan", who);
     return TB_ERR_ARG;
   }
@@ -509,7 +536,7 @@ extern "C" int tb_ternary_gemv_multi(const void* plan_host, const void* plan_dev
   }
   // the workspace size the plan needs: the last module's image end
   const MultiModule* md = reinterpret_cast<const MultiModule*>(static_cast<const char*>(plan_host) + hd.modules_off);
-  int64_t need = 256;
+  int64_t need = kMultiWsHead;
   for (int i = 0; i < hd.count; ++i)
     if (md[i].N > 0) need = std::max<int64_t>(need, md[i].ws_off + static_cast<int64_t>(multi_nch(md[i].K)) * (kMultiImgChunk + 64));
   if (ws_bytes < static_cast<size_t>(need)) {

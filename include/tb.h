@@ -238,9 +238,11 @@ size_t tb_gemv_multi_plan_size(const tb_gemv_module* mods, int64_t count);
 /* Build the plan (host memory, plan_bytes >= tb_gemv_multi_plan_size) for the
  * modules (host array), all sharing x_dtype and block (0, 512 or 1024), and
  * report the workspace the run needs.  The plan holds the module table, the
- * transform tasks and a split of all modules' 16-row output tiles into one
- * range per workgroup of about equal weight bytes; it embeds the device
- * pointers of the modules, so it stays valid while those buffers do.  Errors:
+ * transform tasks and a split of all modules' 16-row output tiles into
+ * pieces of one module each (shrinking toward the end of the list) that the
+ * streaming workgroups take in order from a counter in the workspace; it
+ * embeds the device pointers of the modules, so it stays valid while those
+ * buffers do.  Errors:
  * TB_ERR_ARG, TB_ERR_SHAPE (K % 256 or K % block), TB_ERR_BLOCK /
  * TB_ERR_UNSUPPORTED (block 2048/4096, or K too large for the kernel's LDS),
  * TB_ERR_DTYPE, TB_ERR_ALIGN, TB_ERR_WORKSPACE (plan buffer too small). */

@@ -1,11 +1,10 @@
 """Host logic of the multi-module decode plan (no GPU): argument checks, and
-that the per-workgroup tile ranges partition the concatenated tile list with
-about equal weight bytes per workgroup.  The plan layout parsed here is the
-one tb_gemv_multi.hip writes: a 64-byte header (int32 magic, count, tasks,
-grid, block, x_dtype, max_nch, ring; int64 modules_off, tasks_off,
-ranges_off, total_bytes), 64 bytes per module, int32 pairs (module, chunk)
-per transform task, and int32 quadruples (first module, first tile, end
-tile, 0) per workgroup."""
+that the pieces partition the concatenated tile list, each within one
+module, shrinking toward the end.  The plan layout parsed here is the one
+tb_gemv_multi.hip writes: a 64-byte header (int32 magic, count, tasks, grid,
+block, x_dtype, max_nch, pieces; int64 modules_off, tasks_off, pieces_off,
+total_bytes), 64 bytes per module, int32 pairs (module, chunk) per transform
+task, and int32 quadruples (module, first tile, end tile, 0) per piece."""
 import ctypes
 
 import numpy as np
@@ -37,19 +36,19 @@ def _plan(shapes, block=1024, dtype=tb.TB_BF16):
 def _parse(plan):
     hd = plan[:32].view(np.int32)
     offs = plan[32:64].view(np.int64)
-    magic, count, tasks, grid, block, xdt, max_nch, ring = [int(v) for v in hd]
+    magic, count, tasks, grid, block, xdt, max_nch, npieces = [int(v) for v in hd]
     mods = plan[offs[0]:offs[0] + 64 * count].reshape(count, 64)
     NK = mods[:, 48:64].copy().view(np.int32)  # N, K, tile0, ws_off
     tk = plan[offs[1]:offs[1] + 8 * tasks].view(np.int32).reshape(tasks, 2)
-    rg = plan[offs[2]:offs[2] + 16 * grid].view(np.int32).reshape(grid, 4)
-    return dict(magic=magic, count=count, tasks=tasks, grid=grid, max_nch=max_nch, NK=NK, tk=tk, rg=rg)
+    pc = plan[offs[2]:offs[2] + 16 * npieces].view(np.int32).reshape(npieces, 4)
+    return dict(magic=magic, count=count, tasks=tasks, grid=grid, max_nch=max_nch, NK=NK, tk=tk, pc=pc)
 
 
 SWEEPLIKE = [(10240, 5120), (6144, 5120), (5120, 6144), (17408, 5120), (17408, 5120), (5120, 17408),
              (6144, 5120), (1024, 5120), (1024, 5120), (5120, 6144), (0, 5120), (45, 2048), (248320, 5120)]
 
 
-def test_plan_tasks_and_ranges_partition_tiles():
+def test_plan_tasks_and_pieces_partition_tiles():
     st, plan, ws = _plan(SWEEPLIKE)
     assert st == tb.TB_OK, tb.lib().tb_last_error()
     p = _parse(plan)
@@ -63,24 +62,30 @@ def test_plan_tasks_and_ranges_partition_tiles():
     total = sum(tiles)
     tile0 = np.cumsum([0] + tiles[:-1])
     assert list(p["NK"][:, 2]) == list(tile0)
-    # workspace: 4 KB of operand image (8 groups x 4 limbs x 128 B) + 64 B of group sums per chunk
-    assert ws == sum((4096 + 64) * c for c, (N, K) in zip(nch, SWEEPLIKE) if N > 0)
-    # ranges: contiguous, cover [0, total) once, start module owns the start tile
-    rg = p["rg"]
-    assert rg[0, 1] == 0
-    for g in range(p["grid"] - 1):
-        assert rg[g, 2] == rg[g + 1, 1]
-    assert rg[-1, 2] == total
+    # workspace: a 256-byte head (the piece counter), then per chunk 4 KB of
+    # operand image (8 groups x 4 limbs x 128 B) + 64 B of group sums
+    assert ws == 256 + sum((4096 + 64) * c for c, (N, K) in zip(nch, SWEEPLIKE) if N > 0)
+    assert list(p["NK"][:, 3][np.array(tiles) > 0][:1]) == [256]
+    # pieces: contiguous, cover [0, total) once in order, each inside its module
+    pc = p["pc"]
+    assert pc[0, 1] == 0 and pc[-1, 2] == total
+    assert (pc[1:, 1] == pc[:-1, 2]).all() and (pc[:, 2] > pc[:, 1]).all()
+    for m, a, b, _ in pc:
+        assert tile0[m] <= a < b <= tile0[m] + tiles[m]
+    # sizes: about 1/grid of the cost still left, never below the floor
+    # (1/16 of a workgroup's mean share) unless a module ends first
     cost_tile = np.concatenate([np.full(t, K // 128 + 2) for t, (N, K) in zip(tiles, SWEEPLIKE)])
     cum = np.concatenate([[0], np.cumsum(cost_tile)])
-    share = cum[-1] / p["grid"]
-    for g in range(p["grid"]):
-        a, b = rg[g, 1], rg[g, 2]
-        if a < b:
-            m = rg[g, 0]
-            assert tile0[m] <= a < tile0[m] + tiles[m]
-            # no workgroup exceeds its share by more than one tile
-            assert cum[b] - cum[a] <= share + cost_tile.max()
+    floor = max(1, cum[-1] // (p["grid"] * 16))
+    for m, a, b, _ in pc:
+        left = cum[-1] - cum[a]
+        want = max(floor, left // p["grid"])
+        tc = SWEEPLIKE[m][1] // 128 + 2
+        ends_module = b == tile0[m] + tiles[m]
+        assert cum[b] - cum[a] <= want + tc
+        assert ends_module or cum[b] - cum[a] >= want
+    # the first pieces are large, the last ones small
+    assert (cum[pc[0, 2]] - cum[pc[0, 1]]) > 4 * (cum[pc[-2, 2]] - cum[pc[-2, 1]])
 
 
 @pytest.mark.parametrize("shapes,block,status", [
