@@ -138,10 +138,10 @@ int tb_fwht_signed(const void* x, int x_dtype, float* y, const int8_t* signs,
 size_t tb_ternary_gemv_workspace_size(int64_t B, int64_t K);
 
 /* Workspace bytes that let tb_ternary_gemv take its decode-batch path
- * (2 <= B <= TB_GEMV_MAX_BATCH, block 0, 512 or 1024) for an N x K weight
- * matrix: the per-row transform, and the partial sums of a K-split stream
- * (which grow with N).  Never less than tb_ternary_gemv_workspace_size(B, K);
- * given less than this, tb_ternary_gemv uses its other batch path. */
+ * (2 <= B <= TB_GEMV_MAX_BATCH, block 0, 512 or 1024, K a multiple of 256)
+ * for an N x K weight matrix: the partial rows of a K-split stream (which
+ * grow with N).  Never less than tb_ternary_gemv_workspace_size(B, K); given
+ * less than this, tb_ternary_gemv uses its other batch path. */
 size_t tb_ternary_gemv_workspace_size_n(int64_t B, int64_t K, int64_t N);
 
 /* Packed linear for decode batches [P3 "text model loading"]:
@@ -153,11 +153,12 @@ size_t tb_ternary_gemv_workspace_size_n(int64_t B, int64_t K, int64_t N);
  * aligned, needing no initialisation; it must not be reused by another call
  * until this one completes on the stream.  Equivalent to
  * tb_ternary_gemv_prepare followed by tb_ternary_gemv_run on one stream.
- * For 2 <= B <= 8 and block 0, 512 or 1024, a workspace of
- * tb_ternary_gemv_workspace_size_n(B, K, N) bytes selects the decode-batch
- * path: each CU streams a 128-row block of the weights over one K slice
- * against every batch row's exact operand, and the slices' partial rows are
- * summed in slice order (results do not depend on scheduling). */
+ * For 2 <= B <= 8, block 0, 512 or 1024 and K a multiple of 256, a
+ * workspace of tb_ternary_gemv_workspace_size_n(B, K, N) bytes selects the
+ * decode-batch path: each CU transforms one K slice of every batch row into
+ * exact integer operands in LDS and streams a 128-row block of the weights
+ * over it, and the slices' partial rows are summed in slice order (results
+ * do not depend on scheduling). */
 int tb_ternary_gemv(const void* x, int x_dtype, int64_t B, int64_t K,
                     const int8_t* signs, int block,
                     const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
