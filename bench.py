@@ -135,7 +135,7 @@ def run_counter_pass(args):
         b0 = torch.from_numpy(b).to(dev)
         x = torch.from_numpy(p.x_store.view(np.int16)).view(torch.bfloat16).to(dev)
         sg = torch.from_numpy(p.signs).to(dev)
-        ws = torch.empty(tb.tb_ternary_gemm_workspace_size(p.B, p.K), dtype=torch.uint8, device=dev)
+        ws = torch.empty(tb.tb_ternary_gemm_workspace_size_n(p.B, p.K, p.N), dtype=torch.uint8, device=dev)
         y = torch.empty((p.B, p.N), dtype=torch.float32, device=dev)
         for _ in range(5):
             tb.tb_ternary_gemm(x, sg, p.block, c0, s0, b0, out=y, workspace=ws)
@@ -343,7 +343,7 @@ def run_prefill(args):
     b0 = torch.from_numpy(b).to(dev)
     x = torch.from_numpy(p.x_store.view(np.int16)).view(torch.bfloat16).to(dev)
     sg = torch.from_numpy(p.signs).to(dev)
-    ws = torch.empty(tb.tb_ternary_gemm_workspace_size(M, K), dtype=torch.uint8, device=dev)
+    ws = torch.empty(tb.tb_ternary_gemm_workspace_size_n(M, K, N), dtype=torch.uint8, device=dev)
     y = torch.empty((M, N), dtype=torch.float32, device=dev)
     tb.tb_ternary_gemm(x, sg, p.block, c0, s0, b0, out=y, workspace=ws)
     torch.cuda.synchronize()

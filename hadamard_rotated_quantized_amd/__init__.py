@@ -47,6 +47,7 @@ _SIGNATURES = {
     "tb_ternary_gemv_prepare": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _SZ, _P]),
     "tb_ternary_gemv_run": (_I, [_P, _SZ, _I64, _I64, _P, _P, _P, _I64, _P, _P]),
     "tb_ternary_gemm_workspace_size": (_SZ, [_I64, _I64]),
+    "tb_ternary_gemm_workspace_size_n": (_SZ, [_I64, _I64, _I64]),
     "tb_ternary_gemm_prepare": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _SZ, _P]),
     "tb_ternary_gemm_run": (_I, [_P, _SZ, _I64, _I64, _P, _P, _P, _I64, _P, _P]),
     "tb_ternary_gemm": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
@@ -203,6 +204,10 @@ def tb_ternary_gemm_workspace_size(M: int, K: int) -> int:
     return int(lib().tb_ternary_gemm_workspace_size(M, K))
 
 
+def tb_ternary_gemm_workspace_size_n(M: int, K: int, N: int) -> int:
+    return int(lib().tb_ternary_gemm_workspace_size_n(M, K, N))
+
+
 def _container(codes, scales, biases):
     torch = _torch()
     _dev(codes, "codes")
@@ -262,13 +267,15 @@ def tb_ternary_gemv_run(workspace, B: int, K: int, codes, scales, biases, out=No
     return out
 
 
-def tb_ternary_gemm_prepare(x, signs, block: int, workspace=None):
+def tb_ternary_gemm_prepare(x, signs, block: int, workspace=None, N: int | None = None):
+    """Rotate x (M, K) into a new (or the given) workspace; with N, the new
+    workspace is sized for runs against N output columns (tail split)."""
     torch = _torch()
     _dev(x, "x")
     if signs is not None:
         _dev(signs, "signs", torch.int8)
     M, K = x.shape
-    need = tb_ternary_gemm_workspace_size(M, K)
+    need = tb_ternary_gemm_workspace_size(M, K) if N is None else tb_ternary_gemm_workspace_size_n(M, K, N)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     _check(lib().tb_ternary_gemm_prepare(x.data_ptr(), _xdtype(x), M, K, _ptr(signs), block,
@@ -290,7 +297,8 @@ def tb_ternary_gemm_run(workspace, M: int, K: int, codes, scales, biases, out=No
 
 
 def tb_ternary_gemm(x, signs, block: int, codes, scales, biases, out=None, workspace=None):
-    """y (M, N) float32 = Packed linear of x (M, K), bf16 MFMA path."""
+    """y (M, N) float32 = Packed linear of x (M, K), block-scaled fp6 x fp4
+    MFMA path."""
     torch = _torch()
     _dev(x, "x")
     _container(codes, scales, biases)
@@ -301,7 +309,7 @@ def tb_ternary_gemm(x, signs, block: int, codes, scales, biases, out=None, works
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
     _dev(out, "out", torch.float32)
-    need = tb_ternary_gemm_workspace_size(M, K)
+    need = tb_ternary_gemm_workspace_size_n(M, K, N)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     _check(lib().tb_ternary_gemm(x.data_ptr(), _xdtype(x), M, K, _ptr(signs), block, codes.data_ptr(),

@@ -22,16 +22,19 @@
 //    the run's scale dword, so the four digit products of a run sum to
 //    c * sign * q * 2^E in the fp32 accumulator.  Each input carries a
 //    relative error of at most 2^-16 of its run's largest magnitude.
-//  * gemm_mx_kernel tiles the output 128 x 256 per workgroup (8 waves of
-//    32 x 128).  Per group of 128 inputs it stages the activation records and
-//    the code words through registers into a double-buffered LDS stage (one
-//    barrier per group), runs 2 k-steps x 4 digits x 4 column blocks of MFMAs
-//    into a per-group fp32 accumulator and folds y += s * acc in fp32.  The
-//    bias term sum_g b[n][g] X[m][g] runs after the loop on fp16 MFMA over
-//    the groups, with X (scaled by a per-row power of two) split into an
-//    exact-sum fp16 hi + lo pair.  Workgroups are mapped so that each XCD
-//    walks contiguous output tiles in M-major order: the XCD's workgroups
-//    share one activation row tile in that XCD's L2 while the codes stream.
+//  * gemm_mx_kernel tiles the output 64 x 512 per workgroup (8 waves of
+//    32 x 128).  Per group of 128 inputs, direct-to-LDS buffer loads bring
+//    the activation records, the code words and the scales into a stage of a
+//    three-stage LDS ring (one barrier per group); each wave runs 2 k-steps x
+//    4 digits x 4 column blocks of MFMAs into a per-group fp32 accumulator
+//    and folds y += s * acc in fp32.  The bias term sum_g b[n][g] X[m][g]
+//    runs after the loop on fp16 MFMA over the groups, with X (scaled by a
+//    per-row power of two) split into an exact-sum fp16 hi + lo pair.
+//    Workgroups are mapped so that each XCD walks a contiguous range of an
+//    order that covers bands of 8 row tiles column by column: the 32
+//    workgroups an XCD runs at once span 8 row tiles x 4 column tiles, so
+//    both their activation and their code slices are shared in its L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "tb_device.h"
@@ -66,6 +69,8 @@ constexpr int kCDma = kADma + kStageC / 1024; // codes: loads 25 .. 40
 constexpr int kSDma = kCDma + kStageS / 256;  // scales: loads 41 .. 48 (64 lanes x 4 B)
 constexpr int kDmaSlots = 7;                  // per wave and fill (56 slots, 7 of them padding)
 constexpr int kXcds = 8;
+constexpr int kMxBandRows = 8;               // row tiles per band of the tile order
+constexpr int kMxMaxSlices = 8;              // K slices per tail tile at most
 constexpr uint32_t kFp4Codes = 0x33333333u;
 constexpr int kScaleB = 128;                  // E8M0 of 2^1
 
@@ -316,19 +321,44 @@ __device__ __forceinline__ void mx_digit(const v4u_g* u, const v8i_g* bop, int s
                                                               0, kScaleB);
 }
 
+// First output row and column of tile t of the tile order: bands of
+// kMxBandRows row tiles, each walked column by column.
+__device__ __forceinline__ void mx_tile_origin(int t, int MT, int NT, int& m0, int& n0) {
+  const int band = t / (kMxBandRows * NT), within = t - band * kMxBandRows * NT;
+  const int gm = min(kMxBandRows, MT - band * kMxBandRows);
+  m0 = (band * kMxBandRows + within % gm) * kMxBM;
+  n0 = (within / gm) * kMxBN;
+}
+
+// Workgroups [0, 8 per_xcd) compute the first tiles_main tiles of the tile
+// order over all of K.  When the tiles do not fill a whole number of rounds
+// of the chip, the remaining tiles ("tail") are cut into ks slices of the
+// groups each, one workgroup per (tile, slice) after the main ones; a tail
+// workgroup writes its 64 x 512 partial sums to part[unit] (slice 0 adds the
+// bias term) and gemm_tail_sum_kernel adds the slices in order.
 __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
     const uint8_t* __restrict__ rec, const uint16_t* __restrict__ xh, const uint16_t* __restrict__ xl,
     const float* __restrict__ p2, const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, float* __restrict__ y, int M, int N, int G, int Gp, int MT, int NT,
-    int per_xcd) {
+    int per_xcd, int tiles_main, int ks, float* __restrict__ part) {
   // XCD-aware tile order: workgroup w runs on XCD w % 8; XCD x owns the
-  // contiguous M-major tile range [x * per_xcd, (x + 1) * per_xcd).
+  // contiguous range [x * per_xcd, (x + 1) * per_xcd) of the tile order, so
+  // the workgroups an XCD runs at once (8 row tiles x 4 column tiles) share
+  // both activation and code slices in its L2.
   const int wg = blockIdx.x;
-  const int jx = wg / kXcds;
-  const int tile = (wg % kXcds) * per_xcd + jx;
-  if (jx >= per_xcd || tile >= MT * NT) return;
-  const int m0 = (tile / NT) * kMxBM;
-  const int n0 = (tile % NT) * kMxBN;
+  int tile, unit = -1, gbeg = 0, gend = G;
+  if (wg < per_xcd * kXcds) {
+    tile = (wg % kXcds) * per_xcd + wg / kXcds;
+    if (tile >= tiles_main) return;
+  } else {
+    unit = wg - per_xcd * kXcds;
+    const int ti = unit / ks, slice = unit - ti * ks;
+    tile = tiles_main + ti;
+    gbeg = slice * G / ks;
+    gend = (slice + 1) * G / ks;
+  }
+  int m0, n0;
+  mx_tile_origin(tile, MT, NT, m0, n0);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -386,7 +416,7 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
   auto fill = [&](auto stage_tag, int g) {
     constexpr int ST = decltype(stage_tag)::value;
     const uint32_t dst = lds_addr(mx_stage<ST>());
-    const bool live = g < G;
+    const bool live = g < gend;
 #pragma unroll
     for (int i = 0; i < kDmaSlots; ++i) {
       const int q = wave + 8 * i;
@@ -452,8 +482,8 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
   // The matrix core works through each digit's MFMAs while the reads and
   // loads placed after them are issued.  The refill overwrites the stage of
   // group g - 1, whose reads all completed before the previous barrier.
-  fill(std::integral_constant<int, 0>{}, 0);
-  fill(std::integral_constant<int, 1>{}, 1);
+  fill(std::integral_constant<int, 0>{}, gbeg);
+  fill(std::integral_constant<int, 1>{}, gbeg + 1);
   __builtin_amdgcn_s_waitcnt(wait_vm(kDmaSlots));
   __builtin_amdgcn_s_barrier();
   MxOps r0;
@@ -513,11 +543,11 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
       for (int r = 0; r < 16; ++r) yv[nb][r] = fmaf(sv, acc[nb][r], yv[nb][r]);
     }
   };
-  for (int g = 0; g < G; g += 3) {
+  for (int g = gbeg; g < gend; g += 3) {
     step(std::integral_constant<int, 0>{}, g);
-    if (g + 1 >= G) break;
+    if (g + 1 >= gend) break;
     step(std::integral_constant<int, 1>{}, g + 1);
-    if (g + 2 >= G) break;
+    if (g + 2 >= gend) break;
     step(std::integral_constant<int, 2>{}, g + 2);
   }
 
@@ -533,7 +563,9 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
   v16f_g tb4[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) tb4[nb] = v16f_g{};
-  for (int s2 = 0; s2 < Gp / 16; ++s2) {
+  // (once per tile: tail slices other than the first skip it)
+  const int nbias = gbeg == 0 ? Gp / 16 : 0;
+  for (int s2 = 0; s2 < nbias; ++s2) {
     const int g0 = 16 * s2 + 8 * h;
     const int xo = ((wm * 32 + r32) * Gp + g0) * 2;
     const v4u_g ahv = __builtin_amdgcn_raw_buffer_load_b128(rxh, xo, 0, 0);
@@ -567,16 +599,59 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
     pr[4 * q + 2] = u.z;
     pr[4 * q + 3] = u.w;
   }
+  if (unit < 0) {
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int n = n0 + wn * 128 + 32 * nb + r32;
+    for (int nb = 0; nb < 4; ++nb) {
+      const int n = n0 + wn * 128 + 32 * nb + r32;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-      const float v = fmaf(pr[r], tb4[nb][r], yv[nb][r]);
-      if (m < M && n < N) y[static_cast<int64_t>(m) * N + n] = v;
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+        const float v = fmaf(pr[r], tb4[nb][r], yv[nb][r]);
+        if (m < M && n < N) y[static_cast<int64_t>(m) * N + n] = v;
+      }
+    }
+  } else {
+    // the whole 64 x 512 partial tile, row-major (rows past M or N hold
+    // sums over zeros)
+    float* const pt = part + static_cast<int64_t>(unit) * (kMxBM * kMxBN);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int nn = wn * 128 + 32 * nb + r32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int mm = wm * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+        pt[mm * kMxBN + nn] = fmaf(pr[r], tb4[nb][r], yv[nb][r]);
+      }
     }
   }
+}
+
+// y of the tail tiles: the ks slice partials of each element added in slice
+// order.  One thread per 4 consecutive columns of a tile row.
+__global__ __launch_bounds__(256) void gemm_tail_sum_kernel(const float* __restrict__ part, float* __restrict__ y,
+                                                            int M, int N, int MT, int NT, int tiles_main, int ks) {
+  constexpr int kQuads = kMxBM * kMxBN / 4;  // float4 per partial tile
+  const int idx = static_cast<int>(blockIdx.x) * 256 + static_cast<int>(threadIdx.x);
+  const int ti = idx / kQuads, e4 = idx - ti * kQuads;
+  const int r = e4 / (kMxBN / 4), c4 = e4 - r * (kMxBN / 4);
+  int m0, n0;
+  mx_tile_origin(tiles_main + ti, MT, NT, m0, n0);
+  const float4* p = reinterpret_cast<const float4*>(part) + static_cast<int64_t>(ti) * ks * kQuads + e4;
+  float4 a = p[0];
+  for (int sl = 1; sl < ks; ++sl) {
+    const float4 b = p[static_cast<int64_t>(sl) * kQuads];
+    a.x += b.x;
+    a.y += b.y;
+    a.z += b.z;
+    a.w += b.w;
+  }
+  const int m = m0 + r, n = n0 + 4 * c4;
+  if (m >= M) return;
+  float* const yr = y + static_cast<int64_t>(m) * N;
+  if (n < N) yr[n] = a.x;
+  if (n + 1 < N) yr[n + 1] = a.y;
+  if (n + 2 < N) yr[n + 2] = a.z;
+  if (n + 3 < N) yr[n + 3] = a.w;
 }
 
 static inline int prep_lds_bytes(int64_t G) { return static_cast<int>((kPrepPadded + G) * 4); }
@@ -669,7 +744,37 @@ static void gemm_prepare_launch(const void* x, int x_dtype, int64_t M, int64_t K
   }
 }
 
-static void gemm_run_launch(const void* workspace, int64_t M, int64_t K, const uint32_t* codes,
+static int gemm_device_cus() {
+  int dev = 0, cus = 256;
+  (void)hipGetDevice(&dev);
+  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  return cus;
+}
+
+// The tail split of one run: with one workgroup per CU, T output tiles take
+// ceil(T / CUs) rounds; when the last round is at most half full, its
+// T mod CUs tiles are cut into ks = CUs / (T mod CUs) slices of the groups
+// (at most kMxMaxSlices, at least 2 groups each), whose partial tiles follow
+// the prepared activation in the workspace.
+struct GemmSplit {
+  int64_t tiles_main, tiles_tail, ks, part_off, total;
+};
+static GemmSplit gemm_split_plan(int64_t M, int64_t K, int64_t N, int cus) {
+  const GemmWs lay = gemm_ws_layout(M, K);
+  const int64_t T = ((M + kMxBM - 1) / kMxBM) * ((N + kMxBN - 1) / kMxBN);
+  const int64_t rem = cus > 0 ? T % cus : 0;
+  const int64_t ks = rem > 0 ? std::min<int64_t>(cus / rem, kMxMaxSlices) : 0;
+  GemmSplit sp{T, 0, 1, lay.total, lay.total};
+  if (T > cus && rem > 0 && ks >= 2 && lay.G >= 2 * ks) {
+    sp.tiles_main = T - rem;
+    sp.tiles_tail = rem;
+    sp.ks = ks;
+    sp.total = sp.part_off + rem * ks * kMxBM * kMxBN * 4;
+  }
+  return sp;
+}
+
+static void gemm_run_launch(const void* workspace, size_t ws_bytes, int64_t M, int64_t K, const uint32_t* codes,
                             const uint16_t* scales, const uint16_t* biases, int64_t N, float* y, hipStream_t st) {
   const GemmWs lay = gemm_ws_layout(M, K);
   const char* ws = static_cast<const char*>(workspace);
@@ -678,11 +783,21 @@ static void gemm_run_launch(const void* workspace, int64_t M, int64_t K, const u
   const uint16_t* xl = reinterpret_cast<const uint16_t*>(ws + lay.xl_off);
   const float* p2 = reinterpret_cast<const float*>(ws + lay.p2_off);
   const int64_t MT = (M + kMxBM - 1) / kMxBM, NT = (N + kMxBN - 1) / kMxBN;
-  const int64_t per_xcd = (MT * NT + kXcds - 1) / kXcds;
-  hipLaunchKernelGGL(gemm_mx_kernel, dim3(static_cast<unsigned>(per_xcd * kXcds)), dim3(kMxThreads), 0,
-                     st, rec, xh, xl, p2, codes, scales, biases, y,
-                     static_cast<int>(M), static_cast<int>(N), static_cast<int>(lay.G), static_cast<int>(lay.Gp),
-                     static_cast<int>(MT), static_cast<int>(NT), static_cast<int>(per_xcd));
+  GemmSplit sp = gemm_split_plan(M, K, N, gemm_device_cus());
+  if (ws_bytes < static_cast<size_t>(sp.total)) sp = GemmSplit{MT * NT, 0, 1, lay.total, lay.total};
+  float* part = reinterpret_cast<float*>(const_cast<char*>(ws) + sp.part_off);
+  const int64_t per_xcd = (sp.tiles_main + kXcds - 1) / kXcds;
+  const int64_t grid = per_xcd * kXcds + sp.tiles_tail * sp.ks;
+  hipLaunchKernelGGL(gemm_mx_kernel, dim3(static_cast<unsigned>(grid)), dim3(kMxThreads), 0, st, rec, xh, xl, p2,
+                     codes, scales, biases, y, static_cast<int>(M), static_cast<int>(N), static_cast<int>(lay.G),
+                     static_cast<int>(lay.Gp), static_cast<int>(MT), static_cast<int>(NT), static_cast<int>(per_xcd),
+                     static_cast<int>(sp.tiles_main), static_cast<int>(sp.ks), part);
+  if (sp.tiles_tail > 0) {
+    const int64_t blocks = sp.tiles_tail * (kMxBM * kMxBN / 4) / 256;
+    hipLaunchKernelGGL(gemm_tail_sum_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, part, y,
+                       static_cast<int>(M), static_cast<int>(N), static_cast<int>(MT), static_cast<int>(NT),
+                       static_cast<int>(sp.tiles_main), static_cast<int>(sp.ks));
+  }
 }
 
 }  // namespace tb
@@ -692,6 +807,11 @@ using namespace tb;
 extern "C" size_t tb_ternary_gemm_workspace_size(int64_t M, int64_t K) {
   if (M <= 0 || K <= 0 || K % kGroup) return 0;
   return static_cast<size_t>(gemm_ws_layout(M, K).total);
+}
+
+extern "C" size_t tb_ternary_gemm_workspace_size_n(int64_t M, int64_t K, int64_t N) {
+  if (M <= 0 || K <= 0 || K % kGroup || N <= 0) return tb_ternary_gemm_workspace_size(M, K);
+  return static_cast<size_t>(gemm_split_plan(M, K, N, gemm_device_cus()).total);
 }
 
 extern "C" int tb_ternary_gemm_prepare(const void* x, int x_dtype, int64_t M, int64_t K, const int8_t* signs,
@@ -715,7 +835,7 @@ extern "C" int tb_ternary_gemm_run(const void* workspace, size_t ws_bytes, int64
   if (M == 0 || N == 0) return TB_OK;
   TB_TRY(gemm_run_checks(codes, scales, biases, y, who));
   TB_TRY(gemm_ws_check(workspace, ws_bytes, M, K, who));
-  gemm_run_launch(workspace, M, K, codes, scales, biases, N, y, static_cast<hipStream_t>(stream));
+  gemm_run_launch(workspace, ws_bytes, M, K, codes, scales, biases, N, y, static_cast<hipStream_t>(stream));
   TB_LAUNCH_CHECK(who);
   return TB_OK;
 }
@@ -733,7 +853,7 @@ extern "C" int tb_ternary_gemm(const void* x, int x_dtype, int64_t M, int64_t K,
   hipStream_t st = static_cast<hipStream_t>(stream);
   gemm_prepare_launch(x, x_dtype, M, K, signs, block, workspace, st);
   TB_LAUNCH_CHECK(who);
-  gemm_run_launch(workspace, M, K, codes, scales, biases, N, y, st);
+  gemm_run_launch(workspace, ws_bytes, M, K, codes, scales, biases, N, y, st);
   TB_LAUNCH_CHECK(who);
   return TB_OK;
 }

@@ -182,6 +182,17 @@ int tb_ternary_gemv_run(const void* workspace, size_t ws_bytes, int64_t B, int64
 /* Workspace bytes tb_ternary_gemm / _prepare / _run need for M rows of width K. */
 size_t tb_ternary_gemm_workspace_size(int64_t M, int64_t K);
 
+/* Workspace bytes for M x K activations against N output columns that let
+ * tb_ternary_gemm / _run balance the last round of output tiles: when the
+ * 64 x 512 tiles leave the last round of the GPU's compute units at most
+ * half full, those tiles are split into K slices whose partial tiles (fp32)
+ * follow the prepared activation in the workspace and are added in slice
+ * order by a second kernel (deterministic).  At least
+ * tb_ternary_gemm_workspace_size(M, K); a run with a workspace smaller than
+ * this value (but at least that size) computes every tile whole instead.
+ * Returns tb_ternary_gemm_workspace_size(M, K) for invalid N. */
+size_t tb_ternary_gemm_workspace_size_n(int64_t M, int64_t K, int64_t N);
+
 /* Packed linear for prefill (any M >= 1), same definition as the GEMV:
  *   y[m][n] = sum_k W~[n][k] (R x[m])[k]   (fp32 out, M x N)
  * Runs on the block-scaled fp6 x fp4 MFMA: the 2-bit codes are fp4 operands

@@ -123,6 +123,35 @@ def test_gemm_small_full(M, N, K, block, xd):
     compare(y.cpu().numpy(), want, f"gemm M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("M,N,K,block,xd", [
+    (1083, 8092, 2560, 512, "f32"),    # 272 tiles: 16 tail tiles x 8 slices of 2-3 groups, ragged M, N
+    (640, 13312, 2048, 1024, "bf16"),  # 260 tiles: 4 tail tiles x 8 slices of 2 groups
+])
+def test_gemm_tail_split_matches_oracle_and_whole_tiles(M, N, K, block, xd):
+    """More output tiles than one round of the chip with a short last round:
+    the tail tiles run as K slices whose partials a second kernel adds in
+    order.  Against the oracle, against a run whose workspace is too small
+    for the split (every tile whole), and bitwise against itself."""
+    announce(f"gemm tail split M={M} N={N} K={K} block={block} x={xd}")
+    T = torch()
+    p = synth.make_problem("gemm_split", N, K, M, [M, N, K, block, 13], xd, block)
+    codes, s, b = pack_to_device(p.t, p.scales)
+    x, sg = x_to_device(p), signs_to_device(p.signs)
+    need, base = tb.tb_ternary_gemm_workspace_size_n(M, K, N), tb.tb_ternary_gemm_workspace_size(M, K)
+    assert need > base
+    ws = T.empty(need, dtype=T.uint8, device="cuda")
+    y1 = tb.tb_ternary_gemm(x, sg, block, codes, s, b, workspace=ws)
+    y2 = tb.tb_ternary_gemm(x, sg, block, codes, s, b, workspace=ws)
+    yw = tb.tb_ternary_gemm(x, sg, block, codes, s, b, workspace=T.empty(base, dtype=T.uint8, device="cuda"))
+    T.cuda.synchronize()
+    assert T.equal(y1, y2)
+    d = (y1.double() - yw.double()).abs().max().item()
+    assert d <= 1e-5 * yw.abs().max().item(), d
+    oc, osc, ob = oracle_pack(p)
+    want = oracle.packed_linear(p.x64, p.signs, block, oc, osc, ob)
+    compare(y1.cpu().numpy(), want, f"gemm split M={M} N={N} K={K}")
+
+
 # --------------------------------------------------------------------------
 # exact decode, general affine decode, degenerate cases
 # --------------------------------------------------------------------------
