@@ -174,10 +174,45 @@ __global__ __launch_bounds__(kThreads) void gemm_prep_kernel(const void* __restr
 
   for (int c0 = 0; c0 < K; c0 += kPrepSuper) {
     const int n = min(kPrepSuper, K - c0);  // a multiple of 128 and of L
-    for (int i = tid; i < n; i += kThreads) {
-      float v = load_x<DT>(x, m * K + c0 + i);
-      if constexpr (L > 0) v *= static_cast<float>(signs[c0 + i]);
-      buf[lpad(i)] = v;
+    // 8 consecutive inputs and their signs per vector load; every load of a
+    // thread is issued before any of them is stored
+    constexpr int kVec = 8, kIters = kPrepSuper / kVec / kThreads;
+    static_assert(kPrepSuper % (kVec * kThreads) == 0, "prep pass tiling");
+    float xv[kIters][kVec];
+    uint2 sv[kIters];
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const int i = (tid + it * kThreads) * kVec;
+      sv[it] = make_uint2(0x01010101u, 0x01010101u);  // +1 bytes
+      if (i < n) {
+        const int64_t e = m * K + c0 + i;  // 8-element aligned: K is a multiple of 128
+        if constexpr (DT == TB_F32) {
+          const float4 a = reinterpret_cast<const float4*>(x)[e / 4];
+          const float4 b = reinterpret_cast<const float4*>(x)[e / 4 + 1];
+          xv[it][0] = a.x; xv[it][1] = a.y; xv[it][2] = a.z; xv[it][3] = a.w;
+          xv[it][4] = b.x; xv[it][5] = b.y; xv[it][6] = b.z; xv[it][7] = b.w;
+        } else {
+          const uint4 u = reinterpret_cast<const uint4*>(x)[e / 8];
+          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            xv[it][2 * q] = __uint_as_float(w[q] << 16);
+            xv[it][2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+          }
+        }
+        if constexpr (L > 0) sv[it] = reinterpret_cast<const uint2*>(signs + c0)[i / kVec];
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const int i = (tid + it * kThreads) * kVec;
+      if (i < n) {
+#pragma unroll
+        for (int q = 0; q < kVec; ++q) {
+          const uint32_t sb = ((q < 4 ? sv[it].x : sv[it].y) >> (8 * (q & 3))) & 0x80u;  // bit 7: -1
+          buf[lpad(i + q)] = __uint_as_float(__float_as_uint(xv[it][q]) ^ (sb << 24));
+        }
+      }
     }
     __syncthreads();
     if constexpr (L > 0) fwht_pad<L>(buf, n);
@@ -276,17 +311,16 @@ __device__ __forceinline__ v4i_rs rsrc_words(const void* base, int bytes) {
 // address lds + 16 l (4 l).  Written as assembly so that the stage ring's
 // waits are the kernel's own s_waitcnt vmcnt(n): the ring keeps one fill in
 // flight across the barrier, which the compiler's conservative LDS tracking
-// would otherwise drain.  M0 holds the LDS base; nothing else in these
-// kernels uses M0.
+// would otherwise drain.  M0 holds the LDS base (declared clobbered).
 __device__ __forceinline__ void dma16(v4i_rs r, uint32_t lds, int voff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff),
                "s"(r)
-               : "memory");
+               : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(v4i_rs r, uint32_t lds, int voff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds), "v"(voff),
                "s"(r)
-               : "memory");
+               : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(n) with the other counters left alone
@@ -684,6 +718,15 @@ static int gemm_ws_check(const void* workspace, size_t ws_bytes, int64_t M, int6
   return TB_OK;
 }
 
+// the prep kernel reads x and signs with 16- and 8-byte vector loads
+static int gemm_align_checks(const void* x, const int8_t* signs, const char* who) {
+  if (!aligned(x, 16) || (signs && !aligned(signs, 16))) {
+    set_error("%s: x and signs must be 16-byte aligned", who);
+    return TB_ERR_ALIGN;
+  }
+  return TB_OK;
+}
+
 static int gemm_shape_checks(int64_t M, int64_t K, int64_t N, const char* who) {
   if (M < 0 || N < 0) {
     set_error("%s: M and N must be >= 0", who);
@@ -821,6 +864,7 @@ extern "C" int tb_ternary_gemm_prepare(const void* x, int x_dtype, int64_t M, in
   TB_TRY(check_rotation(K, block, signs, who));
   if (M == 0) return TB_OK;
   TB_TRY(check_dtype(x_dtype, x, who));
+  TB_TRY(gemm_align_checks(x, signs, who));
   TB_TRY(gemm_ws_check(workspace, ws_bytes, M, K, who));
   gemm_prepare_launch(x, x_dtype, M, K, signs, block, workspace, static_cast<hipStream_t>(stream));
   TB_LAUNCH_CHECK(who);
@@ -848,6 +892,7 @@ extern "C" int tb_ternary_gemm(const void* x, int x_dtype, int64_t M, int64_t K,
   TB_TRY(check_rotation(K, block, signs, who));
   if (M == 0 || N == 0) return TB_OK;
   TB_TRY(check_dtype(x_dtype, x, who));
+  TB_TRY(gemm_align_checks(x, signs, who));
   TB_TRY(gemm_run_checks(codes, scales, biases, y, who));
   TB_TRY(gemm_ws_check(workspace, ws_bytes, M, K, who));
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -152,9 +152,27 @@ def _gemm(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(block=100), -3), (dict(K=1100), -2), (dict(M=-1), -1), (dict(dt=3), -7),
     (dict(wsb=8), -10), (dict(scales=DUMMY + 1), -8), (dict(signs=None), -1),
+    (dict(x=DUMMY + 4), -8),      # x needs 16-byte alignment (vector loads in the rotation)
+    (dict(signs=DUMMY + 8), -8),
 ])
 def test_gemm_rejects(kw, status):
     assert _gemm(**kw) == status
+
+
+def test_gemm_prepare_rejects_misaligned_inputs():
+    L = tb.lib()
+    for x, sg in ((DUMMY + 4, DUMMY), (DUMMY, DUMMY + 8)):
+        assert L.tb_ternary_gemm_prepare(x, tb.TB_BF16, 64, 1024, sg, 1024, DUMMY, 1 << 30, None) == -8
+
+
+def test_gemm_workspace_size_n():
+    L = tb.lib()
+    base = L.tb_ternary_gemm_workspace_size(2048, 5120)
+    assert base > 0 and L.tb_ternary_gemm_workspace_size(1, 100) == 0
+    # invalid N falls back to the base size; a valid one is never smaller
+    assert L.tb_ternary_gemm_workspace_size_n(2048, 5120, 0) == base
+    assert L.tb_ternary_gemm_workspace_size_n(2048, 5120, 17408) >= base
+    assert L.tb_ternary_gemm_workspace_size_n(64, 1024, 512) == L.tb_ternary_gemm_workspace_size(64, 1024)
 
 
 def test_gemm_empty_is_noop():
