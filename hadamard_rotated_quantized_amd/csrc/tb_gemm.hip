@@ -374,7 +374,7 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
     const uint8_t* __restrict__ rec, const uint16_t* __restrict__ xh, const uint16_t* __restrict__ xl,
     const float* __restrict__ p2, const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, float* __restrict__ y, int M, int N, int G, int Gp, int MT, int NT,
-    int per_xcd, int tiles_main, int ks, float* __restrict__ part) {
+    int per_xcd, int tiles_main, int ks, float* __restrict__ part, int bvec) {
   // XCD-aware tile order: workgroup w runs on XCD w % 8; XCD x owns the
   // contiguous range [x * per_xcd, (x + 1) * per_xcd) of the tile order, so
   // the workgroups an XCD runs at once (8 row tiles x 4 column tiles) share
@@ -597,27 +597,48 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
   v16f_g tb4[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) tb4[nb] = v16f_g{};
-  // (once per tile: tail slices other than the first skip it)
+  // (once per tile: tail slices other than the first skip it).  The loads
+  // of step s2 + 1 are issued before the MFMAs of step s2.  When G is a
+  // multiple of 8 and the biases are 16-byte aligned (bvec, from the host),
+  // the 8 biases an operand needs are one aligned 16-byte load (a block of 8
+  // groups lies wholly below G or wholly past it).
   const int nbias = gbeg == 0 ? Gp / 16 : 0;
-  for (int s2 = 0; s2 < nbias; ++s2) {
+  auto bias_loads = [&](int s2, v4u_g& ahv, v4u_g& alv, v4u_g* bq) {
     const int g0 = 16 * s2 + 8 * h;
     const int xo = ((wm * 32 + r32) * Gp + g0) * 2;
-    const v4u_g ahv = __builtin_amdgcn_raw_buffer_load_b128(rxh, xo, 0, 0);
-    const v4u_g alv = __builtin_amdgcn_raw_buffer_load_b128(rxl, xo, 0, 0);
+    ahv = __builtin_amdgcn_raw_buffer_load_b128(rxh, xo, 0, 0);
+    alv = __builtin_amdgcn_raw_buffer_load_b128(rxl, xo, 0, 0);
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int bo = (wn * 128 + 32 * nb + r32) * G;
-      uint32_t bw[4];
+      if (bvec) {
+        bq[nb] = __builtin_amdgcn_raw_buffer_load_b128(rb, g0 < G ? (bo + g0) * 2 : kOobOff, 0, 0);
+      } else {
+        uint32_t bw[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ga = g0 + 2 * i, gb = ga + 1;
-        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rb, ga < G ? (bo + ga) * 2 : kOobOff, 0, 0);
-        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rb, gb < G ? (bo + gb) * 2 : kOobOff, 0, 0);
-        bw[i] = lo | (hi << 16);
+        for (int i = 0; i < 4; ++i) {
+          const int ga = g0 + 2 * i, gb = ga + 1;
+          const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rb, ga < G ? (bo + ga) * 2 : kOobOff, 0, 0);
+          const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rb, gb < G ? (bo + gb) * 2 : kOobOff, 0, 0);
+          bw[i] = lo | (hi << 16);
+        }
+        bq[nb] = v4u_g{bw[0], bw[1], bw[2], bw[3]};
       }
-      const v8h_g bv = as_v8h(v4u_g{bw[0], bw[1], bw[2], bw[3]});
-      tb4[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_v8h(ahv), bv, tb4[nb], 0, 0, 0);
-      tb4[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_v8h(alv), bv, tb4[nb], 0, 0, 0);
+    }
+  };
+  v4u_g ahv, alv, bq[4];
+  if (nbias > 0) bias_loads(0, ahv, alv, bq);
+  for (int s2 = 0; s2 < nbias; ++s2) {
+    const v4u_g ah = ahv, al = alv;
+    v4u_g bc[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) bc[nb] = bq[nb];
+    if (s2 + 1 < nbias) bias_loads(s2 + 1, ahv, alv, bq);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const v8h_g bv = as_v8h(bc[nb]);
+      tb4[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_v8h(ah), bv, tb4[nb], 0, 0, 0);
+      tb4[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_v8h(al), bv, tb4[nb], 0, 0, 0);
     }
   }
   // D layout of a 32 x 32 block: lane l, register r holds row
@@ -834,7 +855,8 @@ static void gemm_run_launch(const void* workspace, size_t ws_bytes, int64_t M, i
   hipLaunchKernelGGL(gemm_mx_kernel, dim3(static_cast<unsigned>(grid)), dim3(kMxThreads), 0, st, rec, xh, xl, p2,
                      codes, scales, biases, y, static_cast<int>(M), static_cast<int>(N), static_cast<int>(lay.G),
                      static_cast<int>(lay.Gp), static_cast<int>(MT), static_cast<int>(NT), static_cast<int>(per_xcd),
-                     static_cast<int>(sp.tiles_main), static_cast<int>(sp.ks), part);
+                     static_cast<int>(sp.tiles_main), static_cast<int>(sp.ks), part,
+                     static_cast<int>(lay.G % 8 == 0 && aligned(biases, 16)));
   if (sp.tiles_tail > 0) {
     const int64_t blocks = sp.tiles_tail * (kMxBM * kMxBN / 4) / 256;
     hipLaunchKernelGGL(gemm_tail_sum_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, part, y,
