@@ -38,6 +38,7 @@
 #include <type_traits>
 
 #include "tb_device.h"
+#include "tb_xform.h"
 
 namespace tb {
 
@@ -271,6 +272,131 @@ __global__ __launch_bounds__(kThreads) void gemm_prep_kernel(const void* __restr
   const int t = mxx > 0.f ? __builtin_amdgcn_frexp_expf(mxx) - 15 : 0;
   for (int g = tid; g < Gp; g += kThreads) {
     const float xv = g < G ? ldexpf(xs[g], -t) : 0.f;
+    const uint16_t hb = half_bits(xv);
+    const float rem = xv - half_bits_to_float(hb);
+    xh[m * Gp + g] = hb;
+    xl[m * Gp + g] = half_bits(rem);
+  }
+  if (tid == 0) p2[m] = ldexpf(1.f, t);
+}
+
+// The same records from the matrix-core transform (blocks 0, 512, 1024): one
+// workgroup of min(chunks, 8) waves per activation row, wave w taking chunks
+// w, w + waves, ... of 1024 inputs (at most 128 VGPRs, so several rows share
+// a CU).  xform_rotate leaves lane l holding, in registers 4 Q + t,
+// inputs (l & 3) | t << 2 | ((l >> 2) & 7) << 4 | (l >> 5) << 7 | Q << 8 of
+// the chunk: for each Q a run of 32 inputs sits on 8 consecutive lanes (4
+// each), and lane bits b0 = l & 1, b1 = (l >> 1) & 1, b2 = (l >> 2) & 1 put
+// its 4 inputs at operand positions 16 b2 + 8 b0 + b1 + 2 t.  So the lane's
+// four 6-bit fields of a digit sit at bits 6 b1 + 12 t of the 48-bit window
+// starting at bit 96 b2 + 48 b0 of the digit's 24 bytes; lane pairs (b1 = 0,
+// 1) merge their fields and the b1 = 0 lane writes the window into the
+// wave's LDS copy of the chunk's 8 records (3200 contiguous bytes of the
+// workspace), which then goes out as full-wave 16-byte stores.
+template <int L, int DT>
+__global__ __launch_bounds__(512, 4) void gemm_prep_mfma_kernel(const void* __restrict__ x,
+                                                             const int8_t* __restrict__ signs, int K, int G, int Gp,
+                                                             uint8_t* __restrict__ rec, uint16_t* __restrict__ xh,
+                                                             uint16_t* __restrict__ xl, float* __restrict__ p2) {
+  extern __shared__ float2 prep_xs2[];  // (group sum, -) per group of the row's chunks
+  __shared__ float red[8];
+  __shared__ __attribute__((aligned(16))) uint8_t prep_stage[8][8 * kRecBytes];  // per wave: a chunk's records
+  constexpr int ESZ = DT == TB_F32 ? 4 : 2;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nthreads = static_cast<int>(blockDim.x), nwaves = nthreads >> 6;
+  const int64_t m = blockIdx.x;
+  const int nch = (K + 1023) >> 10;
+  const auto rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(static_cast<const char*>(x) + m * K * ESZ), 0, K * ESZ, kRsrcWord3);
+  const auto rsg = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(signs), 0, L > 0 ? K : 0, kRsrcWord3);
+  const v4u* cst = reinterpret_cast<const v4u*>(&kXformConst.w[xf_mode<L>()][0][lane][0]);
+  const v4u* cst2 = reinterpret_cast<const v4u*>(&kXformConst.w[xf_mode<L>()][1][lane][0]);
+  const v4u cf[2] = {cst[0], cst[1]};
+  const v4u cs[2] = {cst2[0], cst2[1]};
+  const float inv = inv_sqrt_block_or_one<L>();
+  const int b0 = lane & 1, b1 = (lane >> 1) & 1, b2 = (lane >> 2) & 1;
+  const int rr = (lane >> 3) & 3;  // run of the group
+  const int h = lane >> 5;
+  uint8_t* const stg = prep_stage[wave];
+  for (int c = wave; c < nch; c += nwaves) {
+    XformIn<DT> in;
+    xform_issue<L, DT>(rx, rsg, static_cast<int64_t>(c) * 1024, c * 1024, lane, in);
+    float v128;
+    const v16f U = xform_rotate<L, DT>(in, lane, cf, cs, v128);
+    xform_group_sums<L>(U, v128, 8 * c, lane, 0.f, prep_xs2);
+#pragma unroll
+    for (int Q = 0; Q < 4; ++Q) {
+      const int gk = 8 * c + h + 2 * Q;
+      float xr[4];
+      float mx = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        xr[t] = U[4 * Q + t] * inv;
+        mx = fmaxf(mx, fabsf(xr[t]));
+      }
+      mx = fmaxf(mx, xor_lane(mx, 0, lane));
+      mx = fmaxf(mx, xor_lane(mx, 1, lane));
+      mx = fmaxf(mx, xor_lane(mx, 2, lane));
+      int E = 0;
+      if (mx > 0.f) E = min(max(__builtin_amdgcn_frexp_expf(mx) - 16, -130), 112);
+      uint32_t q[4], sg[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        q[t] = min(static_cast<uint32_t>(rintf(ldexpf(fabsf(xr[t]), -E))), 65535u);
+        sg[t] = (__float_as_uint(xr[t]) >> 31) << 5;
+      }
+      uint8_t* const dst = stg + (h + 2 * Q) * kRecBytes;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint64_t w = 0;  // the lane's fields of digit j in the 48-bit window
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint64_t f = sg[t] | ((q[t] >> (4 * j)) & 15u);
+          w |= f << (12 * t + 6 * b1);
+        }
+        uint32_t lo = static_cast<uint32_t>(w), hi = static_cast<uint32_t>(w >> 32);
+        lo |= static_cast<uint32_t>(xor_lane_i(static_cast<int>(lo), 1, lane));
+        hi |= static_cast<uint32_t>(xor_lane_i(static_cast<int>(hi), 1, lane));
+        if (b1 == 0) {
+          uint8_t* d = dst + rr * kRunBytes + 24 * j + 12 * b2;
+          if (b0 == 0) {
+            *reinterpret_cast<uint32_t*>(d) = lo;
+            *reinterpret_cast<uint16_t*>(d + 4) = static_cast<uint16_t>(hi);
+          } else {
+            *reinterpret_cast<uint16_t*>(d + 6) = static_cast<uint16_t>(lo);
+            *reinterpret_cast<uint32_t*>(d + 8) = (lo >> 16) | (hi << 16);
+          }
+        }
+      }
+      if ((lane & 7) == 0) {
+        const uint32_t e0 = static_cast<uint32_t>(E + 130);
+        *reinterpret_cast<uint32_t*>(dst + kScaleOff + 4 * rr) = e0 | ((e0 + 4) << 8) | ((e0 + 8) << 16) | ((e0 + 12) << 24);
+      }
+    }
+    // the chunk's records (its groups below G) as 16-byte stores; a wave's
+    // LDS accesses complete in order, so the reads see the writes above
+    const int units = min(8, G - 8 * c) * (kRecBytes / 16);
+    v4u_g* const out = reinterpret_cast<v4u_g*>(rec + (m * G + 8 * c) * kRecBytes);
+#pragma unroll
+    for (int i = 0; i < (8 * kRecBytes / 16 + 63) / 64; ++i) {
+      const int u = 64 * i + lane;
+      if (u < units) out[u] = reinterpret_cast<const v4u_g*>(stg)[u];
+    }
+  }
+  __syncthreads();
+  // per-row power of two for the bias operand: max |X| * 2^-t in [2^14, 2^15)
+  float mxx = 0.f;
+  for (int g = tid; g < G; g += nthreads) mxx = fmaxf(mxx, fabsf(prep_xs2[g].x));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mxx = fmaxf(mxx, __shfl_xor(mxx, o));
+  if (lane == 0) red[wave] = mxx;
+  __syncthreads();
+  mxx = red[0];
+  for (int w = 1; w < nwaves; ++w) mxx = fmaxf(mxx, red[w]);
+  const int t = mxx > 0.f ? __builtin_amdgcn_frexp_expf(mxx) - 15 : 0;
+  for (int g = tid; g < Gp; g += nthreads) {
+    const float xv = g < G ? ldexpf(prep_xs2[g].x, -t) : 0.f;
     const uint16_t hb = half_bits(xv);
     const float rem = xv - half_bits_to_float(hb);
     xh[m * Gp + g] = hb;
@@ -718,6 +844,17 @@ static void launch_gemm_prep(const void* x, int dt, const int8_t* signs, int64_t
   uint16_t* xh = reinterpret_cast<uint16_t*>(ws + lay.xh_off);
   uint16_t* xl = reinterpret_cast<uint16_t*>(ws + lay.xl_off);
   float* p2 = reinterpret_cast<float*>(ws + lay.p2_off);
+  if constexpr (L <= 1024) {
+    // blocks 0 / 512 / 1024: the matrix-core transform, one wave per chunk
+    const int lds_m = static_cast<int>((K + 1023) / 1024 * 8 * sizeof(float2));
+    auto km = dt == TB_F32 ? gemm_prep_mfma_kernel<L, TB_F32> : gemm_prep_mfma_kernel<L, TB_BF16>;
+    if (lds_m > 64 * 1024)
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(km), hipFuncAttributeMaxDynamicSharedMemorySize, lds_m);
+    const int waves = static_cast<int>(std::min<int64_t>((K + 1023) / 1024, 8));
+    hipLaunchKernelGGL(km, dim3(static_cast<unsigned>(M)), dim3(64 * waves), static_cast<size_t>(lds_m), st, x, signs,
+                       static_cast<int>(K), static_cast<int>(lay.G), static_cast<int>(lay.Gp), rec, xh, xl, p2);
+    return;
+  }
   const int lds = prep_lds_bytes(lay.G);
   auto kern = dt == TB_F32 ? gemm_prep_kernel<L, TB_F32> : gemm_prep_kernel<L, TB_BF16>;
   if (lds > 64 * 1024)

@@ -152,6 +152,29 @@ def test_gemm_tail_split_matches_oracle_and_whole_tiles(M, N, K, block, xd):
     compare(y1.cpu().numpy(), want, f"gemm split M={M} N={N} K={K}")
 
 
+def test_gemm_biases_not_16_byte_aligned():
+    """The epilogue reads the biases as 16-byte vectors only when they are
+    16-byte aligned; a pack whose biases start 4 elements into a buffer takes
+    the 2-byte loads and must give the same result."""
+    announce("gemm M=96 N=600 K=1024 with biases at a 8-byte offset")
+    T = torch()
+    M, N, K = 96, 600, 1024
+    p = synth.make_problem("gemm_unaligned", N, K, M, [M, N, K, 21], "bf16", 1024)
+    codes, s, b = pack_to_device(p.t, p.scales)
+    x, sg = x_to_device(p), signs_to_device(p.signs)
+    buf = T.empty(b.numel() + 4, dtype=b.dtype, device="cuda")
+    b_off = buf[4:].view(b.shape)
+    b_off.copy_(b)
+    assert b_off.data_ptr() % 16 == 8
+    y_al = tb.tb_ternary_gemm(x, sg, 1024, codes, s, b)
+    y_un = tb.tb_ternary_gemm(x, sg, 1024, codes, s, b_off)
+    T.cuda.synchronize()
+    assert T.equal(y_al, y_un)
+    oc, osc, ob = oracle_pack(p)
+    want = oracle.packed_linear(p.x64, p.signs, 1024, oc, osc, ob)
+    compare(y_un.cpu().numpy(), want, "gemm unaligned biases")
+
+
 # --------------------------------------------------------------------------
 # exact decode, general affine decode, degenerate cases
 # --------------------------------------------------------------------------
