@@ -53,7 +53,8 @@ COUNTER_SUMMARIES = {
                [os.path.join(_CSRC, f) for f in ("tb_gemv_band.hip", "tb_xform.h", "tb_gemv.h", "tb_device.h",
                                                   "tb_common.h")] + [_BUILD]),
     "prefill_gate_up": (os.path.join(ROOT, "profiles", "gemm_mx_kernel_prefill_gate_up_counters.txt"),
-                        [os.path.join(_CSRC, f) for f in ("tb_gemm.hip", "tb_device.h", "tb_common.h")] + [_BUILD]),
+                        [os.path.join(_CSRC, f) for f in ("tb_gemm.hip", "tb_xform.h", "tb_gemv.h", "tb_device.h",
+                                                           "tb_common.h")] + [_BUILD]),
 }
 
 

@@ -12,8 +12,10 @@
 //    field is the e2m1 number c / 2, so (w & 0x33333333) and
 //    ((w >> 2) & 0x33333333) are two fp4 operand dwords holding the 16 codes
 //    of a word; the B block scale 2^1 restores c.
-//  * gemm_prep_kernel rotates each row once per call and writes it as four
-//    signed base-16 digits per input.  For each run of 32 consecutive inputs
+//  * The prep kernel (gemm_prep_mfma_kernel on the matrix cores for blocks
+//    0 / 512 / 1024, gemm_prep_kernel with LDS butterflies for 2048 / 4096)
+//    rotates each row once per call and writes it as four signed base-16
+//    digits per input.  For each run of 32 consecutive inputs
 //    of a row, a power-of-two exponent E makes q = round(|xr| 2^-E) a 16-bit
 //    integer (the run's largest |xr| maps into [2^15, 2^16)); digit j is
 //    (q >> 4j) & 15 with the sign of xr, stored as the e2m3 number digit / 8
