@@ -329,7 +329,6 @@ __global__ __launch_bounds__(512, 4) void gemm_prep_mfma_kernel(const void* __re
     xform_group_sums<L>(U, v128, 8 * c, lane, 0.f, prep_xs2);
 #pragma unroll
     for (int Q = 0; Q < 4; ++Q) {
-      const int gk = 8 * c + h + 2 * Q;
       float xr[4];
       float mx = 0.f;
 #pragma unroll
@@ -439,16 +438,17 @@ __device__ __forceinline__ v4i_rs rsrc_words(const void* base, int bytes) {
 // address lds + 16 l (4 l).  Written as assembly so that the stage ring's
 // waits are the kernel's own s_waitcnt vmcnt(n): the ring keeps one fill in
 // flight across the barrier, which the compiler's conservative LDS tracking
-// would otherwise drain.  M0 holds the LDS base (declared clobbered).
+// would otherwise drain.  M0 holds the LDS base; the compiler reserves M0
+// and nothing else in these kernels uses it.
 __device__ __forceinline__ void dma16(v4i_rs r, uint32_t lds, int voff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff),
                "s"(r)
-               : "memory", "m0");
+               : "memory");
 }
 __device__ __forceinline__ void dma4(v4i_rs r, uint32_t lds, int voff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds), "v"(voff),
                "s"(r)
-               : "memory", "m0");
+               : "memory");
 }
 
 // s_waitcnt vmcnt(n) with the other counters left alone
