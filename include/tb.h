@@ -129,7 +129,10 @@ int tb_pack_device(const int8_t* t, const uint16_t* scales, int64_t N, int64_t K
  *   inverse = 1:  y = signs .* (H x) / sqrt(block)      (inverse)
  * x: rows x K of x_dtype (TB_F32 or TB_BF16), row-major; y: rows x K fp32.
  * y may alias x when x is fp32.  block in {512,1024,2048,4096}, K % block == 0.
- * x and y 4-byte aligned (x 2-byte for bf16). */
+ * x and y 4-byte aligned (x 2-byte for bf16).
+ * Applied forward to the rows of a dense N x K weight matrix W it performs
+ * the offline fold W R^T [P2 "ternary weights + folded Hadamard rotation"]:
+ * row n of W R^T is the forward transform of row n of W. */
 int tb_fwht_signed(const void* x, int x_dtype, float* y, const int8_t* signs,
                    int64_t rows, int64_t K, int block, int inverse, void* stream);
 

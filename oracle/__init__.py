@@ -30,6 +30,7 @@ from .reference import (  # noqa: F401
     packed_linear,
     packed_linear_rows,
     embed_inverse,
+    fold_rotation,
     container_bytes,
     bf16_bits_to_f64,
     f16_to_f64,

@@ -300,3 +300,21 @@ def embed_inverse(ids, codes, scales, biases, signs, block: int) -> np.ndarray:
         else:
             out[ok] = fwht_signed(rows, signs, block, inverse=True)
     return out
+
+
+# --------------------------------------------------------------------------
+# the offline fold
+# --------------------------------------------------------------------------
+def fold_rotation(w, signs, block: int) -> np.ndarray:
+    """Fold the rotation into a dense weight matrix: W_s = W R^T, fp64.
+
+    [P2 "ternary weights + folded Hadamard rotation"] each matrix is rotated
+    block by block before it is quantized, and the stored weights already sit
+    in the rotated basis, so that W x = (W R^T)(R x) with R x the activation
+    transform of the Packed linear.  With R = blockdiag(H) diag(sigma) and H
+    symmetric, row n of W R^T is (R w_n)^T, i.e. the forward signed transform
+    of that row.  The ternarization of W_s that follows is not given by the
+    pages and is not part of this function.
+    """
+    w = np.atleast_2d(np.asarray(w, dtype=np.float64))
+    return fwht_signed(w, signs, block)

@@ -274,6 +274,23 @@ def pin_folded_rotation_bruteforce(o):
                                    rtol=0, atol=1e-14 * scale)
 
 
+def pin_fold_bruteforce(o):
+    """The offline fold W_s = W R^T against a dense R built from scipy's
+    Hadamard matrix, and the identity it exists for: W x == W_s (R x), with a
+    dense fp64 W, blocks 512 and 1024, distinct signs per block."""
+    rng = _rng(27)
+    for N, K, L in ((40, 2048, 1024), (9, 1536, 512)):
+        W = rng.standard_normal((N, K))
+        sig = np.where(rng.random(K) < 0.5, -1, 1).astype(np.int8)
+        x = rng.standard_normal((2, K))
+        Ws = o.fold_rotation(W, sig, L)
+        R = _dense_rotation(sig, L)
+        np.testing.assert_allclose(Ws, W @ R.T, rtol=0, atol=1e-13 * np.abs(W).max())
+        xr = o.fwht_signed(x, sig, L)
+        want = x @ W.T
+        np.testing.assert_allclose(xr @ Ws.T, want, rtol=0, atol=1e-12 * np.abs(want).max())
+
+
 def pin_unrotated_is_plain_matmul(o):
     """block = 0: y = x @ (s*t)^T, brute force."""
     rng = _rng(21)

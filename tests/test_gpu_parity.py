@@ -329,6 +329,39 @@ def test_fwht_matches_oracle_and_inverts(block):
     assert T.equal(xb, y)
 
 
+@pytest.mark.parametrize("block", [512, 1024])
+def test_offline_fold_on_device_recovers_packed_weights(block):
+    """The offline fold W_s = W R^T is the forward signed transform of each
+    weight row, so tb_fwht_signed over the rows of a dense W performs it.
+    W is built on the host as W~ R from packed ternary weights W~; the device
+    fold must give back W~ (and its ternary codes), and the Packed linear on
+    W~ must equal the unrotated product W x."""
+    announce(f"offline fold block={block}")
+    T = torch()
+    rng = np.random.default_rng(31 + block)
+    N, K = 96, 3 * block * (2 if block == 512 else 1)
+    t = synth.draw_ternary(rng, N, K)
+    sc = synth.draw_scales(rng, N, K)
+    sig = synth.draw_signs(rng, K)
+    oc, osc, ob = oracle.pack(t, sc)
+    w_packed = oracle.dequantize(oc, osc, ob, K)
+    W = oracle.fwht_signed(w_packed, sig, block, inverse=True)  # W~ R, row by row
+    sd = signs_to_device(sig)
+    Wd = T.from_numpy(W.astype(np.float32)).cuda()
+    Ws = tb.tb_fwht_signed(Wd, sd, block)
+    T.cuda.synchronize()
+    got = Ws.cpu().numpy().astype(np.float64)
+    compare(got, oracle.fold_rotation(W.astype(np.float32), sig, block), "fold vs oracle")
+    g = np.arange(K) // 128
+    s64 = sc.astype(np.float64)[:, g]
+    assert np.array_equal(np.rint(got / s64).astype(np.int8), t)
+    x64, x = synth.draw_activations(rng, 2, K, "f32")
+    codes, s, b = pack_to_device(t, sc)
+    y = tb.tb_ternary_gemv(T.from_numpy(np.ascontiguousarray(x)).cuda(), sd, block, codes, s, b)
+    T.cuda.synchronize()
+    compare(y.cpu().numpy(), x64 @ W.T, "Packed linear vs unrotated product")
+
+
 def test_fwht_bf16_input():
     announce("fwht bf16")
     T = torch()

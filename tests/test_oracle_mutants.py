@@ -13,6 +13,8 @@ SRC_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__
                         "oracle", "reference.py")
 
 MUTANTS = {
+    "fold_uses_inverse": ("return fwht_signed(w, signs, block)",
+                          "return fwht_signed(w, signs, block, inverse=True)"),
     "no_normalization": ("return a.reshape(*lead, K) / math.sqrt(block)",
                          "return a.reshape(*lead, K)"),
     "butterfly_swapped_halves": ("a = np.stack((lo + hi, lo - hi), axis=3)",
