@@ -545,6 +545,35 @@ def test_gemv_wide_layer_sampled_rows(N, B):
     compare(y.cpu().numpy()[:, rows], want, f"wide N={N} B={B}")
 
 
+def test_maximum_size_lm_head_and_embedding_table():
+    """The largest module: the lm_head / embedding table of V = 248,320 rows
+    of K = 5120 (1.27 G weights, 357.6 MB packed), drawn and packed on the
+    device.  The GEMV is checked on sampled rows (first and last rows and tile
+    edges included), the embedding on ids 0, V - 1 and one drawn id."""
+    V, K = synth.VOCAB, 5120
+    announce(f"maximum size: lm_head GEMV N={V} K={K} and embedding rows")
+    T = torch()
+    dev = T.device("cuda")
+    t, sc, x = synth.device_module_draw(4242, V, K, 1, dev)
+    codes, s, b = tb.tb_pack_device(t, sc)
+    sig = synth.sweep_signs()[K]
+    sd = signs_to_device(sig)
+    y = tb.tb_ternary_gemv(x, sd, 1024, codes, s, b)
+    rng = np.random.default_rng(4242)
+    ids = np.array([0, V - 1, int(rng.integers(0, V))], np.int32)
+    out = tb.tb_embed_inverse(T.from_numpy(ids).to(dev), codes, s, b, sd, 1024)
+    T.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, 15, 16, V // 2, V - 17, V - 16, V - 1],
+                                     rng.integers(0, V, 1000)]))
+    rt = T.from_numpy(rows).to(dev)
+    oc, osc, ob = oracle.pack(t[rt].cpu().numpy(), sc[rt].cpu().numpy())
+    want = oracle.packed_linear(x.float().cpu().numpy().astype(np.float64), sig, 1024, oc, osc, ob)
+    compare(y[:, rt].cpu().numpy(), want, "lm_head sampled rows")
+    it = T.from_numpy(ids.astype(np.int64)).to(dev)
+    ec, es, eb = oracle.pack(t[it].cpu().numpy(), sc[it].cpu().numpy())
+    compare(out.cpu().numpy(), oracle.embed_inverse(np.arange(3), ec, es, eb, sig, 1024), "embedding edge ids")
+
+
 def test_gemv_one_call_graph_replays_match_eager():
     """The single-launch call captured in a HIP graph: every replay, with
     eager work in between, equals the eager result bitwise."""
