@@ -389,7 +389,7 @@ extern "C" int tb_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int
     return TB_ERR_ARG;
   }
   int max_nch = 1;
-  int64_t tiles = 0, ws = 0, cost = 0;
+  int64_t tiles = 0, ws = 0;
   for (int64_t i = 0; i < count; ++i) {
     const tb_gemv_module& m = mods[i];
     if (m.N < 0 || m.K <= 0) {
@@ -421,7 +421,6 @@ extern "C" int tb_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int
     max_nch = std::max(max_nch, nch);
     tiles += (m.N + 15) / 16;
     ws += static_cast<int64_t>(nch) * (kMultiImgChunk + 64);
-    cost += (m.N + 15) / 16 * (m.K / 128 + 2);
   }
   if (multi_lds_total(max_nch) > kMultiLdsMax) {
     set_error("%s: K up to %d takes too much LDS for the stream kernel", who, max_nch * 1024);
