@@ -50,7 +50,7 @@ constexpr int kMultiRing = 4;                       // span pairs in flight per 
 constexpr int kMultiYbuf = 32;                      // finished tiles a wave holds in LDS before writing them
 constexpr int64_t kMultiLdsMax = 150 * 1024;
 constexpr int kMultiWsHead = 256;                   // workspace bytes before the first image: the piece counter
-constexpr int kMultiPieceFloor = 16;                // smallest piece: 1 / 16 of a workgroup's mean share
+constexpr int kMultiPieceFloor = 64;                // smallest piece: 1 / 64 of a workgroup's mean share
 
 struct MultiHeader {  // 64 bytes
   int32_t magic, count, tasks, grid;

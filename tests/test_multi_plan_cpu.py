@@ -73,10 +73,10 @@ def test_plan_tasks_and_pieces_partition_tiles():
     for m, a, b, _ in pc:
         assert tile0[m] <= a < b <= tile0[m] + tiles[m]
     # sizes: about 1/grid of the cost still left, never below the floor
-    # (1/16 of a workgroup's mean share) unless a module ends first
+    # (1/64 of a workgroup's mean share) unless a module ends first
     cost_tile = np.concatenate([np.full(t, K // 128 + 2) for t, (N, K) in zip(tiles, SWEEPLIKE)])
     cum = np.concatenate([[0], np.cumsum(cost_tile)])
-    floor = max(1, cum[-1] // (p["grid"] * 16))
+    floor = max(1, cum[-1] // (p["grid"] * 64))
     for m, a, b, _ in pc:
         left = cum[-1] - cum[a]
         want = max(floor, left // p["grid"])
