@@ -101,7 +101,10 @@ def tb_pack(t: np.ndarray, scales: np.ndarray):
     sc = np.ascontiguousarray(scales)
     if sc.dtype == np.float16:
         sc = sc.view(np.uint16)
+    if t.ndim != 2:
+        raise ValueError(f"t must be 2-D (N, K), got shape {t.shape}")
     N, K = t.shape
+    _check_width(K)
     if sc.shape != (N, K // 128) or sc.dtype != np.uint16:
         raise ValueError("scales must be float16 (N, K/128)")
     codes = np.empty((N, K // 16), np.uint32)
@@ -114,6 +117,9 @@ def tb_pack(t: np.ndarray, scales: np.ndarray):
 
 def tb_unpack(codes: np.ndarray, K: int) -> np.ndarray:
     codes = np.ascontiguousarray(codes, dtype=np.uint32)
+    _check_width(K)
+    if codes.ndim != 2 or codes.shape[1] != K // 16:
+        raise ValueError(f"codes has shape {codes.shape}, expected (N, {K // 16})")
     N = codes.shape[0]
     out = np.empty((N, K), np.int8)
     _check(lib().tb_unpack(codes.ctypes.data, N, K, out.ctypes.data))
@@ -165,9 +171,11 @@ def tb_pack_device(t, scales, check: bool = True):
     """Pack on the device.  t int8 (N, K), scales float16 (N, K/128), both on
     the GPU.  With check=True, synchronizes and raises on invalid values."""
     torch = _torch()
+    N, K = _rows(t, "t")
+    _check_width(K)
+    _shape(scales, (N, K // 128), "scales")
     _dev(t, "t", torch.int8)
     _dev(scales, "scales", torch.float16)
-    N, K = t.shape
     codes = torch.empty((N, K // 16), dtype=torch.int32, device=t.device)
     so = torch.empty_like(scales)
     bo = torch.empty_like(scales)
@@ -181,9 +189,12 @@ def tb_pack_device(t, scales, check: bool = True):
 
 def tb_fwht_signed(x, signs, block: int, inverse: bool = False, out=None):
     torch = _torch()
+    rows, K = _rows(x)
+    _shape(signs, (K,), "signs")
+    if out is not None:
+        _shape(out, (rows, K), "out")
     _dev(x, "x")
     _dev(signs, "signs", torch.int8)
-    rows, K = x.shape
     if out is None:
         out = torch.empty((rows, K), dtype=torch.float32, device=x.device)
     _dev(out, "out", torch.float32)
@@ -208,6 +219,46 @@ def tb_ternary_gemm_workspace_size_n(M: int, K: int, N: int) -> int:
     return int(lib().tb_ternary_gemm_workspace_size_n(M, K, N))
 
 
+def _shape(t, shape, name):
+    """Raise ValueError unless tensor t has exactly this shape.  Checked
+    before any pointer reaches the library: the C ABI receives only pointers
+    and the sizes claimed here, so a mismatched tensor would be read past its
+    end on the device."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check_width(K, name="K"):
+    if K <= 0 or K % 128:
+        raise ValueError(f"{name}={K} must be a positive multiple of 128")
+
+
+def _container_shapes(codes, scales, biases, N, K):
+    """codes (N, K/16) words, scales and biases (N, K/128)."""
+    _check_width(K)
+    _shape(codes, (N, K // 16), "codes")
+    _shape(scales, (N, K // 128), "scales")
+    _shape(biases, (N, K // 128), "biases")
+
+
+def _signs_shape(signs, K, block):
+    if block == 0:
+        if signs is not None:
+            raise ValueError("block 0 (no rotation) takes no sign vector")
+        return
+    if signs is None:
+        raise ValueError(f"block {block} needs a sign vector of {K} elements")
+    _shape(signs, (K,), "signs")
+
+
+def _rows(x, name="x"):
+    if x.dim() != 2:
+        raise ValueError(f"{name} must be 2-D (rows, K), got shape {tuple(x.shape)}")
+    return int(x.shape[0]), int(x.shape[1])
+
+
 def _container(codes, scales, biases):
     torch = _torch()
     _dev(codes, "codes")
@@ -220,12 +271,16 @@ def _container(codes, scales, biases):
 def tb_ternary_gemv(x, signs, block: int, codes, scales, biases, out=None, workspace=None):
     """y (B, N) float32 = Packed linear of x (B, K) for B <= 8."""
     torch = _torch()
+    B, K = _rows(x)
+    N = int(codes.shape[0])
+    _container_shapes(codes, scales, biases, N, K)
+    _signs_shape(signs, K, block)
+    if out is not None:
+        _shape(out, (B, N), "out")
     _dev(x, "x")
     _container(codes, scales, biases)
     if signs is not None:
         _dev(signs, "signs", torch.int8)
-    B, K = x.shape
-    N = codes.shape[0]
     if out is None:
         out = torch.empty((B, N), dtype=torch.float32, device=x.device)
     _dev(out, "out", torch.float32)
@@ -242,10 +297,12 @@ def tb_ternary_gemv_prepare(x, signs, block: int, workspace=None):
     """Rotate and split x (B, K) into a workspace (uint8 tensor) for
     tb_ternary_gemv_run; returns the workspace."""
     torch = _torch()
+    B, K = _rows(x)
+    _check_width(K)
+    _signs_shape(signs, K, block)
     _dev(x, "x")
     if signs is not None:
         _dev(signs, "signs", torch.int8)
-    B, K = x.shape
     need = tb_ternary_gemv_workspace_size(B, K)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
@@ -256,9 +313,12 @@ def tb_ternary_gemv_prepare(x, signs, block: int, workspace=None):
 
 def tb_ternary_gemv_run(workspace, B: int, K: int, codes, scales, biases, out=None):
     torch = _torch()
+    N = int(codes.shape[0])
+    _container_shapes(codes, scales, biases, N, K)
+    if out is not None:
+        _shape(out, (B, N), "out")
     _dev(workspace, "workspace", torch.uint8)
     _container(codes, scales, biases)
-    N = codes.shape[0]
     if out is None:
         out = torch.empty((B, N), dtype=torch.float32, device=workspace.device)
     _dev(out, "out", torch.float32)
@@ -271,10 +331,12 @@ def tb_ternary_gemm_prepare(x, signs, block: int, workspace=None, N: int | None 
     """Rotate x (M, K) into a new (or the given) workspace; with N, the new
     workspace is sized for runs against N output columns (tail split)."""
     torch = _torch()
+    M, K = _rows(x)
+    _check_width(K)
+    _signs_shape(signs, K, block)
     _dev(x, "x")
     if signs is not None:
         _dev(signs, "signs", torch.int8)
-    M, K = x.shape
     need = tb_ternary_gemm_workspace_size(M, K) if N is None else tb_ternary_gemm_workspace_size_n(M, K, N)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
@@ -285,9 +347,12 @@ def tb_ternary_gemm_prepare(x, signs, block: int, workspace=None, N: int | None 
 
 def tb_ternary_gemm_run(workspace, M: int, K: int, codes, scales, biases, out=None):
     torch = _torch()
+    N = int(codes.shape[0])
+    _container_shapes(codes, scales, biases, N, K)
+    if out is not None:
+        _shape(out, (M, N), "out")
     _dev(workspace, "workspace", torch.uint8)
     _container(codes, scales, biases)
-    N = codes.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=workspace.device)
     _dev(out, "out", torch.float32)
@@ -300,12 +365,16 @@ def tb_ternary_gemm(x, signs, block: int, codes, scales, biases, out=None, works
     """y (M, N) float32 = Packed linear of x (M, K), block-scaled fp6 x fp4
     MFMA path."""
     torch = _torch()
+    M, K = _rows(x)
+    N = int(codes.shape[0])
+    _container_shapes(codes, scales, biases, N, K)
+    _signs_shape(signs, K, block)
+    if out is not None:
+        _shape(out, (M, N), "out")
     _dev(x, "x")
     _container(codes, scales, biases)
     if signs is not None:
         _dev(signs, "signs", torch.int8)
-    M, K = x.shape
-    N = codes.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
     _dev(out, "out", torch.float32)
@@ -321,13 +390,19 @@ def tb_ternary_gemm(x, signs, block: int, codes, scales, biases, out=None, works
 def tb_embed_inverse(ids, codes, scales, biases, signs, block: int, out=None):
     """(T, K) float32 rows: inverse-transformed dequantized table rows."""
     torch = _torch()
+    if ids.dim() != 1:
+        raise ValueError(f"ids must be 1-D, got shape {tuple(ids.shape)}")
+    T = int(ids.numel())
+    V = int(codes.shape[0])
+    K = int(codes.shape[1]) * 16 if codes.dim() == 2 else 0
+    _container_shapes(codes, scales, biases, V, K)
+    _signs_shape(signs, K, block)
+    if out is not None:
+        _shape(out, (T, K), "out")
     _dev(ids, "ids", torch.int32)
     _container(codes, scales, biases)
     if signs is not None:
         _dev(signs, "signs", torch.int8)
-    T = ids.numel()
-    V = codes.shape[0]
-    K = codes.shape[1] * 16
     if out is None:
         out = torch.empty((T, K), dtype=torch.float32, device=ids.device)
     _dev(out, "out", torch.float32)
@@ -348,13 +423,19 @@ def tb_gemv_multi_plan(modules, block: int, x_dtype: int = TB_BF16):
     torch = _torch()
     arr = (TbGemvModule * len(modules))()
     for i, (x, signs, codes, scales, biases, y) in enumerate(modules):
+        if x.dim() not in (1, 2) or (x.dim() == 2 and x.shape[0] != 1):
+            raise ValueError(f"module {i}: x must be (K,) or (1, K), got {tuple(x.shape)}")
+        K = int(x.shape[-1])
+        N = int(codes.shape[0])
+        _container_shapes(codes, scales, biases, N, K)
+        _signs_shape(signs, K, block)
+        if y.numel() != N or y.dim() not in (1, 2):
+            raise ValueError(f"module {i}: y must hold N={N} outputs, got shape {tuple(y.shape)}")
         _dev(x, "x")
         _container(codes, scales, biases)
         _dev(y, "y", torch.float32)
         if signs is not None:
             _dev(signs, "signs", torch.int8)
-        K = x.shape[-1]
-        N = codes.shape[0]
         arr[i] = TbGemvModule(x.data_ptr(), _ptr(signs), codes.data_ptr(), scales.data_ptr(), biases.data_ptr(),
                               y.data_ptr(), N, K)
     size = int(lib().tb_gemv_multi_plan_size(arr, len(modules)))

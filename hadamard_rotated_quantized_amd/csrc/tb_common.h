@@ -28,9 +28,12 @@ inline bool block_known(int block) {
 // Returns TB_OK or an error (message set).
 int check_rotation(int64_t K, int block, const int8_t* signs, const char* who);
 
-// Shared validation of a (codes, scales, biases) container of N rows, width K.
+// Shared validation of a (codes, scales, biases) container of N rows, width K:
+// non-NULL, codes 16-byte aligned, scales and biases aligned to sb_align bytes
+// (2 = their element size; the decode-matmul kernels load them as dwords and
+// larger vectors and ask for 4).
 int check_container(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
-                    const char* who);
+                    const char* who, int sb_align = 2);
 
 int check_dtype(int x_dtype, const void* x, const char* who);
 

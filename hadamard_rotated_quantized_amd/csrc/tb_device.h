@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "tb_common.h"
 
 namespace tb {
@@ -83,6 +85,38 @@ __device__ __forceinline__ float inv_sqrt_block() {
   else if constexpr (L == 4096) return 0.015625f;
   else if constexpr (L == 512) return 0.04419417382415922f;
   else return 0.02209708691207961f;  // 2048
+}
+
+
+// ---------------------------------------------------------------------------
+// host helpers shared by the launchers
+// ---------------------------------------------------------------------------
+// Compute units of the current device, queried once per device and cached
+// (256, the MI355X count, when the runtime cannot say).  Thread-safe.
+inline int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  std::atomic<int>& c = cache[dev & 63];
+  int v = c.load(std::memory_order_relaxed);
+  if (v <= 0) {
+    v = 256;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    c.store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// Raise a kernel's dynamic LDS limit to `bytes` once per device.  `done`
+// is the kernel's own bit mask of devices already set; two threads racing
+// both make the same idempotent call.
+inline void lds_limit_once(const void* kernel, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  const uint64_t bit = uint64_t(1) << (dev & 63);
+  if (done.load(std::memory_order_acquire) & bit) return;
+  (void)hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  done.fetch_or(bit, std::memory_order_release);
 }
 
 }  // namespace tb

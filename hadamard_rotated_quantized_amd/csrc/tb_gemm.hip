@@ -947,13 +947,6 @@ static void gemm_prepare_launch(const void* x, int x_dtype, int64_t M, int64_t K
   }
 }
 
-static int gemm_device_cus() {
-  int dev = 0, cus = 256;
-  (void)hipGetDevice(&dev);
-  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  return cus;
-}
-
 // The tail split of one run: with one workgroup per CU, T output tiles take
 // ceil(T / CUs) rounds; when the last round is at most half full, its
 // T mod CUs tiles are cut into ks = CUs / (T mod CUs) slices of the groups
@@ -986,7 +979,7 @@ static void gemm_run_launch(const void* workspace, size_t ws_bytes, int64_t M, i
   const uint16_t* xl = reinterpret_cast<const uint16_t*>(ws + lay.xl_off);
   const float* p2 = reinterpret_cast<const float*>(ws + lay.p2_off);
   const int64_t MT = (M + kMxBM - 1) / kMxBM, NT = (N + kMxBN - 1) / kMxBN;
-  GemmSplit sp = gemm_split_plan(M, K, N, gemm_device_cus());
+  GemmSplit sp = gemm_split_plan(M, K, N, device_cus());
   if (ws_bytes < static_cast<size_t>(sp.total)) sp = GemmSplit{MT * NT, 0, 1, lay.total, lay.total};
   float* part = reinterpret_cast<float*>(const_cast<char*>(ws) + sp.part_off);
   const int64_t per_xcd = (sp.tiles_main + kXcds - 1) / kXcds;
@@ -1015,7 +1008,7 @@ extern "C" size_t tb_ternary_gemm_workspace_size(int64_t M, int64_t K) {
 
 extern "C" size_t tb_ternary_gemm_workspace_size_n(int64_t M, int64_t K, int64_t N) {
   if (M <= 0 || K <= 0 || K % kGroup || N <= 0) return tb_ternary_gemm_workspace_size(M, K);
-  return static_cast<size_t>(gemm_split_plan(M, K, N, gemm_device_cus()).total);
+  return static_cast<size_t>(gemm_split_plan(M, K, N, device_cus()).total);
 }
 
 extern "C" int tb_ternary_gemm_prepare(const void* x, int x_dtype, int64_t M, int64_t K, const int8_t* signs,

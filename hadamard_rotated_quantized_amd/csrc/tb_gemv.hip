@@ -489,12 +489,8 @@ template <int NB, int WPT, bool AG>
 static void launch_main_cfg(const MultiArgs& a, size_t lds, int grid, hipStream_t st) {
   constexpr int M = NB == 1 ? 16 : 32;
   auto kern = gemv_main_kernel<NB, M, WPT, (AG ? 2 : 4), AG>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              150 * 1024);
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  lds_limit_once(reinterpret_cast<const void*>(kern), 150 * 1024, lds_set);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, a);
 }
 
@@ -511,13 +507,6 @@ static void launch_main(const MultiArgs& a, int wpt, int64_t max_gp, int grid, h
     if (wpt == 1) launch_main_cfg<NB, 1, false>(a, lds, grid, st);
     else launch_main_cfg<NB, 4, false>(a, lds, grid, st);
   }
-}
-
-static int device_cus() {
-  int dev = 0, cus = 256;
-  (void)hipGetDevice(&dev);
-  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  return cus;
 }
 
 static int gemv_common_checks(int64_t B, int64_t K, int64_t N, const char* who) {
@@ -639,7 +628,7 @@ static void gemv_run_launch(const void* workspace, int64_t B, int64_t K, const u
 
 static int run_checks(int64_t N, int64_t K, const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
                       const float* y, const char* who) {
-  TB_TRY(check_container(codes, scales, biases, who));
+  TB_TRY(check_container(codes, scales, biases, who, 4));
   if (!y) {
     set_error("%s: y is NULL", who);
     return TB_ERR_ARG;
@@ -720,7 +709,8 @@ extern "C" int tb_ternary_gemv(const void* x, int x_dtype, int64_t B, int64_t K,
     return TB_OK;
   }
   TB_TRY(gemv_ws_check(workspace, ws_bytes, B, K, who));
-  if (gemv_band_eligible(B, K, N, block)) {
+  // the band kernel stages scales and biases with 16-byte direct-to-LDS loads
+  if (gemv_band_eligible(B, K, N, block) && aligned(scales, 16) && aligned(biases, 16)) {
     gemv_band_launch(x, x_dtype, K, signs, block, codes, scales, biases, N, y, st);
     TB_LAUNCH_CHECK(who);
     return TB_OK;

@@ -60,6 +60,8 @@
 // tb_ternary_gemv takes other paths otherwise.
 #include <algorithm>
 
+#include <numeric>
+
 #include "tb_xform.h"
 
 namespace tb {
@@ -328,13 +330,6 @@ __global__ __launch_bounds__(kBandThreads, 1) void gemv_band_kernel(
 // --------------------------------------------------------------------------
 // host side
 // --------------------------------------------------------------------------
-static int band_device_cus() {
-  int dev = 0, cus = 256;
-  (void)hipGetDevice(&dev);
-  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  return cus;
-}
-
 struct BandPlan {
   int rows, tsub, grid, mi;
   int64_t lds;
@@ -346,7 +341,11 @@ static BandPlan band_plan(int64_t K, int64_t N, int cus) {
   const int64_t G = K / kGroup, W = K / kCodesPerWord, RB = W * 4;
   const int64_t Gp = (G + 3) / 4 * 4, S = Gp / 4;
   const int64_t nch = (K + 1023) / 1024;
-  const int64_t rows = std::max<int64_t>((N + cus - 1) / cus, 16);
+  // rows * G a multiple of 8 keeps every band's scale and bias rows (band0 * G
+  // fp16 from a 16-byte aligned base) 16-byte aligned for the direct-to-LDS
+  // staging
+  const int64_t rq = 8 / std::gcd<int64_t>(G, 8);
+  const int64_t rows = (std::max<int64_t>((N + cus - 1) / cus, 16) + rq - 1) / rq * rq;
   const int64_t tsub = (rows + 15) / 16;
   p.rows = static_cast<int>(rows);
   p.tsub = static_cast<int>(tsub);
@@ -367,19 +366,15 @@ static BandPlan band_plan(int64_t K, int64_t N, int cus) {
 
 bool gemv_band_eligible(int64_t B, int64_t K, int64_t N, int block) {
   if (B != 1 || !(block == 0 || block == 512 || block == 1024)) return false;
-  return band_plan(K, N, band_device_cus()).ok;
+  return band_plan(K, N, device_cus()).ok;
 }
 
 template <int L, int DT, int MI>
 static void band_launch_t(const void* x, const int8_t* signs, const uint32_t* codes, const uint16_t* scales,
                           const uint16_t* biases, float* y, int N, int K, const BandPlan& p, hipStream_t st) {
   auto kern = gemv_band_kernel<L, DT, MI>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              static_cast<int>(kBandLdsMax));
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  lds_limit_once(reinterpret_cast<const void*>(kern), static_cast<int>(kBandLdsMax), lds_set);
   hipLaunchKernelGGL(kern, dim3(p.grid), dim3(kBandThreads), static_cast<size_t>(p.lds), st, x, signs, codes, scales,
                      biases, N, K, p.rows, p.tsub, y);
 }
@@ -404,7 +399,7 @@ static void band_launch_l(int dt, const void* x, const int8_t* signs, const uint
 
 void gemv_band_launch(const void* x, int x_dtype, int64_t K, const int8_t* signs, int block, const uint32_t* codes,
                       const uint16_t* scales, const uint16_t* biases, int64_t N, float* y, hipStream_t st) {
-  const BandPlan p = band_plan(K, N, band_device_cus());
+  const BandPlan p = band_plan(K, N, device_cus());
   const int n = static_cast<int>(N), k = static_cast<int>(K);
   if (block == 0) band_launch_l<0>(x_dtype, x, signs, codes, scales, biases, y, n, k, p, st);
   else if (block == 512) band_launch_l<512>(x_dtype, x, signs, codes, scales, biases, y, n, k, p, st);

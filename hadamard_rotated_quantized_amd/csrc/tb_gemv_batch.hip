@@ -54,13 +54,6 @@ struct BatchPlan {
   bool ok;
 };
 
-static int batch_device_cus() {
-  int dev = 0, cus = 256;
-  (void)hipGetDevice(&dev);
-  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  return cus;
-}
-
 // Work units: ceil(N / 128) row blocks x S slices of cps chunks, about one
 // per CU; a slice's operand rows must fit the LDS.
 static BatchPlan batch_plan(int64_t B, int64_t K, int64_t N, int cus) {
@@ -269,11 +262,11 @@ __global__ __launch_bounds__(256) void batch_reduce_kernel(const float* __restri
 bool gemv_batch_eligible(int64_t B, int64_t K, int64_t N, int block) {
   if (B < 2 || B > TB_GEMV_MAX_BATCH || !(block == 0 || block == 512 || block == 1024) || K % 256) return false;
   if (N <= 0 || N > (int64_t(1) << 30) || K > (int64_t(1) << 24)) return false;
-  return batch_plan(B, K, N, batch_device_cus()).ok;
+  return batch_plan(B, K, N, device_cus()).ok;
 }
 
 size_t gemv_batch_workspace(int64_t B, int64_t K, int64_t N) {
-  const BatchPlan p = batch_plan(B, K, N, batch_device_cus());
+  const BatchPlan p = batch_plan(B, K, N, device_cus());
   return static_cast<size_t>(batch_ws_bytes(B, N, p));
 }
 
@@ -282,12 +275,8 @@ static void batch_stream_launch(const BatchPlan& p, const void* x, const int8_t*
                                 const uint16_t* scales, const uint16_t* biases, float* out, int B, int N, int K,
                                 hipStream_t st) {
   auto kern = batch_stream_kernel<NS, L, DT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              static_cast<int>(kBatLdsMax));
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  lds_limit_once(reinterpret_cast<const void*>(kern), static_cast<int>(kBatLdsMax), lds_set);
   hipLaunchKernelGGL(kern, dim3(p.grid), dim3(kBatThreads), static_cast<size_t>(p.lds), st, x, signs, codes, scales,
                      biases, out, B, N, K, p.cps, p.S);
 }
@@ -312,7 +301,7 @@ static void batch_launch_l(int block, int dt, const BatchPlan& p, const void* x,
 void gemv_batch_launch(const void* x, int x_dtype, int64_t B, int64_t K, const int8_t* signs, int block,
                        const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, int64_t N, float* y,
                        void* workspace, hipStream_t st) {
-  const BatchPlan p = batch_plan(B, K, N, batch_device_cus());
+  const BatchPlan p = batch_plan(B, K, N, device_cus());
   const int b = static_cast<int>(B), k = static_cast<int>(K), n = static_cast<int>(N);
   float* out = p.S > 1 ? static_cast<float*>(workspace) : y;
   if (b <= 4) batch_launch_l<1>(block, x_dtype, p, x, signs, codes, scales, biases, out, b, n, k, st);

@@ -515,13 +515,6 @@ __global__ __launch_bounds__(kFusedThreads, NB == 8 ? 2 : 4) void gemv_fused_ker
   }
 }
 
-static int fused_device_cus() {
-  int dev = 0, cus = 256;
-  (void)hipGetDevice(&dev);
-  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  return cus;
-}
-
 // Launch shape of one call.
 struct FusedPlan {
   int mode;
@@ -577,7 +570,7 @@ bool gemv_fused_eligible(int64_t B, int64_t K, int64_t N, int block) {
   if (!(block == 0 || block == 512 || block == 1024)) return false;
   const int64_t nch = (K + 1023) / 1024;
   if (B * nch > (int64_t)kFusedWaves * kFusedChunksPerWave) return false;
-  return fused_plan(B, K, N, fused_device_cus()).lds <= kFusedLdsMax;
+  return fused_plan(B, K, N, device_cus()).lds <= kFusedLdsMax;
 }
 
 template <int NB, int L, int DT, int MODE>
@@ -586,12 +579,8 @@ static void fused_launch_m(const void* x, const int8_t* signs, const uint32_t* c
                            size_t lds, hipStream_t st) {
   constexpr int M = NB == 1 ? 16 : 32;
   auto kern = gemv_fused_kernel<NB, M, L, DT, MODE>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              static_cast<int>(kFusedLdsMax));
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  lds_limit_once(reinterpret_cast<const void*>(kern), static_cast<int>(kFusedLdsMax), lds_set);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kFusedThreads), lds, st, x, signs, codes, scales, biases, N, K, cfg,
                      aux, y);
 }
@@ -638,7 +627,7 @@ static void fused_launch_l(int mode, int block, int dt, const void* x, const int
 void gemv_fused_launch(const void* x, int x_dtype, int64_t B, int64_t K, const int8_t* signs, int block,
                        const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, int64_t N,
                        float* y, hipStream_t st) {
-  const FusedPlan p = fused_plan(B, K, N, fused_device_cus());
+  const FusedPlan p = fused_plan(B, K, N, device_cus());
   const int cfg = static_cast<int>(B) | (p.tsub << 5) | (p.grid << 8);
   const int n = static_cast<int>(N), k = static_cast<int>(K);
   const size_t lds = static_cast<size_t>(p.lds);

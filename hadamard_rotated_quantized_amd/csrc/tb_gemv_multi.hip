@@ -7,9 +7,12 @@
 // A decode step runs hundreds of linears of 1.5 to 360 MB each; launched one
 // by one, each pays a kernel launch and its own ramp.  Here:
 //
-// 1. multi_prep_kernel: one wave per 1024-input chunk of every module's
-//    input, the in-register MFMA transform (tb_xform.h), writing each
-//    module's exact four-limb operand image and group sums to the workspace.
+// 1. multi_prep_kernel: one wave per 1024-input chunk of every distinct
+//    input, the in-register MFMA transform (tb_xform.h), writing its exact
+//    four-limb operand image and group sums to the workspace.  Modules that
+//    read the same x with the same signs (q/k/v_proj, gate/up_proj and
+//    in_proj_qkv/z of a layer: one sign vector per input width, kwkr.cn
+//    "ternary weights + folded Hadamard rotation") share one image.
 //
 // 2. multi_stream_kernel: one persistent workgroup per CU.  The host cuts
 //    the concatenated list of 16-row tiles (all modules, in order) into
@@ -33,6 +36,8 @@
 //    span.
 #include <algorithm>
 #include <array>
+#include <map>
+#include <tuple>
 #include <vector>
 
 #include "tb_xform.h"
@@ -142,7 +147,7 @@ __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __
   const bool a_lane = alg == lg;
   float* const ybuf = reinterpret_cast<float*>(lds + multi_lds_ybuf(max_nch)) + wave * (kMultiYbuf * 16);
 
-  int img_m = -1;  // module whose image is in LDS
+  int img_off = -1;  // workspace offset of the operand image in LDS
   for (;;) {
     // the next piece, taken by one lane (a vector atomic) and shared in LDS
     if (tid == 0) piece_next = atomicAdd(counter, 1);
@@ -156,10 +161,11 @@ __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __
     const int K = md.K, G = K / kGroup, RB = K / 4;
     const int S = (G + GPS - 1) / GPS;
     const int nch = multi_nch(K);
-    // the module's operand image and group sums into LDS (unless they are
-    // there from the previous piece)
-    if (m != img_m) {
-      img_m = m;
+    // the module's operand image and group sums into LDS, unless the
+    // previous piece left the same image there (the same module, or another
+    // module reading the same input)
+    if (md.ws_off != img_off) {
+      img_off = md.ws_off;
       const char* img = ws + md.ws_off;
       const int rows = nch * 8 * kXfLimbs;
       for (int i = tid; i < rows * 8; i += kMultiThreads) {
@@ -296,13 +302,6 @@ __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-static int multi_device_cus() {
-  int dev = 0, cus = 256;
-  (void)hipGetDevice(&dev);
-  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  return cus;
-}
-
 
 static inline int64_t align64(int64_t v) { return (v + 63) & ~int64_t(63); }
 
@@ -350,10 +349,27 @@ static std::vector<std::array<int32_t, 3>> multi_pieces(const tb_gemv_module* mo
   return out;
 }
 
+// Modules that read the same input -- the same x and sign vector at the same
+// width, as q/k/v_proj, gate/up_proj and in_proj_qkv/z of one layer do --
+// share one operand image and its transform tasks.  Per module: the first
+// module of the list with the same input (the image's owner; itself for
+// modules that are skipped or own their image).
+static std::vector<int64_t> multi_image_owner(const tb_gemv_module* mods, int64_t count) {
+  std::vector<int64_t> owner(static_cast<size_t>(count));
+  std::map<std::tuple<const void*, const int8_t*, int64_t>, int64_t> first;
+  for (int64_t i = 0; i < count; ++i) {
+    owner[i] = i;
+    if (mods[i].N <= 0) continue;
+    owner[i] = first.emplace(std::make_tuple(mods[i].x, mods[i].signs, mods[i].K), i).first->second;
+  }
+  return owner;
+}
+
 static int64_t multi_total_tasks(const tb_gemv_module* mods, int64_t count) {
+  const std::vector<int64_t> owner = multi_image_owner(mods, count);
   int64_t t = 0;
   for (int64_t i = 0; i < count; ++i)
-    if (mods[i].N > 0) t += multi_nch(static_cast<int>(mods[i].K));
+    if (mods[i].N > 0 && owner[i] == i) t += multi_nch(static_cast<int>(mods[i].K));
   return t;
 }
 
@@ -365,7 +381,7 @@ extern "C" size_t tb_gemv_multi_plan_size(const tb_gemv_module* mods, int64_t co
   if (!mods || count <= 0) return 0;
   for (int64_t i = 0; i < count; ++i)
     if (mods[i].N < 0 || mods[i].K <= 0) return 0;  // the plan call reports the error
-  const int64_t np = static_cast<int64_t>(multi_pieces(mods, count, multi_device_cus()).size());
+  const int64_t np = static_cast<int64_t>(multi_pieces(mods, count, device_cus()).size());
   return static_cast<size_t>(plan_offsets(count, multi_total_tasks(mods, count), np).total);
 }
 
@@ -420,8 +436,10 @@ extern "C" int tb_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int
     const int nch = multi_nch(static_cast<int>(m.K));
     max_nch = std::max(max_nch, nch);
     tiles += (m.N + 15) / 16;
-    ws += static_cast<int64_t>(nch) * (kMultiImgChunk + 64);
   }
+  const std::vector<int64_t> owner = multi_image_owner(mods, count);
+  for (int64_t i = 0; i < count; ++i)
+    if (mods[i].N > 0 && owner[i] == i) ws += static_cast<int64_t>(multi_nch(static_cast<int>(mods[i].K))) * (kMultiImgChunk + 64);
   if (multi_lds_total(max_nch) > kMultiLdsMax) {
     set_error("%s: K up to %d takes too much LDS for the stream kernel", who, max_nch * 1024);
     return TB_ERR_UNSUPPORTED;
@@ -430,7 +448,7 @@ extern "C" int tb_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int
     set_error("%s: the module list is too large for one plan", who);
     return TB_ERR_SHAPE;
   }
-  const int grid = multi_device_cus();
+  const int grid = device_cus();
   const int64_t ntasks = multi_total_tasks(mods, count);
   const std::vector<std::array<int32_t, 3>> pcs = multi_pieces(mods, count, grid);
   if (pcs.size() >= (size_t(1) << 30)) {
@@ -461,7 +479,7 @@ extern "C" int tb_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int
   std::memcpy(p, &hd, sizeof hd);
   MultiModule* md = reinterpret_cast<MultiModule*>(p + hd.modules_off);
   int32_t* tk = reinterpret_cast<int32_t*>(p + hd.tasks_off);
-  std::vector<int64_t> tile_cost;  // per module: cost of one tile
+  std::vector<int64_t> img_off(static_cast<size_t>(count), 0);  // per image owner: its workspace offset
   int64_t t0 = 0, off = kMultiWsHead, nt = 0;
   for (int64_t i = 0; i < count; ++i) {
     const tb_gemv_module& m = mods[i];
@@ -475,16 +493,19 @@ extern "C" int tb_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int
     d.N = static_cast<int32_t>(m.N);
     d.K = static_cast<int32_t>(m.K);
     d.tile0 = static_cast<int32_t>(t0);
-    d.ws_off = static_cast<int32_t>(off);
+    const bool owns = owner[i] == i;
+    if (m.N > 0 && owns) img_off[i] = off;
+    d.ws_off = static_cast<int32_t>(m.N > 0 ? img_off[owner[i]] : off);
     std::memcpy(md + i, &d, sizeof d);
     if (m.N == 0) continue;
+    t0 += (m.N + 15) / 16;
+    if (!owns) continue;  // the owner's tasks write the shared image
     const int nch = multi_nch(static_cast<int>(m.K));
     for (int c = 0; c < nch; ++c) {
       tk[2 * nt] = static_cast<int32_t>(i);
       tk[2 * nt + 1] = c;
       ++nt;
     }
-    t0 += (m.N + 15) / 16;
     off += static_cast<int64_t>(nch) * (kMultiImgChunk + 64);
   }
   int32_t* pq = reinterpret_cast<int32_t*>(p + hd.pieces_off);
@@ -506,12 +527,8 @@ static void multi_prep_launch(const void* plan, void* ws, int tasks, hipStream_t
 
 template <int NW, int P>
 static void multi_stream_launch(const void* plan, void* ws, int grid, size_t lds, hipStream_t st) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(multi_stream_kernel<NW, P>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kMultiLdsMax));
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  lds_limit_once(reinterpret_cast<const void*>(multi_stream_kernel<NW, P>), static_cast<int>(kMultiLdsMax), lds_set);
   hipLaunchKernelGGL((multi_stream_kernel<NW, P>), dim3(grid), dim3(64 * NW), lds, st,
                      static_cast<const char*>(plan), static_cast<char*>(ws));
 }

@@ -55,7 +55,7 @@ int check_rotation(int64_t K, int block, const int8_t* signs, const char* who) {
 }
 
 int check_container(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
-                    const char* who) {
+                    const char* who, int sb_align) {
   if (!codes || !scales || !biases) {
     set_error("%s: codes, scales and biases must be non-NULL", who);
     return TB_ERR_ARG;
@@ -64,8 +64,8 @@ int check_container(const uint32_t* codes, const uint16_t* scales, const uint16_
     set_error("%s: codes must be 16-byte aligned", who);
     return TB_ERR_ALIGN;
   }
-  if (!aligned(scales, 2) || !aligned(biases, 2)) {
-    set_error("%s: scales and biases must be 2-byte aligned", who);
+  if (!aligned(scales, sb_align) || !aligned(biases, sb_align)) {
+    set_error("%s: scales and biases must be %d-byte aligned", who, sb_align);
     return TB_ERR_ALIGN;
   }
   return TB_OK;

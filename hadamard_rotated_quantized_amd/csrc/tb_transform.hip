@@ -10,6 +10,8 @@
 // One 256-thread workgroup per (row, block): the block is staged in LDS as
 // fp32 (at most 4096 values = 16 KB), transformed in place by radix-4 LDS
 // passes, scaled once by 1/sqrt(L), and written back.
+#include <algorithm>
+
 #include "tb_device.h"
 
 namespace tb {
@@ -85,14 +87,38 @@ __global__ __launch_bounds__(kThreads) void embed_plain_kernel(
     o[k] = (r < 0 || r >= V) ? __builtin_nanf("") : decode_weight(codes, scales, biases, r, K, k);
 }
 
+// Rows (and embedding ids) go in grid.y, which takes at most 65535: larger
+// calls are launched in row chunks with offset pointers.
+constexpr int64_t kRowChunk = 65535;
+
 template <int L>
 static void launch_fwht(const void* x, int dt, float* y, const int8_t* s, int64_t rows, int64_t K,
                         int inverse, hipStream_t st) {
-  dim3 grid(static_cast<unsigned>(K / L), static_cast<unsigned>(rows));
-  if (dt == TB_F32)
-    hipLaunchKernelGGL((fwht_signed_kernel<L, TB_F32>), grid, dim3(kThreads), 0, st, x, y, s, K, inverse);
-  else
-    hipLaunchKernelGGL((fwht_signed_kernel<L, TB_BF16>), grid, dim3(kThreads), 0, st, x, y, s, K, inverse);
+  const int64_t esz = dt == TB_F32 ? 4 : 2;
+  for (int64_t r0 = 0; r0 < rows; r0 += kRowChunk) {
+    const dim3 grid(static_cast<unsigned>(K / L), static_cast<unsigned>(std::min(kRowChunk, rows - r0)));
+    const void* xr = static_cast<const char*>(x) + r0 * K * esz;
+    float* yr = y + r0 * K;
+    if (dt == TB_F32)
+      hipLaunchKernelGGL((fwht_signed_kernel<L, TB_F32>), grid, dim3(kThreads), 0, st, xr, yr, s, K, inverse);
+    else
+      hipLaunchKernelGGL((fwht_signed_kernel<L, TB_BF16>), grid, dim3(kThreads), 0, st, xr, yr, s, K, inverse);
+  }
+}
+
+template <int L>
+static void launch_embed(const int32_t* ids, int64_t T, const uint32_t* codes, const uint16_t* scales,
+                         const uint16_t* biases, int64_t V, int64_t K, const int8_t* signs, float* out,
+                         hipStream_t st) {
+  for (int64_t t0 = 0; t0 < T; t0 += kRowChunk) {
+    const unsigned nt = static_cast<unsigned>(std::min(kRowChunk, T - t0));
+    if constexpr (L == 0)
+      hipLaunchKernelGGL(embed_plain_kernel, dim3(static_cast<unsigned>((K + 1023) / 1024), nt), dim3(kThreads), 0,
+                         st, ids + t0, codes, scales, biases, V, K, out + t0 * K);
+    else
+      hipLaunchKernelGGL(embed_inverse_kernel<L>, dim3(static_cast<unsigned>(K / L), nt), dim3(kThreads), 0, st,
+                         ids + t0, codes, scales, biases, V, K, signs, out + t0 * K);
+  }
 }
 
 }  // namespace tb
@@ -125,10 +151,6 @@ extern "C" int tb_fwht_signed(const void* x, int x_dtype, float* y, const int8_t
     set_error("%s: y must be 4-byte aligned", who);
     return TB_ERR_ALIGN;
   }
-  if (rows > 65535) {
-    set_error("%s: rows=%lld exceeds 65535 per call", who, (long long)rows);
-    return TB_ERR_SHAPE;
-  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   switch (block) {
     case 512: launch_fwht<512>(x, x_dtype, y, signs, rows, K, inverse, st); break;
@@ -160,33 +182,13 @@ extern "C" int tb_embed_inverse(const int32_t* ids, int64_t T, const uint32_t* c
     set_error("%s: ids and out must be 4-byte aligned", who);
     return TB_ERR_ALIGN;
   }
-  if (T > 65535) {
-    set_error("%s: T=%lld exceeds 65535 per call", who, (long long)T);
-    return TB_ERR_SHAPE;
-  }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const dim3 thr(kThreads);
   switch (block) {
-    case 0:
-      hipLaunchKernelGGL(embed_plain_kernel, dim3((unsigned)((K + 1023) / 1024), (unsigned)T), thr, 0,
-                         st, ids, codes, scales, biases, V, K, out);
-      break;
-    case 512:
-      hipLaunchKernelGGL(embed_inverse_kernel<512>, dim3((unsigned)(K / 512), (unsigned)T), thr, 0, st,
-                         ids, codes, scales, biases, V, K, signs, out);
-      break;
-    case 1024:
-      hipLaunchKernelGGL(embed_inverse_kernel<1024>, dim3((unsigned)(K / 1024), (unsigned)T), thr, 0, st,
-                         ids, codes, scales, biases, V, K, signs, out);
-      break;
-    case 2048:
-      hipLaunchKernelGGL(embed_inverse_kernel<2048>, dim3((unsigned)(K / 2048), (unsigned)T), thr, 0, st,
-                         ids, codes, scales, biases, V, K, signs, out);
-      break;
-    default:
-      hipLaunchKernelGGL(embed_inverse_kernel<4096>, dim3((unsigned)(K / 4096), (unsigned)T), thr, 0, st,
-                         ids, codes, scales, biases, V, K, signs, out);
-      break;
+    case 0: launch_embed<0>(ids, T, codes, scales, biases, V, K, signs, out, st); break;
+    case 512: launch_embed<512>(ids, T, codes, scales, biases, V, K, signs, out, st); break;
+    case 1024: launch_embed<1024>(ids, T, codes, scales, biases, V, K, signs, out, st); break;
+    case 2048: launch_embed<2048>(ids, T, codes, scales, biases, V, K, signs, out, st); break;
+    default: launch_embed<4096>(ids, T, codes, scales, biases, V, K, signs, out, st); break;
   }
   TB_LAUNCH_CHECK(who);
   return TB_OK;

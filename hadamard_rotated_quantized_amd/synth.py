@@ -165,6 +165,37 @@ def sweep_signs():
     return {K: draw_signs(rng, K) for K in (5120, 6144, 17408)}
 
 
+def sweep_input_sites():
+    """Per sweep module, the index of the activation it reads, in the order
+    of sweep_modules().  Modules of one layer that read the same hidden state
+    share it, as a decode layer feeds them: q/k/v_proj (or in_proj_qkv and
+    in_proj_z) read the attention input, o_proj (out_proj) the attention
+    output, gate/up_proj the MLP input and down_proj the MLP's inner state;
+    lm_head reads the final hidden state.  The embedding lookup reads none
+    (-1)."""
+    sites, index = [], {}
+    for name, N, K, kind in sweep_modules():
+        if kind != "linear":
+            sites.append(-1)
+            continue
+        short = name.split(".")[-1]
+        layer = name.split(".")[1] if name.startswith("layers.") else "final"
+        role = {"q_proj": "attn_in", "k_proj": "attn_in", "v_proj": "attn_in", "in_proj_qkv": "attn_in",
+                "in_proj_z": "attn_in", "o_proj": "attn_out", "out_proj": "attn_out", "gate_proj": "mlp_in",
+                "up_proj": "mlp_in", "down_proj": "mlp_mid", "lm_head": "final"}[short]
+        sites.append(index.setdefault((layer, role), len(index)))
+    return sites
+
+
+def device_site_x(site: int, K: int, device):
+    """Activation of input site `site` of the sweep: (1, K) bf16, N(0, 1)
+    rounded to nearest even, drawn on `device` with torch's generator."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(SWEEP_SEED * 1_000_003 + 700_001 + site)
+    return torch.randn((1, K), generator=g, device=device).to(torch.bfloat16)
+
+
 def device_module_draw(index: int, N: int, K: int, B: int, device):
     """Draw module `index` of the sweep on `device` with torch's generator:
     returns (t int8 (N,K), scales fp16 (N,K/128), x bf16 (B,K)) as tensors."""

@@ -150,8 +150,8 @@ size_t tb_ternary_gemv_workspace_size_n(int64_t B, int64_t K, int64_t N);
 /* Packed linear for decode batches [P3 "text model loading"]:
  *   y[b][n] = sum_k W~[n][k] (R x[b])[k],  b < B <= TB_GEMV_MAX_BATCH.
  * x: B x K (x_dtype), 16-byte aligned; signs 16-byte aligned; codes/scales/
- * biases as defined above (codes 16-byte aligned); y: B x N fp32
- * (overwritten, 4-byte aligned).  workspace: device
+ * biases as defined above (codes 16-byte aligned, scales and biases 4-byte
+ * aligned, else TB_ERR_ALIGN); y: B x N fp32 (overwritten, 4-byte aligned).  workspace: device
  * scratch of at least tb_ternary_gemv_workspace_size(B, K) bytes, 16-byte
  * aligned, needing no initialisation; it must not be reused by another call
  * until this one completes on the stream.  Equivalent to
@@ -252,7 +252,9 @@ size_t tb_gemv_multi_plan_size(const tb_gemv_module* mods, int64_t count);
 
 /* Build the plan (host memory, plan_bytes >= tb_gemv_multi_plan_size) for the
  * modules (host array), all sharing x_dtype and block (0, 512 or 1024), and
- * report the workspace the run needs.  The plan holds the module table, the
+ * report the workspace the run needs.  Modules with the same x, signs and K
+ * (e.g. q/k/v_proj reading one hidden state) share one transform and one
+ * operand image.  The plan holds the module table, the
  * transform tasks and a split of all modules' 16-row output tiles into
  * pieces of one module each (shrinking toward the end of the list) that the
  * streaming workgroups take in order from a counter in the workspace; it

@@ -220,3 +220,96 @@ def test_binding_refuses_host_tensors():
     torch = pytest.importorskip("torch")
     with pytest.raises(TypeError):
         tb.tb_fwht_signed(torch.zeros(1, 1024), torch.ones(1024, dtype=torch.int8), 1024)
+
+
+def test_gemv_rejects_scales_not_dword_aligned():
+    # the decode-matmul kernels load scales and biases as dwords and vectors
+    assert _gemv(scales=DUMMY + 2) == -8
+    assert _gemv(biases=DUMMY + 2) == -8
+    assert tb.lib().tb_ternary_gemv_run(DUMMY, 1 << 30, 1, 1024, DUMMY, DUMMY + 2, DUMMY, 16, DUMMY, None) == -8
+
+
+# --- the Python binding checks tensor shapes before any pointer is passed ---
+def _host_linear(N=32, K=1024, B=2):
+    torch = pytest.importorskip("torch")
+    return dict(x=torch.zeros(B, K, dtype=torch.bfloat16), signs=torch.ones(K, dtype=torch.int8),
+                codes=torch.zeros(N, K // 16, dtype=torch.int32), scales=torch.zeros(N, K // 128, dtype=torch.float16),
+                biases=torch.zeros(N, K // 128, dtype=torch.float16))
+
+
+def _bad_variants():
+    torch = pytest.importorskip("torch")
+    return [
+        ("codes", torch.zeros(32, 1024 // 16 - 1, dtype=torch.int32)),   # one word short per row
+        ("codes", torch.zeros(32 * 64, dtype=torch.int32)),              # flat
+        ("scales", torch.zeros(32, 4, dtype=torch.float16)),             # K/128 = 8
+        ("biases", torch.zeros(31, 8, dtype=torch.float16)),             # N - 1 rows
+        ("signs", torch.ones(512, dtype=torch.int8)),                    # half width
+        ("x", torch.zeros(2, 1000, dtype=torch.bfloat16)),               # K not a multiple of 128
+        ("x", torch.zeros(1024, dtype=torch.bfloat16)),                  # not 2-D
+    ]
+
+
+@pytest.mark.parametrize("i", range(7))
+def test_binding_gemv_gemm_reject_mismatched_shapes(i):
+    name, bad = _bad_variants()[i]
+    for fn in (tb.tb_ternary_gemv, tb.tb_ternary_gemm):
+        a = _host_linear()
+        a[name] = bad
+        with pytest.raises(ValueError):
+            fn(a["x"], a["signs"], 1024, a["codes"], a["scales"], a["biases"])
+
+
+def test_binding_rejects_wrong_out_and_sign_presence():
+    torch = pytest.importorskip("torch")
+    a = _host_linear()
+    with pytest.raises(ValueError):
+        tb.tb_ternary_gemv(a["x"], a["signs"], 1024, a["codes"], a["scales"], a["biases"],
+                           out=torch.zeros(2, 31))
+    with pytest.raises(ValueError):   # block 0 takes no signs
+        tb.tb_ternary_gemv(a["x"], a["signs"], 0, a["codes"], a["scales"], a["biases"])
+    with pytest.raises(ValueError):   # a block needs signs
+        tb.tb_ternary_gemm(a["x"], None, 1024, a["codes"], a["scales"], a["biases"])
+    with pytest.raises(ValueError):
+        tb.tb_ternary_gemv_run(torch.zeros(16, dtype=torch.uint8), 2, 2048, a["codes"], a["scales"], a["biases"])
+    with pytest.raises(ValueError):
+        tb.tb_ternary_gemm_run(torch.zeros(16, dtype=torch.uint8), 2, 1024, a["codes"], a["scales"][:, :4],
+                               a["biases"])
+
+
+def test_binding_embed_fwht_pack_reject_mismatched_shapes():
+    torch = pytest.importorskip("torch")
+    a = _host_linear()
+    ids = torch.zeros(3, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        tb.tb_embed_inverse(ids, a["codes"], a["scales"][:, :7], a["biases"], a["signs"], 1024)
+    with pytest.raises(ValueError):
+        tb.tb_embed_inverse(ids, a["codes"], a["scales"], a["biases"], a["signs"][:1000], 1024)
+    with pytest.raises(ValueError):
+        tb.tb_embed_inverse(ids.view(3, 1), a["codes"], a["scales"], a["biases"], a["signs"], 1024)
+    with pytest.raises(ValueError):
+        tb.tb_fwht_signed(torch.zeros(2, 2048), torch.ones(1024, dtype=torch.int8), 1024)
+    with pytest.raises(ValueError):
+        tb.tb_fwht_signed(torch.zeros(2, 1024), torch.ones(1024, dtype=torch.int8), 1024, out=torch.zeros(1, 1024))
+    with pytest.raises(ValueError):
+        tb.tb_pack_device(torch.zeros(4, 256, dtype=torch.int8), torch.zeros(4, 3, dtype=torch.float16))
+
+
+def test_binding_multi_plan_rejects_mismatched_module():
+    torch = pytest.importorskip("torch")
+    a = _host_linear(B=1)
+    y = torch.zeros(1, 32)
+    mod = [a["x"], a["signs"], a["codes"], a["scales"], a["biases"], y]
+    for j, bad in ((2, a["codes"][:, :10]), (3, a["scales"][:5]), (1, a["signs"][:100]), (5, torch.zeros(1, 30)),
+                   (0, torch.zeros(2, 1024, dtype=torch.bfloat16))):
+        m = list(mod)
+        m[j] = bad
+        with pytest.raises(ValueError):
+            tb.tb_gemv_multi_plan([tuple(m)], 1024)
+
+
+def test_host_pack_unpack_reject_bad_shapes():
+    with pytest.raises(ValueError):
+        tb.tb_pack(np.zeros((4, 100), np.int8), np.zeros((4, 0), np.float16))
+    with pytest.raises(ValueError):
+        tb.tb_unpack(np.zeros((4, 63), np.uint32), 1024)

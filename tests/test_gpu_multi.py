@@ -87,3 +87,41 @@ def test_multi_graph_replays_match_eager():
         T.cuda.synchronize()
         for e, m in zip(eager, mods):
             assert T.equal(e, m[5]), r
+
+
+def test_multi_shared_inputs_match_oracle_and_single_calls():
+    """Modules that read one activation (same x tensor and signs) share one
+    transform and one operand image; interleaved with modules that read
+    others, every module must still match the oracle and its single call."""
+    announce("multi shared inputs")
+    T = torch()
+    rng = np.random.default_rng(73)
+    inputs = {}
+    for key, K in (("a", 5120), ("b", 17408), ("c", 5120)):
+        x64, xs = synth.draw_activations(rng, 1, K, "bf16")
+        sig = synth.draw_signs(rng, K)
+        inputs[key] = (x64, T.from_numpy(xs.view(np.int16)).view(T.bfloat16).cuda(), sig, signs_to_device(sig))
+    plan_spec = [("a", 300), ("a", 1024), ("b", 513), ("a", 77), ("c", 640), ("b", 100), ("c", 16)]
+    mods, want = [], []
+    for j, (key, N) in enumerate(plan_spec):
+        x64, x, sig, sg = inputs[key]
+        K = x.shape[-1]
+        t = synth.draw_ternary(rng, N, K)
+        sc = synth.draw_scales(rng, N, K)
+        codes, s, b = pack_to_device(t, sc)
+        y = T.full((1, N), float("nan"), dtype=T.float32, device="cuda")
+        mods.append((x, sg, codes, s, b, y))
+        oc, osc, ob = oracle.pack(t, sc)
+        want.append(oracle.packed_linear(x64, sig, 1024, oc, osc, ob))
+    plan, wsb = tb.tb_gemv_multi_plan(mods, 1024)
+    assert int(plan[:32].view(np.int32)[2]) == 5 + 17 + 5   # one transform per distinct input
+    pd = T.from_numpy(plan).cuda()
+    ws = T.empty(wsb, dtype=T.uint8, device="cuda")
+    tb.tb_ternary_gemv_multi(plan, pd, ws)
+    T.cuda.synchronize()
+    for (key, N), m, w in zip(plan_spec, mods, want):
+        compare(m[5].cpu().numpy(), w, f"shared input {key} N={N}")
+        y1 = tb.tb_ternary_gemv(m[0], m[1], 1024, m[2], m[3], m[4])
+        T.cuda.synchronize()
+        d = (y1.double() - m[5].double()).abs().max().item()
+        assert d <= 1e-6 * y1.abs().max().item(), (key, N, d)

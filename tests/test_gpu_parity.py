@@ -61,21 +61,27 @@ def test_down_proj_gemv_batches():
         compare(y.cpu().numpy(), want[:B], f"down_proj B={B}")
 
 
-def test_prefill_gemm_sampled_rows():
-    announce("prefill_gate_up M=2048 K=5120 N=17408 bf16 seed 4 (sampled rows)")
+def test_prefill_gemm_full():
+    """Every one of the 2048 x 17408 outputs against the fp64 oracle, in the
+    launch configuration the benchmark times (the workspace that enables the
+    tail split)."""
+    announce("prefill_gate_up M=2048 K=5120 N=17408 bf16 seed 4 (all outputs)")
     T = torch()
     p = synth.config_problem("prefill_gate_up")
     codes, s, b = pack_to_device(p.t, p.scales)
     x = x_to_device(p)
     sg = signs_to_device(p.signs)
-    y = tb.tb_ternary_gemm(x, sg, 1024, codes, s, b)
+    ws = T.empty(tb.tb_ternary_gemm_workspace_size_n(p.B, p.K, p.N), dtype=T.uint8, device="cuda")
+    y = tb.tb_ternary_gemm(x, sg, 1024, codes, s, b, workspace=ws)
     T.cuda.synchronize()
-    rows = np.unique(np.concatenate([[0, 1, 127, 128, 1023, 2047],
-                                     np.random.default_rng(44).integers(0, 2048, 26)]))
+    got = y.cpu().numpy()
     oc, osc, ob = oracle_pack(p)
-    want = oracle.packed_linear(p.x64[rows], p.signs, 1024, oc, osc, ob)
-    got = y[T.from_numpy(rows).cuda()].cpu().numpy()
-    compare(got, want, "prefill sampled rows")
+    want = oracle.packed_linear(p.x64, p.signs, 1024, oc, osc, ob)
+    compare(got, want, "prefill all outputs")
+    # and per 64 x 512 output tile (whole tiles and the tail's K-sliced tiles)
+    tile_err = np.abs(got - want).reshape(p.B // 64, 64, -1).max(axis=1)
+    assert np.isfinite(tile_err).all()
+    assert tile_err.max() <= 1e-3 * np.abs(want).max()
 
 
 # --------------------------------------------------------------------------
@@ -84,6 +90,8 @@ def test_prefill_gemm_sampled_rows():
 RAGGED = [
     # (N, K, B, block, xdtype)
     (1, 1024, 1, 1024, "bf16"),
+    (4352, 384, 1, 0, "bf16"),    # G = 3 odd: band rows rounded to a multiple of 8 (17 -> 24)
+    (4099, 1152, 1, 0, "f32"),    # G = 9 odd, ragged last band
     (17, 2048, 3, 512, "f32"),
     (1000, 6144, 2, 2048, "bf16"),
     (100, 8192, 5, 4096, "bf16"),
@@ -104,6 +112,8 @@ def test_gemv_ragged(N, K, B, block, xd):
 
 GEMM_CASES = [
     (200, 300, 2048, 1024, "bf16"),
+    (100, 260, 4096, 2048, "bf16"),
+    (33, 70, 2048, 2048, "f32"),
     (1, 77, 1024, 512, "f32"),
     (129, 129, 4096, 4096, "bf16"),
     (64, 256, 384, 0, "f32"),
@@ -651,3 +661,92 @@ def test_gemv_batch_with_small_workspace_takes_another_path():
     compare(y_small.cpu().numpy(), oracle.packed_linear(p.x64, p.signs, 1024, oc, osc, ob), "small workspace")
     d = (y_small.double() - y_full.double()).abs().max().item()
     assert d <= 1e-6 * y_full.abs().max().item(), d
+
+
+# --------------------------------------------------------------------------
+# scale / bias views at a 4-byte (not 16-byte) offset
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("N,K,B", [(6144, 5120, 1), (5120, 17408, 1), (700, 5120, 4), (300, 1152, 3)])
+def test_gemv_scales_biases_at_dword_offset(N, K, B):
+    """Scales and biases that start 4 bytes into their buffers (dword- but not
+    16-byte aligned) give the same result as aligned ones on every GEMV path
+    (band, fused, batch, prepare/run)."""
+    announce(f"gemv scales/biases at +4 bytes N={N} K={K} B={B}")
+    T = torch()
+    p = synth.make_problem("offset_sb", N, K, B, [N, K, B, 77], "bf16", 1024 if K % 1024 == 0 else 0)
+    codes, s, b = pack_to_device(p.t, p.scales)
+    x, sg = x_to_device(p), signs_to_device(p.signs)
+
+    def shifted(t):
+        buf = T.empty(t.numel() + 2, dtype=t.dtype, device="cuda")
+        v = buf[2:].view(t.shape)
+        v.copy_(t)
+        assert v.data_ptr() % 16 == 4
+        return v
+
+    s4, b4 = shifted(s), shifted(b)
+    y_al = tb.tb_ternary_gemv(x, sg, p.block, codes, s, b)
+    y_off = tb.tb_ternary_gemv(x, sg, p.block, codes, s4, b4)
+    T.cuda.synchronize()
+    d = (y_al.double() - y_off.double()).abs().max().item()
+    assert d <= 1e-6 * y_al.abs().max().item(), d
+    oc, osc, ob = oracle_pack(p)
+    compare(y_off.cpu().numpy(), oracle.packed_linear(p.x64, p.signs, p.block, oc, osc, ob), "offset views")
+
+
+# --------------------------------------------------------------------------
+# other contract block sizes on the embedding path; calls past 65535 rows
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("block", [512, 2048, 4096])
+def test_embed_inverse_other_blocks(block):
+    announce(f"embed V=300 K=8192 block={block}")
+    T = torch()
+    V, K = 300, 8192
+    rng = np.random.default_rng(100 + block)
+    t = synth.draw_ternary(rng, V, K)
+    sc = synth.draw_scales(rng, V, K)
+    sig = synth.draw_signs(rng, K)
+    codes, s, b = pack_to_device(t, sc)
+    ids = np.array([0, V - 1, 5, 5, -3, V, 150], np.int32)
+    out = tb.tb_embed_inverse(T.from_numpy(ids).cuda(), codes, s, b, signs_to_device(sig), block)
+    T.cuda.synchronize()
+    oc, osc, ob = oracle.pack(t, sc)
+    want = oracle.embed_inverse(ids, oc, osc, ob, sig, block)
+    got = out.cpu().numpy()
+    ok = (ids >= 0) & (ids < V)
+    assert np.isnan(got[~ok]).all()
+    compare(got[ok], want[ok], f"embed block {block}")
+
+
+def test_fold_and_embed_past_65535_rows():
+    """The transform and the embedding put rows in the grid's y dimension
+    (65535 at most per launch); a call of 70,000 rows is launched in chunks.
+    Rows on both sides of each chunk boundary, the last row, and drawn rows
+    against the oracle."""
+    announce("fwht 70000 x 1024 (fold) and embed of 70000 ids")
+    T = torch()
+    R, K = 70000, 1024
+    rng = np.random.default_rng(65536)
+    sig = synth.draw_signs(rng, K)
+    sd = signs_to_device(sig)
+    g = T.Generator(device="cuda")
+    g.manual_seed(65536)
+    W = T.randn((R, K), generator=g, device="cuda")
+    Ws = tb.tb_fwht_signed(W, sd, 1024)
+    T.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, 65534, 65535, 65536, R - 1], rng.integers(0, R, 58)]))
+    rt = T.from_numpy(rows).cuda()
+    compare(Ws[rt].cpu().numpy(), oracle.fold_rotation(W[rt].cpu().numpy(), sig, 1024), "fold 70000 rows")
+    V = 2000
+    t = synth.draw_ternary(rng, V, 2048)
+    sc = synth.draw_scales(rng, V, 2048)
+    sig2 = synth.draw_signs(rng, 2048)
+    codes, s, b = pack_to_device(t, sc)
+    ids = rng.integers(0, V, R).astype(np.int32)
+    ids[65535] = V - 1
+    ids[R - 1] = 0
+    out = tb.tb_embed_inverse(T.from_numpy(ids).cuda(), codes, s, b, signs_to_device(sig2), 2048)
+    T.cuda.synchronize()
+    oc, osc, ob = oracle.pack(t, sc)
+    want = oracle.embed_inverse(ids[rows], oc, osc, ob, sig2, 2048)
+    compare(out[rt].cpu().numpy(), want, "embed 70000 ids")

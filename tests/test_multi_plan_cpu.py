@@ -122,3 +122,53 @@ def test_run_refuses_foreign_plan():
     junk = np.zeros(256, np.uint8)
     st = tb.lib().tb_ternary_gemv_multi(junk.ctypes.data, FAKE, FAKE, 1 << 20, None)
     assert st == -1
+
+
+def _mods_shared(spec, block=1024):
+    """spec: (N, K, input id) per module; modules with the same input id get
+    the same fake x and sign pointers."""
+    arr = (tb.TbGemvModule * len(spec))()
+    for i, (N, K, inp) in enumerate(spec):
+        xb = FAKE * (64 * inp + 1)
+        wb = FAKE * (64 * i + 1000)
+        arr[i] = tb.TbGemvModule(xb, xb + FAKE if block else None, wb, wb + FAKE, wb + 2 * FAKE, wb + 3 * FAKE, N, K)
+    return arr
+
+
+def _plan_arr(arr, n, block=1024):
+    size = tb.lib().tb_gemv_multi_plan_size(arr, n)
+    plan = np.zeros(max(size, 64), np.uint8)
+    ws = ctypes.c_size_t(0)
+    st = tb.lib().tb_gemv_multi_plan(arr, n, tb.TB_BF16, block, plan.ctypes.data, plan.nbytes, ctypes.byref(ws))
+    assert st == tb.TB_OK, tb.lib().tb_last_error()
+    return _parse(plan), ws.value
+
+
+def test_modules_reading_one_input_share_transform_and_image():
+    # one full-attention layer + MLP: q/k/v read input 0, o_proj input 1,
+    # gate/up input 2, down_proj input 3 (as a decode layer feeds them)
+    spec = [(6144, 5120, 0), (1024, 5120, 0), (1024, 5120, 0), (5120, 6144, 1),
+            (17408, 5120, 2), (17408, 5120, 2), (5120, 17408, 3)]
+    p, ws = _plan_arr(_mods_shared(spec), len(spec))
+    # tasks: one set per distinct input (5 + 6 + 5 + 17 chunks), owned by the
+    # first module that reads it
+    assert p["tasks"] == 5 + 6 + 5 + 17
+    assert sorted({int(m) for m in p["tk"][:, 0]}) == [0, 3, 4, 6]
+    off = p["NK"][:, 3]
+    assert off[0] == off[1] == off[2] and off[4] == off[5]
+    assert len({off[0], off[3], off[4], off[6]}) == 4
+    # the same modules with distinct inputs need one image each
+    p2, ws2 = _plan_arr(_mods_shared([(N, K, i) for i, (N, K, _) in enumerate(spec)]), len(spec))
+    assert p2["tasks"] == 5 + 5 + 5 + 6 + 5 + 5 + 17
+    img = lambda K: (K + 1023) // 1024 * (8 * 4 * 128 + 64)
+    assert ws2 - ws == 2 * img(5120) + img(5120)
+
+
+def test_same_x_different_signs_or_width_is_not_shared():
+    arr = _mods_shared([(256, 5120, 0), (256, 5120, 0)])
+    arr[1].signs = arr[1].signs + 16 * FAKE   # same x, another sign vector
+    p, _ = _plan_arr(arr, 2)
+    assert p["tasks"] == 10 and p["NK"][0, 3] != p["NK"][1, 3]
+    arr = _mods_shared([(256, 5120, 0), (256, 4096, 0)])  # same pointers, another width
+    p, _ = _plan_arr(arr, 2)
+    assert p["tasks"] == 9 and p["NK"][0, 3] != p["NK"][1, 3]
