@@ -44,6 +44,7 @@ _SIGNATURES = {
     "tb_ternary_gemv_workspace_size": (_SZ, [_I64, _I64]),
     "tb_ternary_gemv_workspace_size_n": (_SZ, [_I64, _I64, _I64]),
     "tb_ternary_gemv": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
+    "tb_ternary_gemv_noalloc": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _P, _P, _I64, _P, _P]),
     "tb_ternary_gemv_prepare": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _SZ, _P]),
     "tb_ternary_gemv_run": (_I, [_P, _SZ, _I64, _I64, _P, _P, _P, _I64, _P, _P]),
     "tb_ternary_gemm_workspace_size": (_SZ, [_I64, _I64]),
@@ -290,6 +291,29 @@ def tb_ternary_gemv(x, signs, block: int, codes, scales, biases, out=None, works
     _check(lib().tb_ternary_gemv(x.data_ptr(), _xdtype(x), B, K, _ptr(signs), block, codes.data_ptr(),
                                  scales.data_ptr(), biases.data_ptr(), N, out.data_ptr(),
                                  workspace.data_ptr(), workspace.numel(), _stream()))
+    return out
+
+
+def tb_ternary_gemv_noalloc(x, signs, block: int, codes, scales, biases, out=None):
+    """tb_ternary_gemv with the library's static device scratch as its
+    workspace (no device allocation by the library; `out` is allocated here
+    only when the caller passes none)."""
+    torch = _torch()
+    B, K = _rows(x)
+    N = int(codes.shape[0])
+    _container_shapes(codes, scales, biases, N, K)
+    _signs_shape(signs, K, block)
+    if out is not None:
+        _shape(out, (B, N), "out")
+    _dev(x, "x")
+    _container(codes, scales, biases)
+    if signs is not None:
+        _dev(signs, "signs", torch.int8)
+    if out is None:
+        out = torch.empty((B, N), dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    _check(lib().tb_ternary_gemv_noalloc(x.data_ptr(), _xdtype(x), B, K, _ptr(signs), block, codes.data_ptr(),
+                                         scales.data_ptr(), biases.data_ptr(), N, out.data_ptr(), _stream()))
     return out
 
 

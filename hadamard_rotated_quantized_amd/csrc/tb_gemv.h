@@ -185,6 +185,15 @@ void gemv_band_launch(const void* x, int x_dtype, int64_t K, const int8_t* signs
                       const uint16_t* scales, const uint16_t* biases, int64_t N, float* y, hipStream_t st);
 
 bool gemv_fused_eligible(int64_t B, int64_t K, int64_t N, int block);
+
+// tb_ternary_gemv's argument checks (everything but the workspace) and its
+// path choice and launches, for entry points that bring their own workspace
+int gemv_checked_args(const void* x, int x_dtype, int64_t B, int64_t K, const int8_t* signs, int block,
+                      const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, int64_t N,
+                      const float* y, const char* who);
+int gemv_dispatch(const void* x, int x_dtype, int64_t B, int64_t K, const int8_t* signs, int block,
+                  const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, int64_t N, float* y,
+                  void* workspace, size_t ws_bytes, hipStream_t st, const char* who);
 void gemv_fused_launch(const void* x, int x_dtype, int64_t B, int64_t K, const int8_t* signs, int block,
                        const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, int64_t N,
                        float* y, hipStream_t st);

@@ -689,18 +689,25 @@ extern "C" int tb_ternary_gemv_run(const void* workspace, size_t ws_bytes, int64
   return TB_OK;
 }
 
-extern "C" int tb_ternary_gemv(const void* x, int x_dtype, int64_t B, int64_t K,
-                               const int8_t* signs, int block, const uint32_t* codes,
-                               const uint16_t* scales, const uint16_t* biases, int64_t N, float* y,
-                               void* workspace, size_t ws_bytes, void* stream) {
-  const char* who = "tb_ternary_gemv";
+namespace tb {
+
+// Host checks of tb_ternary_gemv's arguments other than the workspace.
+int gemv_checked_args(const void* x, int x_dtype, int64_t B, int64_t K, const int8_t* signs, int block,
+                           const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, int64_t N,
+                           const float* y, const char* who) {
   TB_TRY(gemv_common_checks(B, K, N, who));
   TB_TRY(check_rotation(K, block, signs, who));
   if (B == 0 || N == 0) return TB_OK;
   TB_TRY(check_dtype(x_dtype, x, who));
   TB_TRY(prep_align_checks(x, signs, who));
   TB_TRY(run_checks(N, K, codes, scales, biases, y, who));
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  return TB_OK;
+}
+
+// The path choice and launches of tb_ternary_gemv, after gemv_checked_args.
+int gemv_dispatch(const void* x, int x_dtype, int64_t B, int64_t K, const int8_t* signs, int block,
+                  const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, int64_t N, float* y,
+                  void* workspace, size_t ws_bytes, hipStream_t st, const char* who) {
   const size_t batch_ws = gemv_batch_eligible(B, K, N, block) ? gemv_batch_workspace(B, K, N) : 0;
   if (gemv_batch_eligible(B, K, N, block) &&
       (batch_ws == 0 || (workspace && aligned(workspace, 16) && ws_bytes >= batch_ws))) {
@@ -725,4 +732,17 @@ extern "C" int tb_ternary_gemv(const void* x, int x_dtype, int64_t B, int64_t K,
   gemv_run_launch(workspace, B, K, codes, scales, biases, N, y, st);
   TB_LAUNCH_CHECK(who);
   return TB_OK;
+}
+
+}  // namespace tb
+
+extern "C" int tb_ternary_gemv(const void* x, int x_dtype, int64_t B, int64_t K,
+                               const int8_t* signs, int block, const uint32_t* codes,
+                               const uint16_t* scales, const uint16_t* biases, int64_t N, float* y,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  const char* who = "tb_ternary_gemv";
+  TB_TRY(gemv_checked_args(x, x_dtype, B, K, signs, block, codes, scales, biases, N, y, who));
+  if (B == 0 || N == 0) return TB_OK;
+  return gemv_dispatch(x, x_dtype, B, K, signs, block, codes, scales, biases, N, y, workspace, ws_bytes,
+                       static_cast<hipStream_t>(stream), who);
 }

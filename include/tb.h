@@ -167,6 +167,28 @@ int tb_ternary_gemv(const void* x, int x_dtype, int64_t B, int64_t K,
                     const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
                     int64_t N, float* y, void* workspace, size_t ws_bytes, void* stream);
 
+/* Bytes of device scratch tb_ternary_gemv_noalloc holds per GPU. */
+#define TB_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* tb_ternary_gemv for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, result and kernels as tb_ternary_gemv, without the
+ * workspace: the library keeps TB_NOALLOC_SCRATCH_BYTES of static device
+ * memory per GPU (held until the process ends) and uses it as the workspace.
+ * It calls no allocator.  The decode-batch path runs when its partial rows
+ * fit there (every N up to 248,320 at K = 5120 and B = 8 does); otherwise
+ * the other batch path.  A call whose smallest workspace,
+ * tb_ternary_gemv_workspace_size(B, K), exceeds the scratch returns
+ * TB_ERR_WORKSPACE before enqueuing anything; TB_ERR_HIP if the scratch's
+ * device address cannot be obtained.  Every call on one GPU shares that
+ * GPU's scratch, and no call needs it cleared: calls that may overlap on
+ * one GPU (concurrent streams, threads) race and must be serialized by the
+ * caller. */
+int tb_ternary_gemv_noalloc(const void* x, int x_dtype, int64_t B, int64_t K,
+                            const int8_t* signs, int block,
+                            const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                            int64_t N, float* y, void* stream);
+
 /* First half of tb_ternary_gemv: rotate x (R x, signs then the normalized
  * block transform) and store it in the workspace as exact integer limbs in
  * the matmul kernel's operand layout (format private to the library).  One
