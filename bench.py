@@ -5,19 +5,22 @@ K = 5120, N = 6144, batch 1, bf16 activations, 2.25-bit packed weights.
 One step = one full pass of the path over one input vector: the signed
 1024-block transform of x, its exact split into integer limbs, and the
 weight-streaming ternary matmul -- one tb_ternary_gemv call, which runs as a
-single kernel launch at this shape.  Steps
-rotate over enough distinct copies of the packed weights (>= 1 GiB in
-total) that the 256 MB last-level cache cannot serve a repeat, so every
-step streams its weights from HBM.
+single kernel launch at this shape.  Steps rotate over enough distinct
+copies of the packed weights (>= 1 GiB in total) that the 256 MB last-level
+cache cannot serve a repeat, so every step streams its weights from HBM.
 
 Prints ONE JSON line.  `value` is effective weight GB/s of the whole step
 (N*K*9/32 bytes of codes, scales and biases per step, over the HIP-event
 time of the timed region); `roofline` prices that kernel against the 8 TB/s
 HBM peak, its average launch duration taken from HIP events around the
 back-to-back launches of the timed region; `cpu_baseline` times the fp64
-oracle on the host on the same workload.
+oracle on the host on the same workload.  The default line also carries
+`detail.sweep`: the full batch-1 decode step of the 64-layer model (401
+packed linears in one multi-module plan + one embedding lookup), its rate,
+roofline, per-layer times and its own oracle baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload q_proj]
+                    [--workload down_proj --batch B | prefill_gate_up | sweep | tiny]
 """
 from __future__ import annotations
 
@@ -48,14 +51,71 @@ def log(msg):
 # it includes, the build flags).
 _CSRC = os.path.join(ROOT, "hadamard_rotated_quantized_amd", "csrc")
 _BUILD = os.path.join(ROOT, "hadamard_rotated_quantized_amd", "build.py")
+def _srcs(*names):
+    return [os.path.join(_CSRC, f) for f in names + ("tb_gemv.h", "tb_device.h", "tb_common.h")] + [_BUILD]
+
+
 COUNTER_SUMMARIES = {
     "q_proj": (os.path.join(ROOT, "profiles", "gemv_band_kernel_q_proj_counters.txt"),
-               [os.path.join(_CSRC, f) for f in ("tb_gemv_band.hip", "tb_xform.h", "tb_gemv.h", "tb_device.h",
-                                                  "tb_common.h")] + [_BUILD]),
+               _srcs("tb_gemv_band.hip", "tb_xform.h")),
     "prefill_gate_up": (os.path.join(ROOT, "profiles", "gemm_mx_kernel_prefill_gate_up_counters.txt"),
-                        [os.path.join(_CSRC, f) for f in ("tb_gemm.hip", "tb_xform.h", "tb_gemv.h", "tb_device.h",
-                                                           "tb_common.h")] + [_BUILD]),
+                        _srcs("tb_gemm.hip", "tb_xform.h")),
+    "sweep": (os.path.join(ROOT, "profiles", "multi_stream_kernel_sweep_counters.txt"),
+              _srcs("tb_gemv_multi.hip", "tb_xform.h")),
+    "down_proj_b1": (os.path.join(ROOT, "profiles", "gemv_fused_kernel_down_proj_b1_counters.txt"),
+                     _srcs("tb_gemv_fused.hip")),
+    "down_proj_b8": (os.path.join(ROOT, "profiles", "batch_stream_kernel_down_proj_b8_counters.txt"),
+                     _srcs("tb_gemv_batch.hip", "tb_xform.h")),
 }
+
+
+def counter_key(workload, batch=None):
+    """Key of the counter summary of a workload's dominant kernel."""
+    if workload == "down_proj":
+        return f"down_proj_b{batch or 1}"
+    return workload
+
+
+def host_info():
+    """(cores this process may use, CPU model, BLAS library, BLAS threads)."""
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = "unknown", None
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas = f"{i.get('internal_api')} {i.get('version')}"
+                threads = i.get("num_threads")
+                break
+    except Exception:
+        pass
+    return cores, model, blas, threads
+
+
+def _oracle_threads(cores):
+    """Context that runs the oracle's BLAS on `cores` threads (no-op without
+    threadpoolctl)."""
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=cores, user_api="blas")
+    except Exception:
+        import contextlib
+        return contextlib.nullcontext()
+
+
+def cpu_baseline_record(value, unit, sample):
+    cores, model, blas, threads = host_info()
+    return {"value": value, "unit": unit, "cores": cores, "kind": "oracle", "sample": sample,
+            "cpu_model": model, "blas": f"{blas}, {threads} threads"}
 
 
 def kernel_source_hash(workload="q_proj"):
@@ -91,24 +151,235 @@ def measured_traffic(workload):
 
 
 def cpu_baseline_gemv(p, codes, scales, biases, budget_s=12.0):
-    """Time the fp64 oracle on the same workload (bounded number of calls)."""
+    """Time the fp64 oracle on the same workload (bounded number of calls),
+    its BLAS on every core this process may use."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        blas_threads = 1
-    t0 = time.perf_counter()
-    oracle.packed_linear(p.x64, p.signs, p.block, codes, scales, biases)
-    one = time.perf_counter() - t0
-    reps = max(1, min(20, int(budget_s / max(one, 1e-3))))
-    t0 = time.perf_counter()
-    for _ in range(reps):
+    cores = len(os.sched_getaffinity(0))
+    with _oracle_threads(cores):
+        t0 = time.perf_counter()
         oracle.packed_linear(p.x64, p.signs, p.block, codes, scales, biases)
-    per = (time.perf_counter() - t0) / reps
-    return per, reps + 1, blas_threads
+        one = time.perf_counter() - t0
+        reps = max(1, min(20, int(budget_s / max(one, 1e-3))))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.packed_linear(p.x64, p.signs, p.block, codes, scales, biases)
+        per = (time.perf_counter() - t0) / reps
+    return per, reps + 1
 
 
+GEMV_DTYPE = ("int8 MFMA on exact limbs of the rotated activation (4 x 8 bits, ~30-bit fixed point) x 2-bit codes, "
+              "int32 accumulate, fp32 scale/bias epilogue")
+
+
+def _time_graph(torch, g, n_replays, spacer=None):
+    """Seconds for n_replays back-to-back replays of graph g, from HIP events
+    on the stream.  With a spacer graph, one untimed replay of it is enqueued
+    first, so the timed replays are already queued behind it when the start
+    event fires and the graph's launch latency stays out of the region."""
+    torch.cuda.synchronize()
+    if spacer is not None:
+        spacer.replay()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n_replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3
+
+
+def _parity(got, want):
+    got = np.asarray(got, dtype=np.float64)
+    rel = float(np.linalg.norm(got - want) / np.linalg.norm(want))
+    mabs = float(np.abs(got - want).max() / np.abs(want).max())
+    return rel, mabs
+
+
+def _device_problem(p, dev):
+    import torch
+    import hadamard_rotated_quantized_amd as tb
+    codes, s, b = tb.tb_pack(p.t, p.scales)
+    c0 = torch.from_numpy(codes.view(np.int32)).to(dev)
+    s0 = torch.from_numpy(s).to(dev)
+    b0 = torch.from_numpy(b).to(dev)
+    x = (torch.from_numpy(p.x_store.view(np.int16)).view(torch.bfloat16) if p.xdtype == "bf16"
+         else torch.from_numpy(p.x_store)).to(dev)
+    sg = torch.from_numpy(p.signs).to(dev) if p.signs is not None else None
+    return c0, s0, b0, x, sg
+
+
+# ---------------------------------------------------------------------------
+# the 402-module decode sweep
+# ---------------------------------------------------------------------------
+def sweep_setup(dev, check_rows=512, lm_head_rows=2048):
+    """Draw and pack every sweep module on the device (one activation per
+    input site, shared as a layer shares it), keep the host copies of the
+    rows the oracle checks (first module of each shape), and build the plan
+    of the 401 linears."""
+    import torch
+
+    import hadamard_rotated_quantized_amd as tb
+    from hadamard_rotated_quantized_amd import synth
+
+    mods = synth.sweep_modules()
+    sites = synth.sweep_input_sites()
+    signs_h = synth.sweep_signs()
+    signs = {K: torch.from_numpy(v).to(dev) for K, v in signs_h.items()}
+    xs = {}
+    for si, m in zip(sites, mods):
+        if si >= 0 and si not in xs:
+            xs[si] = synth.device_site_x(si, m[2], dev)
+    packs, ys, checks, seen = [], [], {}, set()
+    t0 = time.perf_counter()
+    for i, (name, N, K, kind) in enumerate(mods):
+        t, sc, _ = synth.device_module_draw(i, N, K, 1, dev)
+        packs.append(tb.tb_pack_device(t, sc, check=False))
+        if (N, K, kind) not in seen:
+            seen.add((N, K, kind))
+            rng = np.random.default_rng([synth.SWEEP_SEED, i])
+            if kind == "embedding":
+                rows = np.array([int(np.random.default_rng(synth.SWEEP_SEED).integers(0, N)), 0, N - 1])
+            else:
+                n = lm_head_rows if N == synth.VOCAB else check_rows
+                rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, min(N, n) - 2, replace=False)]))
+            rt = torch.from_numpy(rows).to(dev)
+            checks[i] = (rows, t[rt].cpu().numpy(), sc[rt].cpu().numpy())
+        del t, sc
+        ys.append(torch.empty((1, N) if kind == "linear" else (3, K), dtype=torch.float32, device=dev))
+    torch.cuda.synchronize()
+    log(f"sweep: drew and packed {len(mods)} modules on the device in {time.perf_counter() - t0:.1f} s")
+    lin = [i for i, m in enumerate(mods) if m[3] == "linear"]
+    emb = [i for i, m in enumerate(mods) if m[3] == "embedding"]
+    emb_ids = torch.from_numpy(checks[emb[0]][0].astype(np.int32)).to(dev)
+
+    def plan_of(idx):
+        plan, wsb = tb.tb_gemv_multi_plan([(xs[sites[i]], signs[mods[i][2]], *packs[i], ys[i]) for i in idx], 1024)
+        return plan, torch.from_numpy(plan).to(dev), torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+    return dict(mods=mods, sites=sites, signs=signs, signs_h=signs_h, xs=xs, packs=packs, ys=ys, checks=checks,
+                lin=lin, emb=emb, emb_ids=emb_ids, plan=plan_of(lin), plan_of=plan_of)
+
+
+def sweep_measure(n_steps, with_cpu, with_context):
+    """Time the sweep step (multi-module path for the 401 linears + the
+    embedding lookup of one token) and report it; parity of one module of
+    every shape against the oracle first."""
+    import torch
+
+    import hadamard_rotated_quantized_amd as tb
+    import oracle
+
+    dev = torch.device("cuda:0")
+    sw = sweep_setup(dev)
+    mods, ys, packs, signs = sw["mods"], sw["ys"], sw["packs"], sw["signs"]
+    plan, plan_dev, mws = sw["plan"]
+
+    def step(ids=sw["emb_ids"][:1]):
+        """One decode token: every linear, and the embedding lookup of one id."""
+        tb.tb_ternary_gemv_multi(plan, plan_dev, mws)
+        for i in sw["emb"]:
+            tb.tb_embed_inverse(ids, *packs[i], signs[mods[i][2]], 1024, out=ys[i][:ids.numel()])
+
+    step(sw["emb_ids"])  # the parity run looks up the drawn id and the first and last rows
+    torch.cuda.synchronize()
+    checked, worst = [], 0.0
+    cpu_s = {}  # oracle seconds per checked row, by shape
+    for i, (rows, t_rows, sc_rows) in sw["checks"].items():
+        name, N, K, kind = mods[i]
+        oc, osc, ob = oracle.pack(t_rows, sc_rows)
+        t0 = time.perf_counter()
+        if kind == "linear":
+            x64 = sw["xs"][sw["sites"][i]].float().cpu().numpy().astype(np.float64)
+            want = oracle.packed_linear(x64, sw["signs_h"][K], 1024, oc, osc, ob)
+            got = ys[i][:, torch.from_numpy(rows).to(dev)].cpu().numpy()
+        else:
+            want = oracle.embed_inverse(np.arange(rows.size), oc, osc, ob, sw["signs_h"][K], 1024)
+            got = ys[i].cpu().numpy()
+        cpu_s[(N, K, kind)] = (time.perf_counter() - t0) / rows.size
+        rel, mabs = _parity(got, want)
+        worst = max(worst, rel)
+        checked.append(f"{name.split('.')[-1]}:{rel:.1e}")
+        if not (rel <= 1e-4 and mabs <= 1e-3):
+            raise SystemExit(f"sweep parity check failed on {name}: rel {rel:.2e} max-abs {mabs:.2e}")
+    log("sweep parity " + ", ".join(checked))
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    g.replay()
+    nrep = max(3, min(n_steps, 50))
+    sec = _time_graph(torch, g, nrep, spacer=g) / nrep
+    wbytes = sum(N * K * 9 // 32 for (_, N, K, kind) in mods if kind == "linear")
+    value = wbytes / sec / 1e9
+
+    # per layer type and lm_head: plans of only those modules, timed alike
+    def layer_plan_us(idx, reps):
+        pl, pd, ws = sw["plan_of"](idx)
+        gl = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gl):
+            tb.tb_ternary_gemv_multi(pl, pd, ws)
+        gl.replay()
+        return _time_graph(torch, gl, reps, spacer=gl) / reps * 1e6
+
+    layer_of = lambda m: int(m[0].split(".")[1]) if m[0].startswith("layers.") else -1
+    lin_layers = [i for i in sw["lin"] if layer_of(mods[i]) >= 0 and layer_of(mods[i]) % 4 != 3]
+    full_layers = [i for i in sw["lin"] if layer_of(mods[i]) >= 0 and layer_of(mods[i]) % 4 == 3]
+    lm = [i for i in sw["lin"] if mods[i][0] == "lm_head"]
+    lin_us = layer_plan_us(lin_layers, 10) / 48
+    full_us = layer_plan_us(full_layers, 10) / 16
+    lm_us = layer_plan_us(lm, 20)
+    lbytes = lambda idx: sum(mods[i][1] * mods[i][2] * 9 // 32 for i in idx)
+    out = {"workload": "batch-1 decode sweep: 401 packed linears of a 64-layer hidden-5120 model (48 linear-"
+                       "attention + 16 full-attention layers, MLP 17408, lm_head 248320) in one multi-module plan "
+                       "(transform launch + persistent streaming launch) + one embedding lookup",
+           "modules": len(mods), "weight_bytes": wbytes, "steps": nrep,
+           "ms_per_step": round(sec * 1e3, 4), "GB/s": round(value, 1), "frac": round(value / HBM_PEAK_GBS, 4),
+           "us_per_linear_attention_layer_with_mlp": round(lin_us, 2),
+           "us_per_full_attention_layer_with_mlp": round(full_us, 2),
+           "lm_head_us": round(lm_us, 2),
+           "layer_GBps": {"linear_attention+mlp": round(lbytes(lin_layers) / 48 / (lin_us * 1e-6) / 1e9, 1),
+                          "full_attention+mlp": round(lbytes(full_layers) / 16 / (full_us * 1e-6) / 1e9, 1),
+                          "lm_head": round(lbytes(lm) / (lm_us * 1e-6) / 1e9, 1)},
+           "layer_timing": "each from a plan of only those modules (all 48 linear-attention layers with their MLPs, "
+                           "all 16 full-attention layers with theirs, lm_head alone), HIP graphs, divided by the "
+                           "layer count",
+           "roofline": {"bound": "hbm", "kernel": "multi_stream_kernel", "achieved": round(value, 2),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4),
+                        "traffic": measured_traffic("sweep")},
+           "parity_worst_rel_l2": worst, "parity": checked}
+    if with_cpu:
+        # the oracle per row of each shape (timed above on the checked rows),
+        # scaled to every row of every module of the sweep
+        est = sum(cpu_s[(N, K, kind)] * (N if kind == "linear" else 1) for (_, N, K, kind) in mods)
+        nrows = sum(r[0].size for r in sw["checks"].values())
+        spent = sum(cpu_s[tuple(mods[i][1:])] * r[0].size for i, r in sw["checks"].items())
+        out["cpu_baseline"] = cpu_baseline_record(
+            round(wbytes / est / 1e9, 4), "GB/s",
+            f"fp64 oracle on {nrows} rows (one module of each of the {len(cpu_s)} shapes, the rows the parity "
+            f"check reads), {spent:.1f} s; scaled per row to every row of the sweep: {est:.0f} s per step")
+    if with_context:
+        def call(i):
+            name, N, K, kind = mods[i]
+            if kind == "linear":
+                tb.tb_ternary_gemv(sw["xs"][sw["sites"][i]], signs[K], 1024, *packs[i], out=ys[i])
+            else:
+                tb.tb_embed_inverse(sw["emb_ids"], *packs[i], signs[K], 1024, out=ys[i])
+        gsep = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gsep):
+            for i in range(len(mods)):
+                call(i)
+        gsep.replay()
+        r = max(3, min(n_steps, 20))
+        sep = _time_graph(torch, gsep, r, spacer=gsep) / r
+        out["separate_calls_ms"] = round(sep * 1e3, 4)
+        out["separate_calls_GBps"] = round(wbytes / sep / 1e9, 1)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# counter passes (rocprofv3 --pmc)
+# ---------------------------------------------------------------------------
 def run_counter_pass(args):
     """Eager launches only, no timing: the command that rocprofv3 --pmc passes
     wrap.  `--workload copy` runs plain device copies of a known size (the
@@ -128,14 +399,17 @@ def run_counter_pass(args):
     import hadamard_rotated_quantized_amd as tb
     from hadamard_rotated_quantized_amd import synth
 
-    p = synth.config_problem(args.workload)
-    codes, s, b = tb.tb_pack(p.t, p.scales)
+    if args.workload == "sweep":
+        sw = sweep_setup(dev, check_rows=2, lm_head_rows=2)
+        plan, pd, ws = sw["plan"]
+        for _ in range(3):
+            tb.tb_ternary_gemv_multi(plan, pd, ws)
+        torch.cuda.synchronize()
+        print(json.dumps({"counter_pass": "sweep", "launches": 3}), flush=True)
+        return
+    p = synth.config_problem(args.workload, args.batch)
+    c0, s0, b0, x, sg = _device_problem(p, dev)
     if args.workload == "prefill_gate_up":
-        c0 = torch.from_numpy(codes.view(np.int32)).to(dev)
-        s0 = torch.from_numpy(s).to(dev)
-        b0 = torch.from_numpy(b).to(dev)
-        x = torch.from_numpy(p.x_store.view(np.int16)).view(torch.bfloat16).to(dev)
-        sg = torch.from_numpy(p.signs).to(dev)
         ws = torch.empty(tb.tb_ternary_gemm_workspace_size_n(p.B, p.K, p.N), dtype=torch.uint8, device=dev)
         y = torch.empty((p.B, p.N), dtype=torch.float32, device=dev)
         for _ in range(5):
@@ -143,25 +417,23 @@ def run_counter_pass(args):
         torch.cuda.synchronize()
         print(json.dumps({"counter_pass": args.workload, "launches": 5}), flush=True)
         return
-    c0 = torch.from_numpy(codes.view(np.int32)).to(dev)
-    s0 = torch.from_numpy(s).to(dev)
-    b0 = torch.from_numpy(b).to(dev)
     R = args.replicas or max(1, math.ceil((1 << 30) / (p.N * p.K * 9 // 32)))
     reps = [(c0, s0, b0)] + [(c0.clone(), s0.clone(), b0.clone()) for _ in range(R - 1)]
-    x = (torch.from_numpy(p.x_store.view(np.int16)).view(torch.bfloat16) if p.xdtype == "bf16"
-         else torch.from_numpy(p.x_store)).to(dev)
-    sg = torch.from_numpy(p.signs).to(dev)
     ws = torch.empty(tb.tb_ternary_gemv_workspace_size_n(p.B, p.K, p.N), dtype=torch.uint8, device=dev)
     y = torch.empty((p.B, p.N), dtype=torch.float32, device=dev)
     for i in range(3 * R):
         tb.tb_ternary_gemv(x, sg, p.block, *reps[i % R], out=y, workspace=ws)
     torch.cuda.synchronize()
-    print(json.dumps({"counter_pass": args.workload, "launches": 3 * R, "replicas": R,
+    print(json.dumps({"counter_pass": args.workload, "batch": p.B, "launches": 3 * R, "replicas": R,
                       "weight_bytes": p.N * p.K * 9 // 32}), flush=True)
 
 
+# ---------------------------------------------------------------------------
+# decode GEMV workloads (the headline)
+# ---------------------------------------------------------------------------
 def run_gemv(args):
-    """Decode GEMV workloads: q_proj (default), tiny, down_proj (--batch 1..8)."""
+    """Decode GEMV workloads: q_proj (default), tiny, down_proj (--batch 1..8).
+    The default run also measures the 402-module decode sweep (detail.sweep)."""
     import torch
 
     import hadamard_rotated_quantized_amd as tb
@@ -172,16 +444,10 @@ def run_gemv(args):
     N, K, B = p.N, p.K, p.B
     wbytes = N * K * 9 // 32
     log(f"workload {args.workload}: N={N} K={K} B={B} weight bytes {wbytes}")
-    codes, s, b = tb.tb_pack(p.t, p.scales)
     dev = torch.device("cuda:0")
-    c0 = torch.from_numpy(codes.view(np.int32)).to(dev)
-    s0 = torch.from_numpy(s).to(dev)
-    b0 = torch.from_numpy(b).to(dev)
+    c0, s0, b0, x, sg = _device_problem(p, dev)
     R = args.replicas or max(1, math.ceil((1 << 30) / wbytes))
     reps = [(c0, s0, b0)] + [(c0.clone(), s0.clone(), b0.clone()) for _ in range(R - 1)]
-    x = (torch.from_numpy(p.x_store.view(np.int16)).view(torch.bfloat16) if p.xdtype == "bf16"
-         else torch.from_numpy(p.x_store)).to(dev)
-    sg = torch.from_numpy(p.signs).to(dev)
     ws = torch.empty(tb.tb_ternary_gemv_workspace_size_n(B, K, N), dtype=torch.uint8, device=dev)
     y = torch.empty((B, N), dtype=torch.float32, device=dev)
 
@@ -190,9 +456,7 @@ def run_gemv(args):
     want = oracle.packed_linear(p.x64, p.signs, p.block, oc, osc, ob)
     tb.tb_ternary_gemv(x, sg, p.block, *reps[R - 1], out=y, workspace=ws)
     torch.cuda.synchronize()
-    got = y.cpu().numpy().astype(np.float64)
-    rel = float(np.linalg.norm(got - want) / np.linalg.norm(want))
-    mabs = float(np.abs(got - want).max() / np.abs(want).max())
+    rel, mabs = _parity(y.cpu().numpy(), want)
     log(f"parity rel L2 {rel:.2e} max-abs {mabs:.2e}")
     if not (rel <= 1e-4 and mabs <= 1e-3):
         raise SystemExit("parity check failed; refusing to report a number")
@@ -211,43 +475,51 @@ def run_gemv(args):
                     tb.tb_ternary_gemv_run(ws, B, K, c, sc, bi, out=y)
         return g
 
-    def time_graph(g, n_replays, n_steps):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(n_replays):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / n_steps  # us per step
-
     y_eager = y.clone()
     full, rem = divmod(args.steps, R)
     g_steps = capture(R, True)
-    g_rem = capture(rem, True) if rem else None
+    g_rem = capture(rem, True) if rem and args.steps > 2 * R else None
+    # warm-up: every graph the timed region replays is replayed first (the
+    # first replay of a graph also uploads it)
     for _ in range(max(1, args.warmup // R)):
-        g_steps.replay()
-    torch.cuda.synchronize()
-
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(full):
         g_steps.replay()
     if g_rem is not None:
         g_rem.replay()
+    torch.cuda.synchronize()
+
+    # Timed: exactly `steps` steps, queued behind untimed replays of the ring
+    # so that they run back to back from the start event on.  A graph replay
+    # carries a fixed cost of about 10 us on top of its kernels, which a
+    # long region spreads over thousands of steps; a short region (at most
+    # two rings) is issued as eager calls instead, all of them enqueued while
+    # the spacer replays still run (each ring replay covers the host time of
+    # far more than R calls).
+    eager = args.steps <= 2 * R
+    for _ in range(3 if eager else 1):
+        g_steps.replay()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    if eager:
+        for i in range(args.steps):
+            tb.tb_ternary_gemv(x, sg, p.block, *reps[i % R], out=y, workspace=ws)
+    else:
+        for _ in range(full):
+            g_steps.replay()
+        if g_rem is not None:
+            g_rem.replay()
     t1.record()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
     if not torch.equal(y, y_eager):
-        raise SystemExit("graph replay result differs from the eager result")
+        raise SystemExit("the timed steps' result differs from the first call's")
 
-    # Batch 1: one step is one launch of the single-launch band kernel, so
-    # the kernel's average launch duration is the timed region over the
-    # launches (the dispatch gap between back-to-back launches included).
-    # Batches 2..8: a step is the K-split streaming kernel plus, when K is
-    # split over several workgroups, the slice-sum kernel; the rate over the
-    # whole step is then a lower bound for the streaming kernel alone.
+    # Batch 1: one step is one launch of the single-launch kernel, so the
+    # kernel's average launch duration is the timed region over the launches
+    # (the dispatch gap between back-to-back launches included).  Batches
+    # 2..8: a step is the K-split streaming kernel plus, when K is split over
+    # several workgroups, the slice-sum kernel; the rate over the whole step
+    # is then a lower bound for the streaming kernel alone.
     ms_step = total_ms / args.steps
     main_us = ms_step * 1e3
     value = wbytes * args.steps / (total_ms * 1e-3) / 1e9
@@ -258,21 +530,23 @@ def run_gemv(args):
     reps_k = max(1, min(20, args.steps // R))
     g_two = capture(R, False)
     g_two.replay()
-    two_us = time_graph(g_two, reps_k, reps_k * R)
+    two_us = _time_graph(torch, g_two, reps_k, spacer=g_two) / (reps_k * R) * 1e6
     g_hot = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_hot):
         for _ in range(100):
             tb.tb_ternary_gemv(x, sg, p.block, c0, s0, b0, out=y, workspace=ws)
     g_hot.replay()
-    hot_us = time_graph(g_hot, 5, 500)
+    hot_us = _time_graph(torch, g_hot, 5, spacer=g_hot) / 500 * 1e6
 
     cpu = None
     if not args.no_cpu_baseline:
-        per, ncalls, thr = cpu_baseline_gemv(p, oc, osc, ob)
-        cpu = {"value": round(wbytes / per / 1e9, 4), "unit": "GB/s", "cores": thr, "kind": "oracle",
-               "sample": f"{ncalls} full {args.workload} calls (N={N}, K={K}, B={B}), "
-                         f"{per * 1e3:.1f} ms each, numpy fp64 (decode single-threaded, BLAS {thr} threads)"}
+        per, ncalls = cpu_baseline_gemv(p, oc, osc, ob)
+        cpu = cpu_baseline_record(round(wbytes / per / 1e9, 4), "GB/s",
+                                  f"{ncalls} full {args.workload} calls (N={N}, K={K}, B={B}), {per * 1e3:.1f} ms "
+                                  "each, numpy fp64 (unpack and dequantize single-threaded, matvec on BLAS)")
 
+    kernel = "gemv_band_kernel" if B == 1 and args.workload != "down_proj" else (
+        "gemv_fused_kernel" if B == 1 else "batch_stream_kernel (+ batch_reduce_kernel)")
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -284,17 +558,19 @@ def run_gemv(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8",
+        "dtype": GEMV_DTYPE,
         "data": "synthetic",
         "config": {"workload": f"{args.workload} decode GEMV N={N} K={K} batch {B} {p.xdtype} activations, "
                                f"2.25 bpw packed weights, {R} rotating weight replicas",
                    "N": N, "K": K, "batch": B, "block": p.block, "replicas": R},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(counter_key(args.workload, B))},
         "cpu_baseline": cpu,
-        "detail": {"kernel": "gemv_band_kernel" if B == 1 else "batch_stream_kernel (+ batch_reduce_kernel)",
+        "detail": {"kernel": kernel,
                    "kernel_us_mean": round(main_us, 3),
-                   "timing": "HIP graph of back-to-back steps over the replica ring; " +
+                   "timing": ("eager calls" if eager else "HIP graph replays") +
+                             " of back-to-back steps over the replica ring, queued behind untimed replays; " +
                              ("one step is one launch of the single-launch kernel" if B == 1 else
                               "one step is the streaming launch plus the slice-sum launch when K is split"),
                    "step_us": round(ms_step * 1e3, 3),
@@ -302,27 +578,16 @@ def run_gemv(args):
                    "hot_step_us_same_replica": round(hot_us, 3),
                    "parity_rel_l2": rel, "parity_max_abs_rel": mabs},
     }
+    if args.workload == "q_proj" and not args.no_sweep:
+        del reps, g_steps, g_rem, g_two, g_hot
+        torch.cuda.empty_cache()
+        out["detail"]["sweep"] = sweep_measure(args.steps, not args.no_cpu_baseline, False)
     print(json.dumps(out), flush=True)
 
 
-def _time_graph(torch, g, n_replays):
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(n_replays):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e-3  # seconds
-
-
-def _parity(got, want):
-    got = np.asarray(got, dtype=np.float64)
-    rel = float(np.linalg.norm(got - want) / np.linalg.norm(want))
-    mabs = float(np.abs(got - want).max() / np.abs(want).max())
-    return rel, mabs
-
-
+# ---------------------------------------------------------------------------
+# prefill GEMM
+# ---------------------------------------------------------------------------
 def run_prefill(args):
     """Prefill GEMM gate/up_proj: M=2048, K=5120, N=17408, bf16 x.  One step =
     one tb_ternary_gemm call (rotation + fp6 digit kernel, then the
@@ -338,18 +603,13 @@ def run_prefill(args):
     M, N, K = p.B, p.N, p.K
     flops = 2.0 * M * N * K
     dev = torch.device("cuda:0")
-    codes, s, b = tb.tb_pack(p.t, p.scales)
-    c0 = torch.from_numpy(codes.view(np.int32)).to(dev)
-    s0 = torch.from_numpy(s).to(dev)
-    b0 = torch.from_numpy(b).to(dev)
-    x = torch.from_numpy(p.x_store.view(np.int16)).view(torch.bfloat16).to(dev)
-    sg = torch.from_numpy(p.signs).to(dev)
+    c0, s0, b0, x, sg = _device_problem(p, dev)
     ws = torch.empty(tb.tb_ternary_gemm_workspace_size_n(M, K, N), dtype=torch.uint8, device=dev)
     y = torch.empty((M, N), dtype=torch.float32, device=dev)
     tb.tb_ternary_gemm(x, sg, p.block, c0, s0, b0, out=y, workspace=ws)
     torch.cuda.synchronize()
-    rows = np.unique(np.concatenate([[0, 1, 127, 128, 1023, M - 1],
-                                     np.random.default_rng(44).integers(0, M, 26)]))
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 1023, M - 1],
+                                     np.random.default_rng(44).integers(0, M, 56)]))
     oc, osc, ob = oracle.pack(p.t, p.scales)
     want = oracle.packed_linear(p.x64[rows], p.signs, p.block, oc, osc, ob)
     rel, mabs = _parity(y[torch.from_numpy(rows).to(dev)].cpu().numpy(), want)
@@ -357,7 +617,7 @@ def run_prefill(args):
     if not (rel <= 1e-4 and mabs <= 1e-3):
         raise SystemExit("parity check failed; refusing to report a number")
 
-    steps = max(1, min(args.steps, 200))
+    steps = max(10, min(args.steps, 200)) // 10 * 10
     warm = max(1, min(args.warmup, 20))
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -369,28 +629,30 @@ def run_prefill(args):
             tb.tb_ternary_gemm_run(ws, M, K, c0, s0, b0, out=y)
     for _ in range(max(1, warm // 10)):
         g.replay()
-    torch.cuda.synchronize()
-    nrep = max(1, steps // 10)
-    t = _time_graph(torch, g, nrep) / (nrep * 10)
-    t_run = _time_graph(torch, g2, nrep) / (nrep * 10)
+    g2.replay()
+    nrep = steps // 10
+    t = _time_graph(torch, g, nrep, spacer=g) / steps
+    t_run = _time_graph(torch, g2, nrep, spacer=g2) / steps
     tflops = flops / t / 1e12
     run_tflops = flops / t_run / 1e12
 
     cpu = None
     if not args.no_cpu_baseline:
         sample = 16
-        t0 = time.perf_counter()
-        oracle.packed_linear(p.x64[:sample], p.signs, p.block, oc, osc, ob)
-        per = time.perf_counter() - t0
-        cpu = {"value": round(2.0 * sample * N * K / per / 1e12, 6), "unit": "TFLOP/s", "cores": _blas_threads(),
-               "kind": "oracle",
-               "sample": f"{sample} of the {M} activation rows against the whole {N}x{K} pack, {per:.1f} s, numpy fp64"}
+        with _oracle_threads(len(os.sched_getaffinity(0))):
+            t0 = time.perf_counter()
+            oracle.packed_linear(p.x64[:sample], p.signs, p.block, oc, osc, ob)
+            per = time.perf_counter() - t0
+        cpu = cpu_baseline_record(round(2.0 * sample * N * K / per / 1e12, 6), "TFLOP/s",
+                                  f"{sample} of the {M} activation rows against the whole {N}x{K} pack, {per:.1f} s, "
+                                  "numpy fp64")
 
     out = {
         "metric": "algorithmic TFLOP/s of the prefill Packed linear (2 M N K per call)",
-        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": nrep * 10, "warmup": warm,
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warm,
         "ms_per_step": round(t * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp6 x fp4 (block-scaled MFMA, fp32 accumulate)", "data": "synthetic",
+        "dtype": "fp6 digits of the rotated activation x fp4 codes (block-scaled MFMA), fp32 accumulate",
+        "data": "synthetic",
         "config": {"workload": f"prefill gate/up_proj GEMM M={M} K={K} N={N}, bf16 activations, 2.25 bpw packed "
                                "weights", "M": M, "N": N, "K": K, "block": p.block},
         "roofline": {"bound": "mfma", "achieved": round(run_tflops, 2), "peak": FP6_PEAK_TFLOPS,
@@ -407,174 +669,19 @@ def run_prefill(args):
     print(json.dumps(out), flush=True)
 
 
-def _blas_threads():
-    try:
-        from threadpoolctl import threadpool_info
-        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        return 1
-
-
 def run_sweep(args):
-    """The full decode sweep at batch 1: the 401 packed linears of the
-    64-layer model (3:1 linear:full attention layers, MLP 17408, lm_head
-    248320) and one embedding row with the inverse transform.  Every module
-    has its own synthetic pack and input (modules are not chained).  One step
-    = all 402 calls, captured once as a HIP graph."""
-    import torch
-
-    import hadamard_rotated_quantized_amd as tb
-    import oracle
-    from hadamard_rotated_quantized_amd import synth
-
-    dev = torch.device("cuda:0")
-    mods = synth.sweep_modules()
-    signs_h = synth.sweep_signs()
-    signs = {k: torch.from_numpy(v).to(dev) for k, v in signs_h.items()}
-    packs, xs, ys = [], [], []
-    t0 = time.perf_counter()
-    for i, (name, N, K, kind) in enumerate(mods):
-        t, sc, x = synth.device_module_draw(i, N, K, 1, dev)
-        codes, so, bo = tb.tb_pack_device(t, sc, check=False)
-        del t, sc
-        packs.append((codes, so, bo))
-        xs.append(x)
-        ys.append(torch.empty((1, N) if kind == "linear" else (1, K), dtype=torch.float32, device=dev))
-    torch.cuda.synchronize()
-    log(f"drew and packed {len(mods)} modules in {time.perf_counter() - t0:.1f} s")
-    embed_id = torch.tensor([int(np.random.default_rng(synth.SWEEP_SEED).integers(0, synth.VOCAB))],
-                            dtype=torch.int32, device=dev)
-    wsz = tb.tb_ternary_gemv_workspace_size(1, max(m[2] for m in mods))
-    ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
-
-    def call(i):
-        name, N, K, kind = mods[i]
-        c, sc, bi = packs[i]
-        if kind == "linear":
-            tb.tb_ternary_gemv(xs[i], signs[K], 1024, c, sc, bi, out=ys[i], workspace=ws)
-        else:
-            tb.tb_embed_inverse(embed_id, c, sc, bi, signs[K], 1024, out=ys[i])
-
-    for i in range(len(mods)):
-        call(i)
-    torch.cuda.synchronize()
-    # parity on one module of every shape (lm_head on sampled rows) and the embedding row
-    checked, worst = [], 0.0
-    seen = set()
-    for i, (name, N, K, kind) in enumerate(mods):
-        key = (N, K, kind)
-        if key in seen:
-            continue
-        seen.add(key)
-        t, sc, _ = synth.device_module_draw(i, N, K, 1, dev)
-        if kind == "linear":
-            rows = np.arange(N) if N <= 20000 else np.unique(np.concatenate(
-                [[0, N - 1], np.random.default_rng(i).integers(0, N, 2046)]))
-        else:
-            rows = np.array([int(embed_id.item())])
-        rt = torch.from_numpy(rows).to(dev)
-        oc, osc, ob = oracle.pack(t[rt].cpu().numpy(), sc[rt].cpu().numpy())
-        del t, sc
-        if kind == "linear":
-            xh = xs[i].float().cpu().numpy().astype(np.float64)
-            want = oracle.packed_linear(xh, signs_h[K], 1024, oc, osc, ob)
-            got = ys[i][:, rt].cpu().numpy()
-        else:
-            want = oracle.embed_inverse([0], oc, osc, ob, signs_h[K], 1024)
-            got = ys[i].cpu().numpy()
-        rel, mabs = _parity(got, want)
-        worst = max(worst, rel)
-        checked.append(f"{name}:{rel:.1e}")
-        if not (rel <= 1e-4 and mabs <= 1e-3):
-            raise SystemExit(f"parity check failed on {name}: rel {rel:.2e} max-abs {mabs:.2e}")
-    log("parity " + ", ".join(checked))
-
-    # the step: all 401 linears through the multi-module path (one transform
-    # launch, one persistent streaming launch) plus the embedding row
-    lin = [i for i, m in enumerate(mods) if m[3] == "linear"]
-    emb = [i for i, m in enumerate(mods) if m[3] == "embedding"]
-    plan, wsb = tb.tb_gemv_multi_plan([(xs[i], signs[mods[i][2]], *packs[i], ys[i]) for i in lin], 1024)
-    plan_dev = torch.from_numpy(plan).to(dev)
-    mws = torch.empty(wsb, dtype=torch.uint8, device=dev)
-
-    def step():
-        tb.tb_ternary_gemv_multi(plan, plan_dev, mws)
-        for i in emb:
-            call(i)
-
-    # the multi path must reproduce the per-module calls' outputs (checked
-    # against the oracle above) within the parity bar
-    ref = [ys[i].clone() for i in lin]
-    for i in lin:
-        ys[i].fill_(float("nan"))
-    step()
-    torch.cuda.synchronize()
-    worst_multi = 0.0
-    for r, i in zip(ref, lin):
-        d = float((ys[i].double() - r.double()).norm() / r.double().norm())
-        worst_multi = max(worst_multi, d)
-    log(f"multi-module path vs per-module calls: worst rel L2 {worst_multi:.2e}")
-    if not worst_multi <= 1e-4:
-        raise SystemExit("multi-module path disagrees with the per-module calls")
-
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        step()
-    g.replay()
-    torch.cuda.synchronize()
-    nrep = max(3, min(args.steps, 50))
-    sec = _time_graph(torch, g, nrep) / nrep
-    wbytes = sum(N * K * 9 // 32 for (_, N, K, kind) in mods if kind == "linear") + 5120 * 9 // 32
-    value = wbytes / sec / 1e9
-
-    # context: the same 402 modules as separate calls in one graph
-    gsep = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gsep):
-        for i in range(len(mods)):
-            call(i)
-    gsep.replay()
-    torch.cuda.synchronize()
-    sep_sec = _time_graph(torch, gsep, max(3, min(args.steps, 20))) / max(3, min(args.steps, 20))
-
-    # per-shape timing: a graph of every module of one shape, back to back;
-    # a shape with few modules (lm_head, the embedding row) is called again
-    # in the graph until it holds at least 32 calls, so that the graph's own
-    # launch cost is spread as it is for the other shapes
-    per_shape = {}
-    for key in sorted({(m[1], m[2], m[3]) for m in mods}):
-        idx = [i for i, m in enumerate(mods) if (m[1], m[2], m[3]) == key]
-        idx = idx * max(1, -(-32 // len(idx)))
-        gs = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gs):
-            for i in idx:
-                call(i)
-        gs.replay()
-        torch.cuda.synchronize()
-        r = max(3, min(20, 2000 // len(idx)))
-        us = _time_graph(torch, gs, r) / (r * len(idx)) * 1e6
-        N, K, kind = key
-        b = N * K * 9 // 32 if kind == "linear" else 5120 * 9 // 32
-        per_shape[f"{kind} {N}x{K}"] = {"count": sum(m[1:] == key for m in mods), "calls_timed": len(idx),
-                                        "us_each": round(us, 3),
-                                        "GB/s": round(b / (us * 1e-6) / 1e9, 1)}
-
+    """The full decode sweep at batch 1 as its own line: the 401 packed
+    linears of the 64-layer model and one embedding row; one step = the
+    multi-module plan + the embedding call, captured as one HIP graph."""
+    d = sweep_measure(args.steps, not args.no_cpu_baseline, True)
     out = {
         "metric": "effective weight GB/s (2.25 bpw), full batch-1 decode sweep of 402 packed modules",
-        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": nrep, "warmup": 1,
-        "ms_per_step": round(sec * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int8", "data": "synthetic",
-        "config": {"workload": "decode sweep: 401 packed linears of a 64-layer hidden-5120 model (48 linear-"
-                               "attention + 16 full-attention layers, MLP 17408, lm_head 248320) + 1 embedding "
-                               "row, batch 1: multi-module path (transform launch + persistent streaming "
-                               "launch) and the embedding call", "modules": len(mods),
-                   "weight_bytes": wbytes},
-        "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None},
-        "cpu_baseline": None,
-        "detail": {"separate_calls_ms": round(sep_sec * 1e3, 4),
-                   "separate_calls_GBps": round(wbytes / sep_sec / 1e9, 2),
-                   "multi_vs_separate_worst_rel_l2": worst_multi,
-                   "per_shape_separate_calls": per_shape, "parity_worst_rel_l2": worst, "parity": checked},
+        "value": d["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": d["steps"], "warmup": 1,
+        "ms_per_step": d["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": GEMV_DTYPE, "data": "synthetic",
+        "config": {"workload": d["workload"], "modules": d["modules"], "weight_bytes": d["weight_bytes"]},
+        "roofline": d["roofline"], "cpu_baseline": d.get("cpu_baseline"),
+        "detail": {k: v for k, v in d.items() if k not in ("roofline", "cpu_baseline", "workload")},
     }
     print(json.dumps(out), flush=True)
 
@@ -589,6 +696,7 @@ def main():
     ap.add_argument("--batch", type=int, default=None, help="down_proj batch (1, 2, 4 or 8)")
     ap.add_argument("--replicas", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="q_proj line without the sweep detail")
     ap.add_argument("--counters-only", action="store_true",
                     help="eager launches without timing, for rocprofv3 --pmc passes")
     args = ap.parse_args()
@@ -596,6 +704,8 @@ def main():
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
+    if args.workload == "down_proj" and args.batch is None:
+        args.batch = 1
     if args.counters_only:
         run_counter_pass(args)
     elif args.workload == "copy":
@@ -605,8 +715,6 @@ def main():
     elif args.workload == "sweep":
         run_sweep(args)
     else:
-        if args.workload == "down_proj" and args.batch is None:
-            args.batch = 1
         run_gemv(args)
 
 
