@@ -35,3 +35,19 @@ from .reference import (  # noqa: F401
     bf16_bits_to_f64,
     f16_to_f64,
 )
+from .formats import (  # noqa: F401
+    PQ2_BLOCK_BYTES,
+    PTQ1_BLOCK_BYTES,
+    pq2_from_mlx,
+    pq2_to_mlx,
+    pq2_codes,
+    pq2_dequantize_rows,
+    pq2_packed_linear,
+    ptq1_pack,
+    ptq1_unpack,
+    ptq1_codes,
+    ptq1_dequantize_rows,
+    ptq1_packed_linear,
+    container_bytes_pq2,
+    container_bytes_ptq1,
+)

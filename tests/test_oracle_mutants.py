@@ -68,3 +68,51 @@ def test_mutant_is_caught(name):
         except (AssertionError, ValueError, IndexError, TypeError) as e:  # any failure counts
             caught.append(pin.__name__)
     assert caught, f"no pin catches the planted mistake {name}"
+
+
+# --- the PQ2_0 / PTQ1_0 oracle (oracle/formats.py) -------------------------
+from oracle_pins_formats import PINS_FORMATS  # noqa: E402
+
+FORMATS_PATH = os.path.join(os.path.dirname(SRC_PATH), "formats.py")
+
+MUTANTS_FORMATS = {
+    "pq2_scale_after_codes": ("out = np.concatenate([_scale_bytes(s), qs], axis=2)",
+                              "out = np.concatenate([qs, _scale_bytes(s)], axis=2)"),
+    "pq2_codes_high_bits_first": ("qs = cb[..., 0] | (cb[..., 1] << 2) | (cb[..., 2] << 4) | (cb[..., 3] << 6)",
+                                  "qs = cb[..., 3] | (cb[..., 2] << 2) | (cb[..., 1] << 4) | (cb[..., 0] << 6)"),
+    "pq2_decode_reads_high_bits_first": ("c = np.stack([(qs >> (2 * j)) & 3 for j in range(4)], axis=-1)",
+                                         "c = np.stack([(qs >> (6 - 2 * j)) & 3 for j in range(4)], axis=-1)"),
+    "pq2_decode_without_offset": ("return d[:, np.arange(K) // GROUP] * (c - 1.0)",
+                                  "return d[:, np.arange(K) // GROUP] * c"),
+    "pq2_accepts_any_bias": ("if not np.array_equal(b, s ^ np.uint16(0x8000)):", "if False:"),
+    "pq2_scale_bytes_swapped": ("return (lo | (hi << 8)).view(np.float16)", "return (hi | (lo << 8)).view(np.float16)"),
+    "ptq1_first_code_highest_digit": ("for j in reversed(range(TRITS_PER_BYTE)):", "for j in range(TRITS_PER_BYTE):"),
+    "ptq1_decode_highest_digit_first": (
+        "c = np.stack(digits, axis=-1).reshape(bl.shape[0], bl.shape[1], -1)[:, :, :GROUP]",
+        "c = np.stack(digits[::-1], axis=-1).reshape(bl.shape[0], bl.shape[1], -1)[:, :, :GROUP]"),
+    "ptq1_last_byte_unchecked": ("if (q > 242).any() or (q[:, :, -1] > 26).any():", "if (q > 242).any():"),
+    "ptq1_codes_not_shifted": ("c = (t.astype(np.int64) + 1).reshape(N, G, GROUP)",
+                               "c = (t.astype(np.int64) % 3).reshape(N, G, GROUP)"),
+    "ptq1_group_of_64": ("return f16_to_f64(d)[:, np.arange(K) // GROUP] * t.astype(np.float64)",
+                         "return f16_to_f64(d)[:, np.arange(K) // 64 % (K // GROUP)] * t.astype(np.float64)"),
+}
+
+
+def _mutant_formats(old, new):
+    src = open(FORMATS_PATH).read()
+    assert src.count(old) == 1, f"mutation site not unique/present: {old!r}"
+    mod = types.ModuleType("formats_mutant")
+    exec(compile(src.replace(old, new), "formats_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS_FORMATS))
+def test_formats_mutant_is_caught(name):
+    mod = _mutant_formats(*MUTANTS_FORMATS[name])
+    caught = []
+    for pin in PINS_FORMATS:
+        try:
+            pin(mod)
+        except (AssertionError, ValueError, IndexError, TypeError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake {name}"
