@@ -53,6 +53,13 @@ _SIGNATURES = {
     "tb_ternary_gemm_run": (_I, [_P, _SZ, _I64, _I64, _P, _P, _P, _I64, _P, _P]),
     "tb_ternary_gemm": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
     "tb_embed_inverse": (_I, [_P, _I64, _P, _P, _P, _I64, _I64, _P, _I, _P, _P]),
+    "tb_pq2_from_mlx": (_I, [_P, _P, _P, _I64, _I64, _P]),
+    "tb_pq2_to_mlx": (_I, [_P, _I64, _I64, _P, _P, _P]),
+    "tb_ptq1_pack": (_I, [_P, _P, _I64, _I64, _P]),
+    "tb_ptq1_unpack": (_I, [_P, _I64, _I64, _P, _P]),
+    "tb_blocks_gemv_workspace_size": (_SZ, [_I64]),
+    "tb_pq2_gemv": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _I64, _P, _P, _SZ, _P]),
+    "tb_ptq1_gemv": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _I64, _P, _P, _SZ, _P]),
     "tb_gemv_multi_plan_size": (_SZ, [_P, _I64]),
     "tb_gemv_multi_plan": (_I, [_P, _I64, _I, _I, _P, _SZ, ctypes.POINTER(_SZ)]),
     "tb_ternary_gemv_multi": (_I, [_P, _P, _P, _SZ, _P]),
@@ -479,3 +486,115 @@ def tb_ternary_gemv_multi(plan, plan_device, workspace):
     _dev(workspace, "workspace", torch.uint8)
     _check(lib().tb_ternary_gemv_multi(plan.ctypes.data, plan_device.data_ptr(), workspace.data_ptr(),
                                        workspace.numel(), _stream()))
+
+
+# ---------------------------------------------------------------------------
+# block containers: PQ2_0 (34 bytes per 128 weights) and PTQ1_0 (28 bytes)
+# ---------------------------------------------------------------------------
+PQ2_BLOCK_BYTES = 34
+PTQ1_BLOCK_BYTES = 28
+
+
+def _u16(a, shape, name):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float16:
+        a = a.view(np.uint16)
+    if a.dtype != np.uint16 or a.shape != tuple(shape):
+        raise ValueError(f"{name} must be float16 of shape {tuple(shape)}")
+    return a
+
+
+def tb_pq2_from_mlx(codes: np.ndarray, scales: np.ndarray, biases: np.ndarray) -> np.ndarray:
+    """MLX container (host arrays) -> PQ2_0 blocks uint8 (N, K/128 * 34)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint32)
+    if codes.ndim != 2:
+        raise ValueError("codes must be (N, K/16)")
+    N, K = codes.shape[0], codes.shape[1] * 16
+    _check_width(K)
+    sc = _u16(scales, (N, K // 128), "scales")
+    bi = _u16(biases, (N, K // 128), "biases")
+    out = np.empty((N, K // 128 * PQ2_BLOCK_BYTES), np.uint8)
+    _check(lib().tb_pq2_from_mlx(codes.ctypes.data, sc.ctypes.data, bi.ctypes.data, N, K, out.ctypes.data))
+    return out
+
+
+def tb_pq2_to_mlx(blocks: np.ndarray, K: int):
+    """PQ2_0 blocks (host) -> (codes uint32, scales float16, biases float16)."""
+    _check_width(K)
+    blocks = np.ascontiguousarray(blocks, dtype=np.uint8)
+    if blocks.ndim != 2 or blocks.shape[1] != K // 128 * PQ2_BLOCK_BYTES:
+        raise ValueError(f"blocks must be (N, {K // 128 * PQ2_BLOCK_BYTES})")
+    N = blocks.shape[0]
+    codes = np.empty((N, K // 16), np.uint32)
+    sc = np.empty((N, K // 128), np.uint16)
+    bi = np.empty((N, K // 128), np.uint16)
+    _check(lib().tb_pq2_to_mlx(blocks.ctypes.data, N, K, codes.ctypes.data, sc.ctypes.data, bi.ctypes.data))
+    return codes, sc.view(np.float16), bi.view(np.float16)
+
+
+def tb_ptq1_pack(t: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Ternary t int8 (N, K) and float16 scales (N, K/128) -> PTQ1_0 blocks
+    uint8 (N, K/128 * 28)."""
+    t = np.ascontiguousarray(t, dtype=np.int8)
+    if t.ndim != 2:
+        raise ValueError("t must be (N, K)")
+    N, K = t.shape
+    _check_width(K)
+    sc = _u16(scales, (N, K // 128), "scales")
+    out = np.empty((N, K // 128 * PTQ1_BLOCK_BYTES), np.uint8)
+    _check(lib().tb_ptq1_pack(t.ctypes.data, sc.ctypes.data, N, K, out.ctypes.data))
+    return out
+
+
+def tb_ptq1_unpack(blocks: np.ndarray, K: int):
+    """PTQ1_0 blocks (host) -> (t int8 (N, K), scales float16 (N, K/128))."""
+    _check_width(K)
+    blocks = np.ascontiguousarray(blocks, dtype=np.uint8)
+    if blocks.ndim != 2 or blocks.shape[1] != K // 128 * PTQ1_BLOCK_BYTES:
+        raise ValueError(f"blocks must be (N, {K // 128 * PTQ1_BLOCK_BYTES})")
+    N = blocks.shape[0]
+    t = np.empty((N, K), np.int8)
+    sc = np.empty((N, K // 128), np.uint16)
+    _check(lib().tb_ptq1_unpack(blocks.ctypes.data, N, K, t.ctypes.data, sc.ctypes.data))
+    return t, sc.view(np.float16)
+
+
+def tb_blocks_gemv_workspace_size(K: int) -> int:
+    return int(lib().tb_blocks_gemv_workspace_size(K))
+
+
+def _blocks_gemv(fn, nbytes, x, signs, block, blocks, out, workspace):
+    torch = _torch()
+    B, K = _rows(x)
+    _check_width(K)
+    _signs_shape(signs, K, block)
+    if blocks.dim() != 2 or blocks.shape[1] != K // 128 * nbytes:
+        raise ValueError(f"blocks has shape {tuple(blocks.shape)}, expected (N, {K // 128 * nbytes})")
+    N = int(blocks.shape[0])
+    if out is not None:
+        _shape(out, (B, N), "out")
+    _dev(x, "x")
+    _dev(blocks, "blocks", torch.uint8)
+    if signs is not None:
+        _dev(signs, "signs", torch.int8)
+    if out is None:
+        out = torch.empty((B, N), dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    if workspace is None:
+        workspace = torch.empty(max(tb_blocks_gemv_workspace_size(K), 1), dtype=torch.uint8, device=x.device)
+    _dev(workspace, "workspace", torch.uint8)
+    _check(fn(x.data_ptr(), _xdtype(x), B, K, _ptr(signs), block, blocks.data_ptr(), N, out.data_ptr(),
+              workspace.data_ptr(), workspace.numel(), _stream()))
+    return out
+
+
+def tb_pq2_gemv(x, signs, block: int, blocks, out=None, workspace=None):
+    """y (1, N) float32 = Packed linear of x (1, K) on PQ2_0 blocks (uint8
+    (N, K/128 * 34) on the GPU)."""
+    return _blocks_gemv(lib().tb_pq2_gemv, PQ2_BLOCK_BYTES, x, signs, block, blocks, out, workspace)
+
+
+def tb_ptq1_gemv(x, signs, block: int, blocks, out=None, workspace=None):
+    """y (1, N) float32 = Packed linear of x (1, K) on PTQ1_0 blocks (uint8
+    (N, K/128 * 28) on the GPU)."""
+    return _blocks_gemv(lib().tb_ptq1_gemv, PTQ1_BLOCK_BYTES, x, signs, block, blocks, out, workspace)

@@ -15,6 +15,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef unsigned int v3u __attribute__((ext_vector_type(3)));
 
 constexpr int kLimbs = 3;
 constexpr int kWordsPerGroup = kGroup / kCodesPerWord;  // 8

@@ -297,6 +297,67 @@ int tb_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int x_dtype, i
 int tb_ternary_gemv_multi(const void* plan_host, const void* plan_device,
                           void* workspace, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * The block containers [P2 "packing-format engineering": the same ternary
+ * weights also ship as GGUF blocks of 128 weights; PQ2_0, one 2-bit slot per
+ * trit and an fp16 scale, 34 bytes (2.125 bits/weight), a lossless transcode
+ * of the MLX container checked by an independent unpack and a bit-compare of
+ * the group scales; PTQ1_0, dense trits, 28 bytes (1.75 bits/weight), which
+ * need extra arithmetic to decode].  The pages print neither byte layout;
+ * the reading implemented here:
+ *   block = fp16 scale d (2 bytes, little-endian), then the codes; no bias
+ *           is stored: code c (t = c - 1) decodes to (c - 1) d, the MLX
+ *           decode with bias = -scale;
+ *   PQ2_0   32 code bytes, code k of the block at bits 2 (k % 4) of byte k/4
+ *           (byte for byte the MLX group's eight code words);
+ *   PTQ1_0  26 trit bytes, byte i = sum_j c[5 i + j] 3^j over j < 5 (the
+ *           first code the lowest digit; at most 242); the last byte holds
+ *           codes 125..127 the same way (at most 26).
+ * A row of K weights is K/128 consecutive blocks; rows are consecutive.
+ * ------------------------------------------------------------------------ */
+
+/* MLX container (host) -> PQ2_0 blocks (host, N * K/128 * 34 bytes).
+ * TB_ERR_CODE if a bias is not the negated scale (bit for bit) or a code is
+ * 3 -- PQ2_0 cannot hold them; blocks are then unspecified. */
+int tb_pq2_from_mlx(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                    int64_t N, int64_t K, uint8_t* blocks);
+
+/* PQ2_0 blocks (host) -> MLX container (host): codes, scales = d,
+ * biases = -d.  TB_ERR_CODE if a code is 3. */
+int tb_pq2_to_mlx(const uint8_t* blocks, int64_t N, int64_t K,
+                  uint32_t* codes, uint16_t* scales, uint16_t* biases);
+
+/* Ternary t (int8 [N][K], -1/0/1) and fp16 scales [N][K/128] (host) ->
+ * PTQ1_0 blocks (host, N * K/128 * 28 bytes).  TB_ERR_CODE for a t outside
+ * {-1,0,1}. */
+int tb_ptq1_pack(const int8_t* t, const uint16_t* scales, int64_t N, int64_t K, uint8_t* blocks);
+
+/* PTQ1_0 blocks (host) -> t (int8 [N][K]) and scales (host).  TB_ERR_CODE
+ * if a trit byte is out of range (over 242, or over 26 for a last byte). */
+int tb_ptq1_unpack(const uint8_t* blocks, int64_t N, int64_t K, int8_t* t, uint16_t* scales);
+
+/* Workspace bytes of tb_pq2_gemv / tb_ptq1_gemv for input width K (0 for an
+ * invalid K). */
+size_t tb_blocks_gemv_workspace_size(int64_t K);
+
+/* Packed linear on PQ2_0 / PTQ1_0 blocks at batch 1 [P3 "text model
+ * loading", with the block decode above]:  y[n] = sum_k W~[n][k] (R x)[k].
+ * x: K activations (x_dtype), 16-byte aligned; signs as for tb_ternary_gemv
+ * (16-byte aligned); blocks: device, N rows of K/128 blocks, 4-byte aligned
+ * (trit bytes are not checked on the device: validate with the host
+ * unpack); y: N fp32 (overwritten).  B must be 1 (0 is a no-op; larger
+ * batches return TB_ERR_UNSUPPORTED), K a multiple of 256, block 0, 512 or
+ * 1024 (2048/4096: TB_ERR_UNSUPPORTED).  workspace: device, at least
+ * tb_blocks_gemv_workspace_size(K) bytes, 16-byte aligned, no
+ * initialisation needed.  Two launches: the rotated activation's exact
+ * integer image into the workspace, then the streaming matmul. */
+int tb_pq2_gemv(const void* x, int x_dtype, int64_t B, int64_t K, const int8_t* signs, int block,
+                const uint8_t* blocks, int64_t N, float* y, void* workspace, size_t ws_bytes,
+                void* stream);
+int tb_ptq1_gemv(const void* x, int x_dtype, int64_t B, int64_t K, const int8_t* signs, int block,
+                 const uint8_t* blocks, int64_t N, float* y, void* workspace, size_t ws_bytes,
+                 void* stream);
+
 /* Embedding lookup with the inverse transform [P3 "text model loading"]:
  *   out[t] = signs .* (H_L W~[ids[t]]) / sqrt(L)   blockwise  (block > 0)
  *   out[t] = W~[ids[t]]                                      (block = 0)
