@@ -378,6 +378,79 @@ def sweep_measure(n_steps, with_cpu, with_context):
 
 
 # ---------------------------------------------------------------------------
+# the three containers of one layer: MLX affine (2.25 bpw), PQ2_0 (2.125),
+# PTQ1_0 (1.75)
+# ---------------------------------------------------------------------------
+FORMAT_BITS = {"mlx": 2.25, "pq2": 2.125, "ptq1": 1.75}
+
+
+def format_containers(p, fmt, dev):
+    """Device tensors of one container of problem p and the call that runs
+    the Packed linear on them (batch 1)."""
+    import torch
+
+    import hadamard_rotated_quantized_amd as tb
+    c, s, b = tb.tb_pack(p.t, p.scales)
+    if fmt == "mlx":
+        return (torch.from_numpy(c.view(np.int32)).to(dev), torch.from_numpy(s).to(dev), torch.from_numpy(b).to(dev))
+    blk = tb.tb_pq2_from_mlx(c, s, b) if fmt == "pq2" else tb.tb_ptq1_pack(p.t, p.scales)
+    return (torch.from_numpy(blk).to(dev),)
+
+
+def format_step(fmt, x, sg, block, cont, y, ws):
+    import hadamard_rotated_quantized_amd as tb
+    if fmt == "mlx":
+        tb.tb_ternary_gemv(x, sg, block, *cont, out=y, workspace=ws)
+    elif fmt == "pq2":
+        tb.tb_pq2_gemv(x, sg, block, cont[0], out=y)
+    else:
+        tb.tb_ptq1_gemv(x, sg, block, cont[0], out=y)
+
+
+def formats_measure(p, reps_per_graph=None, replays=10):
+    """Per container: us per batch-1 call over rotating replicas (>= 1 GiB,
+    so no call finds its blocks in the last-level cache), HIP graphs behind
+    an untimed replay; parity of each container against the oracle first."""
+    import torch
+
+    import hadamard_rotated_quantized_amd as tb
+    import oracle
+
+    dev = torch.device("cuda:0")
+    x = (torch.from_numpy(p.x_store.view(np.int16)).view(torch.bfloat16) if p.xdtype == "bf16"
+         else torch.from_numpy(p.x_store)).to(dev)
+    sg = torch.from_numpy(p.signs).to(dev)
+    y = torch.empty((1, p.N), dtype=torch.float32, device=dev)
+    ws = torch.empty(tb.tb_ternary_gemv_workspace_size_n(1, p.K, p.N), dtype=torch.uint8, device=dev)
+    rows = np.unique(np.concatenate([[0, p.N - 1], np.random.default_rng(9).integers(0, p.N, 510)]))
+    oc, osc, ob = oracle.pack(p.t[rows], p.scales[rows])
+    want = oracle.packed_linear(p.x64[:1], p.signs, p.block, oc, osc, ob)
+    out = {}
+    for fmt, bits in FORMAT_BITS.items():
+        cont = format_containers(p, fmt, dev)
+        wbytes = int(p.N * p.K * bits / 8)
+        R = max(2, math.ceil((1 << 30) / wbytes))
+        reps = [cont] + [tuple(t.clone() for t in cont) for _ in range(R - 1)]
+        format_step(fmt, x, sg, p.block, reps[-1], y, ws)
+        torch.cuda.synchronize()
+        rel, mabs = _parity(y[:, torch.from_numpy(rows).to(dev)].cpu().numpy(), want)
+        if not (rel <= 1e-4 and mabs <= 1e-3):
+            raise SystemExit(f"{fmt} parity check failed: rel {rel:.2e} max-abs {mabs:.2e}")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(R):
+                format_step(fmt, x, sg, p.block, reps[i], y, ws)
+        g.replay()
+        us = _time_graph(torch, g, replays, spacer=g) / (replays * R) * 1e6
+        gbs = wbytes / (us * 1e-6) / 1e9
+        out[fmt] = {"bits_per_weight": bits, "weight_bytes": wbytes, "us": round(us, 3), "GB/s": round(gbs, 1),
+                    "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "replicas": R, "parity_rel_l2": rel}
+        del reps, g
+        torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------------------
 # counter passes (rocprofv3 --pmc)
 # ---------------------------------------------------------------------------
 def run_counter_pass(args):
@@ -582,6 +655,13 @@ def run_gemv(args):
         del reps, g_steps, g_rem, g_two, g_hot
         torch.cuda.empty_cache()
         out["detail"]["sweep"] = sweep_measure(args.steps, not args.no_cpu_baseline, False)
+        torch.cuda.empty_cache()
+        gate = synth.make_problem("gate_proj", 17408, 5120, 1, 41, "bf16", 1024)
+        out["detail"]["formats"] = {
+            "about": "batch-1 Packed linear in the three containers of one set of ternary weights: MLX affine "
+                     "(2.25 bpw), PQ2_0 (2.125), PTQ1_0 (1.75); us per call over rotating replicas of >= 1 GiB",
+            "q_proj N=6144 K=5120": formats_measure(p),
+            "gate_proj N=17408 K=5120": formats_measure(gate)}
     print(json.dumps(out), flush=True)
 
 

@@ -57,9 +57,8 @@ _SIGNATURES = {
     "tb_pq2_to_mlx": (_I, [_P, _I64, _I64, _P, _P, _P]),
     "tb_ptq1_pack": (_I, [_P, _P, _I64, _I64, _P]),
     "tb_ptq1_unpack": (_I, [_P, _I64, _I64, _P, _P]),
-    "tb_blocks_gemv_workspace_size": (_SZ, [_I64]),
-    "tb_pq2_gemv": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _I64, _P, _P, _SZ, _P]),
-    "tb_ptq1_gemv": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _I64, _P, _P, _SZ, _P]),
+    "tb_pq2_gemv": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _I64, _P, _P]),
+    "tb_ptq1_gemv": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _I64, _P, _P]),
     "tb_gemv_multi_plan_size": (_SZ, [_P, _I64]),
     "tb_gemv_multi_plan": (_I, [_P, _I64, _I, _I, _P, _SZ, ctypes.POINTER(_SZ)]),
     "tb_ternary_gemv_multi": (_I, [_P, _P, _P, _SZ, _P]),
@@ -559,11 +558,7 @@ def tb_ptq1_unpack(blocks: np.ndarray, K: int):
     return t, sc.view(np.float16)
 
 
-def tb_blocks_gemv_workspace_size(K: int) -> int:
-    return int(lib().tb_blocks_gemv_workspace_size(K))
-
-
-def _blocks_gemv(fn, nbytes, x, signs, block, blocks, out, workspace):
+def _blocks_gemv(fn, nbytes, x, signs, block, blocks, out):
     torch = _torch()
     B, K = _rows(x)
     _check_width(K)
@@ -580,21 +575,17 @@ def _blocks_gemv(fn, nbytes, x, signs, block, blocks, out, workspace):
     if out is None:
         out = torch.empty((B, N), dtype=torch.float32, device=x.device)
     _dev(out, "out", torch.float32)
-    if workspace is None:
-        workspace = torch.empty(max(tb_blocks_gemv_workspace_size(K), 1), dtype=torch.uint8, device=x.device)
-    _dev(workspace, "workspace", torch.uint8)
-    _check(fn(x.data_ptr(), _xdtype(x), B, K, _ptr(signs), block, blocks.data_ptr(), N, out.data_ptr(),
-              workspace.data_ptr(), workspace.numel(), _stream()))
+    _check(fn(x.data_ptr(), _xdtype(x), B, K, _ptr(signs), block, blocks.data_ptr(), N, out.data_ptr(), _stream()))
     return out
 
 
-def tb_pq2_gemv(x, signs, block: int, blocks, out=None, workspace=None):
+def tb_pq2_gemv(x, signs, block: int, blocks, out=None):
     """y (1, N) float32 = Packed linear of x (1, K) on PQ2_0 blocks (uint8
     (N, K/128 * 34) on the GPU)."""
-    return _blocks_gemv(lib().tb_pq2_gemv, PQ2_BLOCK_BYTES, x, signs, block, blocks, out, workspace)
+    return _blocks_gemv(lib().tb_pq2_gemv, PQ2_BLOCK_BYTES, x, signs, block, blocks, out)
 
 
-def tb_ptq1_gemv(x, signs, block: int, blocks, out=None, workspace=None):
+def tb_ptq1_gemv(x, signs, block: int, blocks, out=None):
     """y (1, N) float32 = Packed linear of x (1, K) on PTQ1_0 blocks (uint8
     (N, K/128 * 28) on the GPU)."""
-    return _blocks_gemv(lib().tb_ptq1_gemv, PTQ1_BLOCK_BYTES, x, signs, block, blocks, out, workspace)
+    return _blocks_gemv(lib().tb_ptq1_gemv, PTQ1_BLOCK_BYTES, x, signs, block, blocks, out)

@@ -336,27 +336,22 @@ int tb_ptq1_pack(const int8_t* t, const uint16_t* scales, int64_t N, int64_t K, 
  * if a trit byte is out of range (over 242, or over 26 for a last byte). */
 int tb_ptq1_unpack(const uint8_t* blocks, int64_t N, int64_t K, int8_t* t, uint16_t* scales);
 
-/* Workspace bytes of tb_pq2_gemv / tb_ptq1_gemv for input width K (0 for an
- * invalid K). */
-size_t tb_blocks_gemv_workspace_size(int64_t K);
-
 /* Packed linear on PQ2_0 / PTQ1_0 blocks at batch 1 [P3 "text model
  * loading", with the block decode above]:  y[n] = sum_k W~[n][k] (R x)[k].
  * x: K activations (x_dtype), 16-byte aligned; signs as for tb_ternary_gemv
  * (16-byte aligned); blocks: device, N rows of K/128 blocks, 4-byte aligned
  * (trit bytes are not checked on the device: validate with the host
  * unpack); y: N fp32 (overwritten).  B must be 1 (0 is a no-op; larger
- * batches return TB_ERR_UNSUPPORTED), K a multiple of 256, block 0, 512 or
- * 1024 (2048/4096: TB_ERR_UNSUPPORTED).  workspace: device, at least
- * tb_blocks_gemv_workspace_size(K) bytes, 16-byte aligned, no
- * initialisation needed.  Two launches: the rotated activation's exact
- * integer image into the workspace, then the streaming matmul. */
+ * batches return TB_ERR_UNSUPPORTED), K a multiple of 256 whose operand
+ * image (4.6 KB per 1024 inputs) fits the kernel's LDS beside the band's
+ * partial sums -- every K up to 27648 does, TB_ERR_UNSUPPORTED when it does
+ * not -- and block 0, 512 or 1024
+ * (2048/4096: TB_ERR_UNSUPPORTED).  One launch, no workspace: each
+ * workgroup rotates x into its LDS and streams a band of rows. */
 int tb_pq2_gemv(const void* x, int x_dtype, int64_t B, int64_t K, const int8_t* signs, int block,
-                const uint8_t* blocks, int64_t N, float* y, void* workspace, size_t ws_bytes,
-                void* stream);
+                const uint8_t* blocks, int64_t N, float* y, void* stream);
 int tb_ptq1_gemv(const void* x, int x_dtype, int64_t B, int64_t K, const int8_t* signs, int block,
-                 const uint8_t* blocks, int64_t N, float* y, void* workspace, size_t ws_bytes,
-                 void* stream);
+                 const uint8_t* blocks, int64_t N, float* y, void* stream);
 
 /* Embedding lookup with the inverse transform [P3 "text model loading"]:
  *   out[t] = signs .* (H_L W~[ids[t]]) / sqrt(L)   blockwise  (block > 0)

@@ -76,13 +76,6 @@ def test_ptq1_rejects_invalid_values_and_bytes():
             tb.tb_ptq1_unpack(bad, 256)
 
 
-def test_blocks_gemv_workspace_size():
-    L = tb.lib()
-    assert L.tb_blocks_gemv_workspace_size(5120) >= 5 * 8 * 4 * 128
-    assert L.tb_blocks_gemv_workspace_size(100) == 0
-    assert L.tb_blocks_gemv_workspace_size(384) == 0  # K must be a multiple of 256
-
-
 @pytest.mark.parametrize("fn", ["tb_pq2_gemv", "tb_ptq1_gemv"])
 @pytest.mark.parametrize("kw,status", [
     (dict(B=2), -4),            # batch 1 only
@@ -90,18 +83,15 @@ def test_blocks_gemv_workspace_size():
     (dict(block=300), -3),
     (dict(K=1536 + 128), -2),   # not a multiple of 128 x 2 (256)
     (dict(K=384, block=0, signs=None), -2),
+    (dict(K=34816, block=1024), -4),   # operand image beyond the kernel's LDS
     (dict(blocks=DUMMY + 2), -8),
     (dict(x=DUMMY + 4), -8),
-    (dict(wsb=16), -10),
-    (dict(ws=None), -10),
     (dict(dt=9), -7),
     (dict(blocks=None), -1),
 ])
 def test_blocks_gemv_rejects(fn, kw, status):
-    a = dict(x=DUMMY, dt=tb.TB_BF16, B=1, K=1024, signs=DUMMY, block=1024, blocks=DUMMY, N=32, y=DUMMY, ws=DUMMY,
-             wsb=1 << 20)
+    a = dict(x=DUMMY, dt=tb.TB_BF16, B=1, K=1024, signs=DUMMY, block=1024, blocks=DUMMY, N=32, y=DUMMY)
     a.update(kw)
     f = getattr(tb.lib(), fn)
-    assert f(a["x"], a["dt"], a["B"], a["K"], a["signs"], a["block"], a["blocks"], a["N"], a["y"], a["ws"], a["wsb"],
-             None) == status
-    assert f(DUMMY, tb.TB_BF16, 0, 1024, DUMMY, 1024, None, 32, None, None, 0, None) == 0  # B = 0: no-op
+    assert f(a["x"], a["dt"], a["B"], a["K"], a["signs"], a["block"], a["blocks"], a["N"], a["y"], None) == status
+    assert f(DUMMY, tb.TB_BF16, 0, 1024, DUMMY, 1024, None, 32, None, None) == 0  # B = 0: no-op
