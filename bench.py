@@ -171,6 +171,21 @@ GEMV_DTYPE = ("int8 MFMA on exact limbs of the rotated activation (4 x 8 bits, ~
               "int32 accumulate, fp32 scale/bias epilogue")
 
 
+WARM_SECONDS = 0.1
+
+
+def _warm(torch, g, seconds=WARM_SECONDS):
+    """Replay graph g (untimed) until `seconds` of wall time have passed: the
+    GPU runs its first tens of milliseconds after an idle spell (the oracle's
+    CPU work, setup) about 5% slow, so every timed region is preceded by this
+    much of its own work on top of the requested warm-up steps."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        g.replay()
+        torch.cuda.synchronize()
+
+
 def _time_graph(torch, g, n_replays, spacer=None):
     """Seconds for n_replays back-to-back replays of graph g, from HIP events
     on the stream.  With a spacer graph, one untimed replay of it is enqueued
@@ -308,6 +323,7 @@ def sweep_measure(n_steps, with_cpu, with_context):
     with torch.cuda.graph(g):
         step()
     g.replay()
+    _warm(torch, g)
     nrep = max(3, min(n_steps, 50))
     sec = _time_graph(torch, g, nrep, spacer=g) / nrep
     wbytes = sum(N * K * 9 // 32 for (_, N, K, kind) in mods if kind == "linear")
@@ -320,6 +336,7 @@ def sweep_measure(n_steps, with_cpu, with_context):
         with torch.cuda.graph(gl):
             tb.tb_ternary_gemv_multi(pl, pd, ws)
         gl.replay()
+        _warm(torch, gl, 0.05)
         return _time_graph(torch, gl, reps, spacer=gl) / reps * 1e6
 
     layer_of = lambda m: int(m[0].split(".")[1]) if m[0].startswith("layers.") else -1
@@ -370,6 +387,7 @@ def sweep_measure(n_steps, with_cpu, with_context):
             for i in range(len(mods)):
                 call(i)
         gsep.replay()
+        _warm(torch, gsep, 0.05)
         r = max(3, min(n_steps, 20))
         sep = _time_graph(torch, gsep, r, spacer=gsep) / r
         out["separate_calls_ms"] = round(sep * 1e3, 4)
@@ -441,6 +459,7 @@ def formats_measure(p, reps_per_graph=None, replays=10):
             for i in range(R):
                 format_step(fmt, x, sg, p.block, reps[i], y, ws)
         g.replay()
+        _warm(torch, g, 0.05)
         us = _time_graph(torch, g, replays, spacer=g) / (replays * R) * 1e6
         gbs = wbytes / (us * 1e-6) / 1e9
         out[fmt] = {"bits_per_weight": bits, "weight_bytes": wbytes, "us": round(us, 3), "GB/s": round(gbs, 1),
@@ -558,7 +577,7 @@ def run_gemv(args):
         g_steps.replay()
     if g_rem is not None:
         g_rem.replay()
-    torch.cuda.synchronize()
+    _warm(torch, g_steps)
 
     # Timed: exactly `steps` steps, queued behind untimed replays of the ring
     # so that they run back to back from the start event on.  A graph replay
@@ -603,6 +622,7 @@ def run_gemv(args):
     reps_k = max(1, min(20, args.steps // R))
     g_two = capture(R, False)
     g_two.replay()
+    _warm(torch, g_two, 0.05)
     two_us = _time_graph(torch, g_two, reps_k, spacer=g_two) / (reps_k * R) * 1e6
     g_hot = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_hot):
@@ -710,6 +730,7 @@ def run_prefill(args):
     for _ in range(max(1, warm // 10)):
         g.replay()
     g2.replay()
+    _warm(torch, g)
     nrep = steps // 10
     t = _time_graph(torch, g, nrep, spacer=g) / steps
     t_run = _time_graph(torch, g2, nrep, spacer=g2) / steps

@@ -209,27 +209,40 @@ __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __
     int ip = 0, it = 0;  // pair and tile of the next step to load
     const int lane_c = (ta - md.tile0 + wave) * M * RB + c * RB + lg * 32;
     const int lane_s = ((ta - md.tile0 + wave) * M + c) * G * 2;
-    auto load = [&](int k, MultiPair& st) {
+    // The scales and biases of a round of P = 4 consecutive steps travel with
+    // the round's first slot: lane group lg loads the 16 bytes of step
+    // k + lg for its row (the 8 fp16 of the step's 8 groups), so the row's 4
+    // lanes read one contiguous run when the steps share a tile.  The lanes
+    // exchange them when the round is consumed.
+    auto load = [&](int k, MultiPair& st, bool round_head) {
       const bool live = k < nsteps;
       const int oc = live ? lane_c + it * (NW * M * RB) + ip * 256 : kOob;
-      const int os = live ? lane_s + it * (NW * M * G * 2) + ip * 16 : kOob;
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         const v4u u = __builtin_amdgcn_raw_buffer_load_b128(rc, oc + (h >> 1) * 128 + (h & 1) * 16, 0, 0);
         st.w[h] = make_uint4(u.x, u.y, u.z, u.w);
       }
-      const v4u us = __builtin_amdgcn_raw_buffer_load_b128(rs, os, 0, 0);
-      const v4u ub = __builtin_amdgcn_raw_buffer_load_b128(rb, os, 0, 0);
-      st.s = make_uint4(us.x, us.y, us.z, us.w);
-      st.b = make_uint4(ub.x, ub.y, ub.z, ub.w);
+      if (round_head) {
+        int jp = ip + lg, jt = it;
+        while (jp >= P2) {
+          jp -= P2;
+          ++jt;
+        }
+        const int os = k + lg < nsteps ? lane_s + jt * (NW * M * G * 2) + jp * 16 : kOob;
+        const v4u us = __builtin_amdgcn_raw_buffer_load_b128(rs, os, 0, 0);
+        const v4u ub = __builtin_amdgcn_raw_buffer_load_b128(rb, os, 0, 0);
+        st.s = make_uint4(us.x, us.y, us.z, us.w);
+        st.b = make_uint4(ub.x, ub.y, ub.z, ub.w);
+      }
       if (++ip == P2) {
         ip = 0;
         ++it;
       }
     };
+    static_assert(P % 4 == 0, "a round of scale loads covers 4 ring slots");
     MultiPair ring[P];
 #pragma unroll
-    for (int k = 0; k < P; ++k) load(k, ring[k]);
+    for (int k = 0; k < P; ++k) load(k, ring[k], k % 4 == 0);
 
     uint4 av[kWordsPerGroup];
 #pragma unroll
@@ -271,17 +284,53 @@ __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __
       // groups past K (padding of the last span) contribute nothing
       yacc += s * GPS + lg < G ? sc * (v * xf.y) + bi * xf.x : 0.f;
     };
+    // Step sl of a round needs, from lane group sl of its row, dword
+    // (lg >> 1) of the step's 8 halves for the pair's first span and dword
+    // 2 + (lg >> 1) for its second (the lane's group is 8 p + lg / 8 p + 4 + lg).
+    // Lanes pass that pair of dwords on with the lane-group swaps: a swap of
+    // 16 lanes links lane groups of the same class (lg >> 1), a swap of 32
+    // lanes the other class, so each lane sends the class's pair it will be
+    // read for.  sN / bN: the scale / bias dwords from lane group lg ^ N.
+    const bool k1 = lg >= 2;
+    uint32_t s0x = 0, s0y = 0, s1x = 0, s1y = 0, s2x = 0, s2y = 0, s3x = 0, s3y = 0;
+    uint32_t b0x = 0, b0y = 0, b1x = 0, b1y = 0, b2x = 0, b2y = 0, b3x = 0, b3y = 0;
+    auto xl = [&](uint32_t v, int j) { return static_cast<uint32_t>(xor_lane_i(static_cast<int>(v), j, lane)); };
     for (int base = 0; base < nsteps; base += P) {
 #pragma unroll
       for (int sl = 0; sl < P; ++sl) {
         const MultiPair cur = ring[sl];
-        load(base + sl + P, ring[sl]);  // refill the slot before computing on its data
+        if (sl % 4 == 0) {
+          const uint32_t osx = k1 ? cur.s.y : cur.s.x, osy = k1 ? cur.s.w : cur.s.z;  // own class
+          const uint32_t tsx = k1 ? cur.s.x : cur.s.y, tsy = k1 ? cur.s.z : cur.s.w;  // other class
+          const uint32_t obx = k1 ? cur.b.y : cur.b.x, oby = k1 ? cur.b.w : cur.b.z;
+          const uint32_t tbx = k1 ? cur.b.x : cur.b.y, tby = k1 ? cur.b.z : cur.b.w;
+          s0x = osx;
+          s0y = osy;
+          s1x = xl(osx, 4);
+          s1y = xl(osy, 4);
+          s2x = xl(tsx, 5);
+          s2y = xl(tsy, 5);
+          s3x = xl(xl(tsx, 4), 5);
+          s3y = xl(xl(tsy, 4), 5);
+          b0x = obx;
+          b0y = oby;
+          b1x = xl(obx, 4);
+          b1y = xl(oby, 4);
+          b2x = xl(tbx, 5);
+          b2y = xl(tby, 5);
+          b3x = xl(xl(tbx, 4), 5);
+          b3y = xl(xl(tby, 4), 5);
+        }
+        load(base + sl + P, ring[sl], sl % 4 == 0);  // refill the slot before computing on its data
         if (base + sl < nsteps) {
-          // dwords (lg >> 1) and 2 + (lg >> 1) of the 8 halves hold the
-          // lane's group in the pair's first and second span
-          const bool hi = lg >= 2;
-          span(2 * p, cur.w[0], cur.w[1], hi ? cur.s.y : cur.s.x, hi ? cur.b.y : cur.b.x);
-          if (2 * p + 1 < S) span(2 * p + 1, cur.w[2], cur.w[3], hi ? cur.s.w : cur.s.z, hi ? cur.b.w : cur.b.z);
+          const int m = lg ^ (sl & 3);  // this step's halves came from lane group sl % 4
+          const bool m0 = m & 1, m1 = m & 2;
+          const uint32_t sdx = m1 ? (m0 ? s3x : s2x) : (m0 ? s1x : s0x);
+          const uint32_t sdy = m1 ? (m0 ? s3y : s2y) : (m0 ? s1y : s0y);
+          const uint32_t bdx = m1 ? (m0 ? b3x : b2x) : (m0 ? b1x : b0x);
+          const uint32_t bdy = m1 ? (m0 ? b3y : b2y) : (m0 ? b1y : b0y);
+          span(2 * p, cur.w[0], cur.w[1], sdx, bdx);
+          if (2 * p + 1 < S) span(2 * p + 1, cur.w[2], cur.w[3], sdy, bdy);
           if (++p == P2) {
             // tile done: add the 4 lane groups and park its rows
             float t = yacc + xor_lane(yacc, 4, lane);
