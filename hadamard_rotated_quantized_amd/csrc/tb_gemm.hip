@@ -421,34 +421,24 @@ __device__ __forceinline__ uint8_t* mx_stage() {
   else return mx_stage2;
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint8_t*)(p)));
-}
-
 // Raw buffer resource (stride 0, range checked against `bytes`) as the four
 // scalar words the buffer instructions take.
-typedef int v4i_rs __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t v4i_rs;
 __device__ __forceinline__ v4i_rs rsrc_words(const void* base, int bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return v4i_rs{static_cast<int>(static_cast<uint32_t>(a)), static_cast<int>(static_cast<uint32_t>(a >> 32)), bytes,
-                kRsrcW3};
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcW3);
 }
 
 // Direct-to-LDS buffer loads: lane l's 16 (or 4) bytes at voff land at LDS
-// address lds + 16 l (4 l).  Written as assembly so that the stage ring's
-// waits are the kernel's own s_waitcnt vmcnt(n): the ring keeps one fill in
-// flight across the barrier, which the compiler's conservative LDS tracking
-// would otherwise drain.  M0 holds the LDS base; the compiler reserves M0
-// and nothing else in these kernels uses it.
-__device__ __forceinline__ void dma16(v4i_rs r, uint32_t lds, int voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff),
-               "s"(r)
-               : "memory");
+// address lds + 16 l (4 l).  The destination keeps the provenance of its
+// stage array (mx_stage0/1/2 are separate LDS objects), so the compiler's
+// wait tracking sees that a fill of one stage does not alias the reads of
+// another and the ring's own s_waitcnt vmcnt(n) sets the pace.
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_u8* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, 0, 0, 0);
 }
-__device__ __forceinline__ void dma4(v4i_rs r, uint32_t lds, int voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds), "v"(voff),
-               "s"(r)
-               : "memory");
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, lds_u8* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, voff, 0, 0, 0);
 }
 
 // s_waitcnt vmcnt(n) with the other counters left alone
@@ -577,7 +567,7 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
   // A fill past the last group loads zeros (offsets out of range).
   auto fill = [&](auto stage_tag, int g) {
     constexpr int ST = decltype(stage_tag)::value;
-    const uint32_t dst = lds_addr(mx_stage<ST>());
+    lds_u8* const dst = (lds_u8*)(mx_stage<ST>());
     const bool live = g < gend;
 #pragma unroll
     for (int i = 0; i < kDmaSlots; ++i) {
@@ -589,7 +579,7 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
       } else if (slot_kind[i] == 2) {
         dma4(rs, dst + kStageA + kStageC + (q - kCDma) * 256, live ? ((voff[i] + g) >> 1) * 4 : kOobOff);
       } else {
-        dma4(rs, lds_addr(mx_sink), kOobOff);
+        dma4(rs, (lds_u8*)(mx_sink), kOobOff);
       }
     }
   };
