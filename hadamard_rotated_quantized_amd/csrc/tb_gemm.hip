@@ -70,7 +70,8 @@ constexpr int kStageBytes = kStageA + kStageC + kStageS;  // 44032 B per stage, 
 constexpr int kADma = kStageA / 1024;         // 25 direct-to-LDS loads of 1 KB (64 lanes x 16 B)
 constexpr int kCDma = kADma + kStageC / 1024; // codes: loads 25 .. 40
 constexpr int kSDma = kCDma + kStageS / 256;  // scales: loads 41 .. 48 (64 lanes x 4 B)
-constexpr int kDmaSlots = 7;                  // per wave and fill (56 slots, 7 of them padding)
+constexpr int kDmaSlots = 7;                  // load slots per wave and fill (56 slots, 7 of them padding)
+constexpr int kFillLoads = 8;                 // loads per wave and fill (slot 5 is issued as two loads)
 constexpr int kXcds = 8;
 constexpr int kMxBandRows = 8;               // row tiles per band of the tile order
 constexpr int kMxMaxSlices = 8;              // K slices per tail tile at most
@@ -445,11 +446,13 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, lds_u8* lds, int 
 __host__ __device__ constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
 // Operands of one k-step for one wave, read from a stage: the run's 6 units
-// (4 digits x 24 B), its scale dword, the two code words of each column
-// block, and (second k-step only) the scale dwords of the lane's columns.
+// (4 digits x 24 B), its scale dword, (first k-step only) the four code
+// words of each column block that both k-steps use (words 4h .. 4h + 3 of
+// the group: x, y for k-step 0, z, w for k-step 1), and (second k-step only)
+// the scale dwords of the lane's columns.
 struct MxOps {
   v4u_g a[6];
-  v2u_g c[4];
+  v4u_g c[4];
   int sc;
   uint32_t sd[4];
 };
@@ -532,29 +535,25 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
 
   // Stage fill: 49 direct-to-LDS loads; wave w issues loads w + 8 i, i < 7.
   // Load q < 25 brings activation units 64 q + lane (unit p is record row
-  // p / 25, unit p % 25); loads 25 .. 40 bring code units, LDS unit
-  // pos = 64 (q - 25) + lane holding row pos / 2, half (pos & 1) ^ bit 2 of
-  // the row; loads 41 .. 48 bring the scale dword of column 64 (q - 41) + lane;
-  // loads 49 .. 55 are padding (out of range: zeros into mx_sink).
+  // p / 25, unit p % 25); loads 25 .. 40 bring code units: LDS unit
+  // pos = 64 (q - 25) + lane holds half (pos & 1) ^ x of column n = pos / 2,
+  // x = bit 2 ^ bit 3 of n, so that the 16-byte reads of 16 consecutive
+  // columns fall on distinct banks; loads 41 .. 48 bring the scale dword of
+  // column 64 (q - 41) + lane; loads 49 .. 55 are padding.
   int voff[kDmaSlots];
-  int slot_kind[kDmaSlots];  // 0 activation, 1 codes, 2 scales, 3 padding (uniform)
 #pragma unroll
   for (int i = 0; i < kDmaSlots; ++i) {
     const int q = wave + 8 * i;
     if (q < kADma) {
       const int p = 64 * q + lane;
       voff[i] = (p / kRecUnits) * G * kRecBytes + (p % kRecUnits) * 16;
-      slot_kind[i] = 0;
     } else if (q < kCDma) {
       const int pos = 64 * (q - kADma) + lane, n = pos >> 1;
-      voff[i] = n * W * 4 + (((pos & 1) ^ ((n >> 2) & 1)) * 16);
-      slot_kind[i] = 1;
+      voff[i] = n * W * 4 + (((pos & 1) ^ (((n >> 2) ^ (n >> 3)) & 1)) * 16);
     } else if (q < kSDma) {
       voff[i] = shalf0 + (64 * (q - kCDma) + lane) * G;  // half index of s[n][0] from the resource base
-      slot_kind[i] = 2;
     } else {
       voff[i] = kOobOff;
-      slot_kind[i] = 3;
     }
   }
   // lane's own columns: which half of the staged dword is s[n][g] (flips with g)
@@ -562,32 +561,35 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) spar[nb] = (shalf0 + (wn * 128 + 32 * nb + r32) * G) & 1;
 
-  // Every wave issues exactly kDmaSlots loads per fill (padding included), so
-  // one s_waitcnt vmcnt(kDmaSlots) leaves exactly the newest fill in flight.
-  // A fill past the last group loads zeros (offsets out of range).
+  // Every wave issues exactly kFillLoads loads per fill, so one
+  // s_waitcnt vmcnt(kFillLoads) leaves exactly the newest fill in flight.
+  // Slots 0-2 are activation units for every wave and slot 4 code units;
+  // the kinds of slots 3, 5 and 6 depend on the wave (3: activation for wave
+  // 0, codes otherwise; 5: codes for wave 0, scales otherwise; 6: scales for
+  // wave 0, padding otherwise) and are chosen with wave-uniform selects of
+  // the source and the LDS target, so the fill has no branches: slot 5 is
+  // issued as a 16-byte and a 4-byte load, one of them aimed at mx_sink with
+  // an out-of-range offset.  A fill past the last group loads zeros.
+  const bool w0 = wave == 0;
   auto fill = [&](auto stage_tag, int g) {
     constexpr int ST = decltype(stage_tag)::value;
     lds_u8* const dst = (lds_u8*)(mx_stage<ST>());
+    lds_u8* const sink = (lds_u8*)(mx_sink);
     const bool live = g < gend;
 #pragma unroll
-    for (int i = 0; i < kDmaSlots; ++i) {
-      const int q = wave + 8 * i;
-      if (slot_kind[i] == 0) {
-        dma16(ra, dst + q * 1024, live ? voff[i] + g * kRecBytes : kOobOff);
-      } else if (slot_kind[i] == 1) {
-        dma16(rc, dst + q * 1024, live ? voff[i] + g * 32 : kOobOff);
-      } else if (slot_kind[i] == 2) {
-        dma4(rs, dst + kStageA + kStageC + (q - kCDma) * 256, live ? ((voff[i] + g) >> 1) * 4 : kOobOff);
-      } else {
-        dma4(rs, (lds_u8*)(mx_sink), kOobOff);
-      }
-    }
+    for (int i = 0; i < 3; ++i) dma16(ra, dst + (wave + 8 * i) * 1024, live ? voff[i] + g * kRecBytes : kOobOff);
+    dma16(w0 ? ra : rc, dst + (wave + 24) * 1024, live ? voff[3] + g * (w0 ? kRecBytes : 32) : kOobOff);
+    dma16(rc, dst + (wave + 32) * 1024, live ? voff[4] + g * 32 : kOobOff);
+    dma16(rc, w0 ? dst + 40 * 1024 : sink, live && w0 ? voff[5] + g * 32 : kOobOff);
+    dma4(rs, w0 ? sink : dst + kStageA + kStageC + (wave - 1) * 256,
+         live && !w0 ? ((voff[5] + g) >> 1) * 4 : kOobOff);
+    dma4(rs, w0 ? dst + kStageA + kStageC + 7 * 256 : sink, live && w0 ? ((voff[6] + g) >> 1) * 4 : kOobOff);
   };
 
   // LDS read positions of this lane: record row, and the code unit of column
-  // block 0 (bit 2 of the column is that of r32 in every block)
+  // block 0 (bits 2 and 3 of the column are those of r32 in every block)
   const int arow = (wm * 32 + r32) * kRecBytes;
-  const int cread = kStageA + (2 * (wn * 128 + r32) + (h ^ ((r32 >> 2) & 1))) * 16;  // + 1024 per block
+  const int cread = kStageA + (2 * (wn * 128 + r32) + (h ^ (((r32 >> 2) ^ (r32 >> 3)) & 1))) * 16;  // + 1024 per block
 
   v16f_g yv[4];
 #pragma unroll
@@ -607,18 +609,20 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
   auto read_c = [&](auto stage_tag, int s, MxOps& o, bool with_scales) {
     constexpr int ST = decltype(stage_tag)::value;
     const uint8_t* S = mx_stage<ST>();
+    if (s == 0) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) o.c[nb] = *reinterpret_cast<const v2u_g*>(S + cread + 1024 * nb + 8 * s);
+      for (int nb = 0; nb < 4; ++nb) o.c[nb] = *reinterpret_cast<const v4u_g*>(S + cread + 1024 * nb);
+    }
     if (with_scales) {
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
         o.sd[nb] = *reinterpret_cast<const uint32_t*>(S + kStageA + kStageC + 4 * (wn * 128 + 32 * nb + r32));
     }
   };
-  auto decode = [&](const MxOps& o, v8i_g* bop) {
+  auto decode = [&](const MxOps& o, v8i_g* bop, int ks) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      const uint32_t wa = o.c[nb].x, wb = o.c[nb].y;
+      const uint32_t wa = ks ? o.c[nb].z : o.c[nb].x, wb = ks ? o.c[nb].w : o.c[nb].y;
       bop[nb] = v8i_g{static_cast<int>(wa & kFp4Codes), static_cast<int>((wa >> 2) & kFp4Codes),
                       static_cast<int>(wb & kFp4Codes), static_cast<int>((wb >> 2) & kFp4Codes), 0, 0, 0, 0};
     }
@@ -636,7 +640,7 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
   // group g - 1, whose reads all completed before the previous barrier.
   fill(std::integral_constant<int, 0>{}, gbeg);
   fill(std::integral_constant<int, 1>{}, gbeg + 1);
-  __builtin_amdgcn_s_waitcnt(wait_vm(kDmaSlots));
+  __builtin_amdgcn_s_waitcnt(wait_vm(kFillLoads));
   __builtin_amdgcn_s_barrier();
   MxOps r0;
   read_a(std::integral_constant<int, 0>{}, 0, r0, 0);
@@ -649,7 +653,7 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
     MxOps r1;
     v8i_g bop[4];
     v16f_g acc[4];
-    decode(r0, bop);
+    decode(r0, bop, 0);
     mx_digit<0>(r0.a, bop, r0.sc, true, acc);
     __builtin_amdgcn_sched_barrier(0);
     read_a(stage_tag, 1, r1, 0);
@@ -670,9 +674,9 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
     // every read of this wave done (the refill of the next-but-one group
     // targets what other waves read before this barrier) and this wave's
     // part of the next group's stage landed
-    __builtin_amdgcn_s_waitcnt(wait_vm(kDmaSlots) & ~(0xF << 8));
+    __builtin_amdgcn_s_waitcnt(wait_vm(kFillLoads) & ~(0xF << 8));
     __builtin_amdgcn_s_barrier();
-    decode(r1, bop);
+    decode(r0, bop, 1);
     mx_digit<0>(r1.a, bop, r1.sc, false, acc);
     __builtin_amdgcn_sched_barrier(0);
     read_a(next, 0, r0, 0);
