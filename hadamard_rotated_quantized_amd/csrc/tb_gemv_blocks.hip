@@ -11,12 +11,13 @@
 //   y[n] = sum_g d[n][g] (sum_{k in g} (c[n][k] - 1) xr[k])
 //        = sum_g d[n][g] (f_g sum_k c q_k - X_g),   xr ~= f_g q (exact limbs)
 //
-// One launch, one workgroup per band of about N / CUs rows (whole 16-row
-// tiles).  Each workgroup first issues the first block loads of its waves,
-// then rotates the activation itself: its waves transform the 1024-input
-// chunks on the matrix cores and split them exactly into four limbs, writing
-// the operand image and the group terms (X_g, f_g) straight to LDS
-// (tb_xform.h).  The band's work is (tile, span) items, a span being 4
+// One launch, one workgroup per band of ceil(N / CUs) rows (tiles of 16
+// rows, the last one possibly partial).  Each wave first issues the
+// activation loads of its chunk transforms, then the block loads of its
+// first items, and rotates the activation itself while the blocks are in
+// flight: the waves transform the 1024-input chunks on the matrix cores and
+// split them exactly into four limbs, writing the operand image and the
+// group terms (X_g, f_g) straight to LDS (tb_xform.h).  The band's work is (tile, span) items, a span being 4
 // groups of the tile's 16 rows; each wave takes a contiguous range of items.
 // Lane (lane group lg, row c) loads the whole block (row c, group 4 s + lg)
 // with dword-aligned loads, rebuilds its eight 16-code words in registers
@@ -38,6 +39,7 @@ constexpr int kBlkThreads = 64 * kBlkWaves;
 constexpr int kBlkArow = 144;                        // LDS bytes per (group, limb) operand row
 constexpr int kBlkRing = 4;                          // items of loads in flight per wave
 constexpr int kBlkMaxTiles = 48;                     // tiles of a band (LDS of the partial sums)
+constexpr int kBlkMaxTasks = 3;                      // chunk transforms per wave loaded up front
 constexpr int64_t kBlkLdsMax = 150 * 1024;
 
 enum BlockFormat { kPq2 = 0, kPtq1 = 1 };
@@ -116,7 +118,7 @@ template <int L, int DT, int FMT, int P>
 __global__ __launch_bounds__(kBlkThreads, 1) void blocks_gemv_kernel(const void* __restrict__ x,
                                                                       const int8_t* __restrict__ signs,
                                                                       const uint8_t* __restrict__ blocks, int N, int K,
-                                                                      float* __restrict__ y) {
+                                                                      int R, float* __restrict__ y) {
   constexpr int NW = kBlkWaves, M = 16, GPS = 4, BB = BlkFmt<FMT>::BYTES;
   extern __shared__ uint4 blk_lds_dyn[];
   char* const lds = reinterpret_cast<char*>(blk_lds_dyn);
@@ -131,24 +133,41 @@ __global__ __launch_bounds__(kBlkThreads, 1) void blocks_gemv_kernel(const void*
   uint32_t* const lut = reinterpret_cast<uint32_t*>(lds + blk_lds_lut(nch));
   float* const red = reinterpret_cast<float*>(lds + blk_lds_red(nch));
 
-  // the band: tiles ta .. tb - 1; items i = (tile - ta) S + span; this
-  // wave's items i0 .. i1 - 1
-  const int T = (N + M - 1) / M;
-  const int bid = static_cast<int>(blockIdx.x), grid = static_cast<int>(gridDim.x);
-  const int ta = static_cast<int>(static_cast<int64_t>(bid) * T / grid);
-  const int tb = static_cast<int>(static_cast<int64_t>(bid + 1) * T / grid);
-  const int items = (tb - ta) * S;
+  // the band: rows band0 .. band0 + nrow - 1 in tiles of 16 (the last may be
+  // partial); items i = t S + s; this wave's items i0 .. i1 - 1
+  const int band0 = static_cast<int>(blockIdx.x) * R;
+  const int nrow = min(R, N - band0);
+  const int tsub = (nrow + M - 1) / M;
+  const int items = tsub * S;
   const int i0 = items * wave / NW, i1 = items * (wave + 1) / NW;
   const int nit = i1 - i0;
+
+  // 1. the activation loads of this wave's chunk transforms, first: the
+  //    transforms then wait for these alone (loads complete in order)
+  constexpr int ESZ = DT == TB_F32 ? 4 : 2;
+  const auto rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(x), 0, K * ESZ, kRsrcWord3);
+  const auto rsg = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(signs), 0, L > 0 ? K : 0, kRsrcWord3);
+  XformIn<DT> xin[kBlkMaxTasks];
+#pragma unroll
+  for (int r = 0; r < kBlkMaxTasks; ++r) {
+    const int ch = wave + NW * r;
+    if (ch < nch) xform_issue<L, DT>(rx, rsg, static_cast<int64_t>(ch) * 1024, ch * 1024, lane, xin[r]);
+  }
+
+  // 2. the first P items' loads.  Lane (lg, c) loads block (row c of the
+  //    item's tile, group 4 s + lg); rows past the band and items past the
+  //    wave's range read from an offset past every buffer (zeros, no traffic)
   const auto rbl = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blocks), 0, N * G * BB, kRsrcWord3);
   // G is even (K % 256 == 0), so block (row, 4 s + lg) starts at byte
   // 2 (lg & 1) of a dword for PQ2_0; PTQ1_0 blocks are dword aligned
   const int sh = FMT == kPq2 ? 2 * (lg & 1) : 0;
   int lt = i0 / S, ls = i0 - (i0 / S) * S;  // tile (in the band) and span of the next item to load
-  const int lane_b = (ta * M + c) * G * BB + lg * BB - sh;
   int nload = 0;
   auto load = [&](BlkSlot<FMT>& st) {
-    const int off = nload < nit ? lane_b + lt * (M * G * BB) + ls * (GPS * BB) : kOob;
+    const int rib = lt * M + c;  // row in the band
+    const bool live = nload < nit && rib < nrow;
+    const int blk = (band0 + rib) * G + ls * GPS + lg;
+    const int off = live ? blk * BB - sh : kOob;
     const v4u u0 = __builtin_amdgcn_raw_buffer_load_b128(rbl, off, 0, 0);
     st.d[0] = u0.x;
     st.d[1] = u0.y;
@@ -177,27 +196,31 @@ __global__ __launch_bounds__(kBlkThreads, 1) void blocks_gemv_kernel(const void*
 #pragma unroll
   for (int k = 0; k < P; ++k) load(ring[k]);
 
-  // the band's rotation, while the first blocks are in flight: wave w
-  // transforms chunks w, w + 8, ... into the LDS operand image
+  // 3. the band's rotation while the blocks are in flight: wave w transforms
+  //    chunks w, w + 8, ... into the LDS operand image (chunks beyond the
+  //    up-front tasks load and transform in turn)
   {
-    constexpr int ESZ = DT == TB_F32 ? 4 : 2;
-    const auto rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(x), 0, K * ESZ, kRsrcWord3);
-    const auto rsg = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(signs), 0, L > 0 ? K : 0, kRsrcWord3);
     const v4u* cst = reinterpret_cast<const v4u*>(&kXformConst.w[xf_mode<L>()][0][lane][0]);
     const v4u* cst2 = reinterpret_cast<const v4u*>(&kXformConst.w[xf_mode<L>()][1][lane][0]);
     const v4u cf[2] = {cst[0], cst[1]};
     const v4u cs[2] = {cst2[0], cst2[1]};
-    for (int ch = wave; ch < nch; ch += NW) {
+#pragma unroll
+    for (int r = 0; r < kBlkMaxTasks; ++r) {
+      const int ch = wave + NW * r;
+      if (ch < nch) xform_chunk<L, DT>(xin[r], 8 * ch, lane, cf, cs, lds_a, lds_xf, kBlkArow);
+    }
+    for (int ch = wave + NW * kBlkMaxTasks; ch < nch; ch += NW) {
       XformIn<DT> in;
       xform_issue<L, DT>(rx, rsg, static_cast<int64_t>(ch) * 1024, ch * 1024, lane, in);
       xform_chunk<L, DT>(in, 8 * ch, lane, cf, cs, lds_a, lds_xf, kBlkArow);
     }
     if constexpr (FMT == kPtq1)
       for (int i = tid; i < 256; i += kBlkThreads) lut[i] = trit_byte_codes(static_cast<uint32_t>(i));
-    for (int i = tid; i < (tb - ta) * NW * 16; i += kBlkThreads) red[i] = 0.f;
+    for (int i = tid; i < tsub * NW * 16; i += kBlkThreads) red[i] = 0.f;
   }
   __syncthreads();
 
+  // 4. the items
   uint4 av[kWordsPerGroup];
 #pragma unroll
   for (int w = 0; w < kWordsPerGroup; ++w) av[w] = make_uint4(0, 0, 0, 0);
@@ -248,15 +271,14 @@ __global__ __launch_bounds__(kBlkThreads, 1) void blocks_gemv_kernel(const void*
     }
   }
   __syncthreads();
-  // the band's rows: partial sums added in wave order
-  for (int i = tid; i < (tb - ta) * 16; i += kBlkThreads) {
-    const int t = i >> 4, r = i & 15;
-    const int row = (ta + t) * M + r;
-    if (row < N) {
+  // 5. the band's rows: partial sums added in wave order
+  for (int i = tid; i < tsub * 16; i += kBlkThreads) {
+    const int t = i >> 4, r = i & 15, rib = t * M + r;
+    if (rib < nrow) {
       float a = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) a += red[(t * NW + w) * 16 + r];
-      y[row] = a;
+      y[band0 + rib] = a;
     }
   }
 }
@@ -265,18 +287,21 @@ __global__ __launch_bounds__(kBlkThreads, 1) void blocks_gemv_kernel(const void*
 // host side
 // ---------------------------------------------------------------------------
 struct BlkPlan {
-  int grid;
+  int grid, rows;
   int64_t lds;
 };
 
-// One workgroup per CU while the bands' partial sums fit LDS; more (and
-// narrower) bands beyond that.
+// One workgroup per CU, each with a band of ceil(N / CUs) rows (at least one
+// tile), while the bands' partial sums fit LDS; more (and narrower) bands
+// beyond that.
 static BlkPlan blk_plan(int64_t N, int64_t K) {
   BlkPlan p{};
-  const int64_t T = (N + 15) / 16;
-  const int64_t grid = std::max<int64_t>(std::min<int64_t>(T, device_cus()), (T + kBlkMaxTiles - 1) / kBlkMaxTiles);
-  p.grid = static_cast<int>(grid);
-  p.lds = blk_lds_total(blk_nch(static_cast<int>(K)), static_cast<int>((T + grid - 1) / grid));
+  const int64_t cus = device_cus();
+  int64_t rows = std::max<int64_t>(16, (N + cus - 1) / cus);
+  rows = std::min<int64_t>(rows, int64_t(kBlkMaxTiles) * 16);
+  p.rows = static_cast<int>(rows);
+  p.grid = static_cast<int>((N + rows - 1) / rows);
+  p.lds = blk_lds_total(blk_nch(static_cast<int>(K)), static_cast<int>((rows + 15) / 16));
   return p;
 }
 
@@ -286,7 +311,8 @@ static void blocks_launch_t(const void* x, const int8_t* signs, const uint8_t* b
   auto kern = blocks_gemv_kernel<L, DT, FMT, kBlkRing>;
   static std::atomic<uint64_t> lds_set{0};
   lds_limit_once(reinterpret_cast<const void*>(kern), static_cast<int>(kBlkLdsMax), lds_set);
-  hipLaunchKernelGGL(kern, dim3(p.grid), dim3(kBlkThreads), static_cast<size_t>(p.lds), st, x, signs, blocks, N, K, y);
+  hipLaunchKernelGGL(kern, dim3(p.grid), dim3(kBlkThreads), static_cast<size_t>(p.lds), st, x, signs, blocks, N, K,
+                     p.rows, y);
 }
 
 template <int FMT, int L>
