@@ -71,7 +71,10 @@ constexpr int kADma = kStageA / 1024;         // 25 direct-to-LDS loads of 1 KB 
 constexpr int kCDma = kADma + kStageC / 1024; // codes: loads 25 .. 40
 constexpr int kSDma = kCDma + kStageS / 256;  // scales: loads 41 .. 48 (64 lanes x 4 B)
 constexpr int kDmaSlots = 7;                  // load slots per wave and fill (56 slots, 7 of them padding)
-constexpr int kFillLoads = 8;                 // loads per wave and fill (slot 5 is issued as two loads)
+constexpr int kPkRec = kMxBN * 32 + kMxBN * 2;  // packed weights: bytes per (column tile, group)
+constexpr int kPkScaleOff = kMxBN * 32;         // where the tile's 512 fp16 scales start in that record
+// loads per wave and fill: weights as stored (slot 5 issued as two loads) or packed
+__host__ __device__ constexpr int fill_loads(bool packed) { return packed ? 6 : 8; }
 constexpr int kXcds = 8;
 constexpr int kMxBandRows = 8;               // row tiles per band of the tile order
 constexpr int kMxMaxSlices = 8;              // K slices per tail tile at most
@@ -491,11 +494,17 @@ __device__ __forceinline__ void mx_tile_origin(int t, int MT, int NT, int& m0, i
 // groups each, one workgroup per (tile, slice) after the main ones; a tail
 // workgroup writes its 64 x 512 partial sums to part[unit] (slice 0 adds the
 // bias term) and gemm_tail_sum_kernel adds the slices in order.
+//
+// PK: the codes and scales come from the packed copy (gemm_pack_kernel), one
+// contiguous kPkRec-byte record per (column tile, group), instead of the
+// stored rows: every stage-fill load then reads 1 KB of contiguous memory.
+template <bool PK>
 __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
     const uint8_t* __restrict__ rec, const uint16_t* __restrict__ xh, const uint16_t* __restrict__ xl,
     const float* __restrict__ p2, const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
-    const uint16_t* __restrict__ biases, float* __restrict__ y, int M, int N, int G, int Gp, int MT, int NT,
-    int per_xcd, int tiles_main, int ks, float* __restrict__ part, int bvec) {
+    const uint8_t* __restrict__ wpk, const uint16_t* __restrict__ biases, float* __restrict__ y, int M, int N, int G,
+    int Gp, int MT, int NT, int per_xcd, int tiles_main, int ks, float* __restrict__ part, int bvec) {
+  constexpr int kFillLoads = fill_loads(PK);
   // XCD-aware tile order: workgroup w runs on XCD w % 8; XCD x owns the
   // contiguous range [x * per_xcd, (x + 1) * per_xcd) of the tile order, so
   // the workgroups an XCD runs at once (8 row tiles x 4 column tiles) share
@@ -525,7 +534,9 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
   // computed in 32-bit scalar arithmetic: one tile spans kMxBM / kMxBN rows).
   const int mrows = min(M - m0, kMxBM), nrows = min(N - n0, kMxBN);
   const v4i_rs ra = rsrc_words(rec + static_cast<int64_t>(m0) * G * kRecBytes, mrows * G * kRecBytes);
-  const v4i_rs rc = rsrc_words(codes + static_cast<int64_t>(n0) * W, nrows * W * 4);
+  const v4i_rs rc = PK ? rsrc_words(wpk + static_cast<int64_t>(n0 / kMxBN) * G * kPkRec, G * kPkRec)
+                       : rsrc_words(codes + static_cast<int64_t>(n0) * W, nrows * W * 4);
+  const int cstride = PK ? kPkRec : 32;  // code bytes from one group to the next
   // scales: the aligned dword holding s[n][g]; the resource starts at the
   // dword holding s[n0][0] and ends with the dword holding s[N-1][G-1]
   const uint64_t sp = reinterpret_cast<uint64_t>(scales) + static_cast<uint64_t>(n0) * G * 2;
@@ -549,9 +560,11 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
       voff[i] = (p / kRecUnits) * G * kRecBytes + (p % kRecUnits) * 16;
     } else if (q < kCDma) {
       const int pos = 64 * (q - kADma) + lane, n = pos >> 1;
-      voff[i] = n * W * 4 + (((pos & 1) ^ (((n >> 2) ^ (n >> 3)) & 1)) * 16);
+      const int hx = (pos & 1) ^ (((n >> 2) ^ (n >> 3)) & 1);  // the half of column n this unit holds
+      voff[i] = PK ? (2 * n + hx) * 16 : n * W * 4 + hx * 16;
     } else if (q < kSDma) {
-      voff[i] = shalf0 + (64 * (q - kCDma) + lane) * G;  // half index of s[n][0] from the resource base
+      // half index of s[n][0] from the resource base; packed: 8 scales per lane
+      voff[i] = PK ? kPkScaleOff + 16 * lane : shalf0 + (64 * (q - kCDma) + lane) * G;
     } else {
       voff[i] = kOobOff;
     }
@@ -569,7 +582,9 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
   // wave 0, padding otherwise) and are chosen with wave-uniform selects of
   // the source and the LDS target, so the fill has no branches: slot 5 is
   // issued as a 16-byte and a 4-byte load, one of them aimed at mx_sink with
-  // an out-of-range offset.  A fill past the last group loads zeros.
+  // an out-of-range offset.  Packed weights: slot 5 is codes for wave 0 and
+  // the group's 512 scales for wave 1 (one 16-byte load each), slot 6 is not
+  // issued.  A fill past the last group loads zeros.
   const bool w0 = wave == 0;
   auto fill = [&](auto stage_tag, int g) {
     constexpr int ST = decltype(stage_tag)::value;
@@ -578,12 +593,19 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
     const bool live = g < gend;
 #pragma unroll
     for (int i = 0; i < 3; ++i) dma16(ra, dst + (wave + 8 * i) * 1024, live ? voff[i] + g * kRecBytes : kOobOff);
-    dma16(w0 ? ra : rc, dst + (wave + 24) * 1024, live ? voff[3] + g * (w0 ? kRecBytes : 32) : kOobOff);
-    dma16(rc, dst + (wave + 32) * 1024, live ? voff[4] + g * 32 : kOobOff);
-    dma16(rc, w0 ? dst + 40 * 1024 : sink, live && w0 ? voff[5] + g * 32 : kOobOff);
-    dma4(rs, w0 ? sink : dst + kStageA + kStageC + (wave - 1) * 256,
-         live && !w0 ? ((voff[5] + g) >> 1) * 4 : kOobOff);
-    dma4(rs, w0 ? dst + kStageA + kStageC + 7 * 256 : sink, live && w0 ? ((voff[6] + g) >> 1) * 4 : kOobOff);
+    dma16(w0 ? ra : rc, dst + (wave + 24) * 1024, live ? voff[3] + g * (w0 ? kRecBytes : cstride) : kOobOff);
+    dma16(rc, dst + (wave + 32) * 1024, live ? voff[4] + g * cstride : kOobOff);
+    if constexpr (PK) {
+      // slot 5: codes for wave 0, all 512 scales (16 B per lane) for wave 1
+      const bool w1 = wave == 1;
+      dma16(rc, w0 ? dst + 40 * 1024 : (w1 ? dst + kStageA + kStageC : sink),
+            live && (w0 || w1) ? voff[5] + g * kPkRec : kOobOff);
+    } else {
+      dma16(rc, w0 ? dst + 40 * 1024 : sink, live && w0 ? voff[5] + g * 32 : kOobOff);
+      dma4(rs, w0 ? sink : dst + kStageA + kStageC + (wave - 1) * 256,
+           live && !w0 ? ((voff[5] + g) >> 1) * 4 : kOobOff);
+      dma4(rs, w0 ? dst + kStageA + kStageC + 7 * 256 : sink, live && w0 ? ((voff[6] + g) >> 1) * 4 : kOobOff);
+    }
   };
 
   // LDS read positions of this lane: record row, and the code unit of column
@@ -616,7 +638,8 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
     if (with_scales) {
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
-        o.sd[nb] = *reinterpret_cast<const uint32_t*>(S + kStageA + kStageC + 4 * (wn * 128 + 32 * nb + r32));
+        o.sd[nb] = PK ? *reinterpret_cast<const uint16_t*>(S + kStageA + kStageC + 2 * (wn * 128 + 32 * nb + r32))
+                      : *reinterpret_cast<const uint32_t*>(S + kStageA + kStageC + 4 * (wn * 128 + 32 * nb + r32));
     }
   };
   auto decode = [&](const MxOps& o, v8i_g* bop, int ks) {
@@ -694,7 +717,7 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const uint32_t sd = r1.sd[nb];
-      const float sv = half_bits_to_float(static_cast<uint16_t>((spar[nb] ^ (g & 1)) ? sd >> 16 : sd));
+      const float sv = half_bits_to_float(static_cast<uint16_t>(!PK && (spar[nb] ^ (g & 1)) ? sd >> 16 : sd));
 #pragma unroll
       for (int r = 0; r < 16; ++r) yv[nb][r] = fmaf(sv, acc[nb][r], yv[nb][r]);
     }
@@ -801,6 +824,34 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
       }
     }
   }
+}
+
+// The packed copy of the weights for gemm_mx_kernel<true>: per (column tile
+// nt of 512 rows, group g) one record of kPkRec bytes at (nt G + g) kPkRec:
+// the 512 rows' 32 code bytes of group g in row order, then their 512 fp16
+// scales.  Rows past N are zeros.  One thread per 16-byte unit of a record.
+__global__ __launch_bounds__(256) void gemm_pack_kernel(const uint32_t* __restrict__ codes,
+                                                        const uint16_t* __restrict__ scales, int N, int G,
+                                                        int64_t units, uint8_t* __restrict__ wpk) {
+  constexpr int kUnits = kPkRec / 16;  // 1088: 1024 of codes, 64 of scales
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= units) return;
+  const int64_t r = i / kUnits;
+  const int u = static_cast<int>(i - r * kUnits);
+  const int nt = static_cast<int>(r / G), g = static_cast<int>(r - static_cast<int64_t>(nt) * G);
+  const int W = G * 8;
+  v4u_g v = {0u, 0u, 0u, 0u};
+  if (u < 1024) {
+    const int n = nt * kMxBN + (u >> 1);
+    if (n < N) v = *reinterpret_cast<const v4u_g*>(codes + static_cast<int64_t>(n) * W + g * 8 + (u & 1) * 4);
+  } else {
+    const int n0 = nt * kMxBN + 8 * (u - 1024);
+    uint32_t h[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[j] = n0 + j < N ? scales[static_cast<int64_t>(n0 + j) * G + g] : 0u;
+    v = v4u_g{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+  }
+  *reinterpret_cast<v4u_g*>(wpk + r * kPkRec + u * 16) = v;
 }
 
 // y of the tail tiles: the ks slice partials of each element added in slice
@@ -946,20 +997,33 @@ static void gemm_prepare_launch(const void* x, int x_dtype, int64_t M, int64_t K
 // T mod CUs tiles are cut into ks = CUs / (T mod CUs) slices of the groups
 // (at most kMxMaxSlices, at least 2 groups each), whose partial tiles follow
 // the prepared activation in the workspace.
+//
+// With at least kPkMinRowTiles row tiles (each of which streams all the
+// weights), the run also packs the codes and scales into one contiguous
+// record per (column tile, group) after the partial tiles (gemm_pack_kernel,
+// NT x G x kPkRec bytes) and the matmul reads that copy.
+constexpr int kPkMinRowTiles = 4;
 struct GemmSplit {
-  int64_t tiles_main, tiles_tail, ks, part_off, total;
+  int64_t tiles_main, tiles_tail, ks, part_off, pk_off, total;
+  bool pk;
 };
 static GemmSplit gemm_split_plan(int64_t M, int64_t K, int64_t N, int cus) {
   const GemmWs lay = gemm_ws_layout(M, K);
-  const int64_t T = ((M + kMxBM - 1) / kMxBM) * ((N + kMxBN - 1) / kMxBN);
+  const int64_t MT = (M + kMxBM - 1) / kMxBM, NT = (N + kMxBN - 1) / kMxBN;
+  const int64_t T = MT * NT;
   const int64_t rem = cus > 0 ? T % cus : 0;
   const int64_t ks = rem > 0 ? std::min<int64_t>(cus / rem, kMxMaxSlices) : 0;
-  GemmSplit sp{T, 0, 1, lay.total, lay.total};
+  GemmSplit sp{T, 0, 1, lay.total, lay.total, lay.total, false};
   if (T > cus && rem > 0 && ks >= 2 && lay.G >= 2 * ks) {
     sp.tiles_main = T - rem;
     sp.tiles_tail = rem;
     sp.ks = ks;
     sp.total = sp.part_off + rem * ks * kMxBM * kMxBN * 4;
+  }
+  if (MT >= kPkMinRowTiles) {
+    sp.pk = true;
+    sp.pk_off = g_align256(sp.total);
+    sp.total = sp.pk_off + NT * lay.G * kPkRec;
   }
   return sp;
 }
@@ -974,15 +1038,22 @@ static void gemm_run_launch(const void* workspace, size_t ws_bytes, int64_t M, i
   const float* p2 = reinterpret_cast<const float*>(ws + lay.p2_off);
   const int64_t MT = (M + kMxBM - 1) / kMxBM, NT = (N + kMxBN - 1) / kMxBN;
   GemmSplit sp = gemm_split_plan(M, K, N, device_cus());
-  if (ws_bytes < static_cast<size_t>(sp.total)) sp = GemmSplit{MT * NT, 0, 1, lay.total, lay.total};
+  if (ws_bytes < static_cast<size_t>(sp.total))
+    sp = GemmSplit{MT * NT, 0, 1, lay.total, lay.total, lay.total, false};
   float* part = reinterpret_cast<float*>(const_cast<char*>(ws) + sp.part_off);
+  uint8_t* wpk = reinterpret_cast<uint8_t*>(const_cast<char*>(ws) + sp.pk_off);
+  if (sp.pk) {
+    const int64_t units = NT * lay.G * (kPkRec / 16);
+    hipLaunchKernelGGL(gemm_pack_kernel, dim3(static_cast<unsigned>((units + 255) / 256)), dim3(256), 0, st, codes,
+                       scales, static_cast<int>(N), static_cast<int>(lay.G), units, wpk);
+  }
   const int64_t per_xcd = (sp.tiles_main + kXcds - 1) / kXcds;
   const int64_t grid = per_xcd * kXcds + sp.tiles_tail * sp.ks;
-  hipLaunchKernelGGL(gemm_mx_kernel, dim3(static_cast<unsigned>(grid)), dim3(kMxThreads), 0, st, rec, xh, xl, p2,
-                     codes, scales, biases, y, static_cast<int>(M), static_cast<int>(N), static_cast<int>(lay.G),
-                     static_cast<int>(lay.Gp), static_cast<int>(MT), static_cast<int>(NT), static_cast<int>(per_xcd),
-                     static_cast<int>(sp.tiles_main), static_cast<int>(sp.ks), part,
-                     static_cast<int>(lay.G % 8 == 0 && aligned(biases, 16)));
+  hipLaunchKernelGGL(sp.pk ? gemm_mx_kernel<true> : gemm_mx_kernel<false>, dim3(static_cast<unsigned>(grid)),
+                     dim3(kMxThreads), 0, st, rec, xh, xl, p2, codes, scales, wpk, biases, y, static_cast<int>(M),
+                     static_cast<int>(N), static_cast<int>(lay.G), static_cast<int>(lay.Gp), static_cast<int>(MT),
+                     static_cast<int>(NT), static_cast<int>(per_xcd), static_cast<int>(sp.tiles_main),
+                     static_cast<int>(sp.ks), part, static_cast<int>(lay.G % 8 == 0 && aligned(biases, 16)));
   if (sp.tiles_tail > 0) {
     const int64_t blocks = sp.tiles_tail * (kMxBM * kMxBN / 4) / 256;
     hipLaunchKernelGGL(gemm_tail_sum_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, part, y,

@@ -208,14 +208,20 @@ int tb_ternary_gemv_run(const void* workspace, size_t ws_bytes, int64_t B, int64
 size_t tb_ternary_gemm_workspace_size(int64_t M, int64_t K);
 
 /* Workspace bytes for M x K activations against N output columns that let
- * tb_ternary_gemm / _run balance the last round of output tiles: when the
- * 64 x 512 tiles leave the last round of the GPU's compute units at most
- * half full, those tiles are split into K slices whose partial tiles (fp32)
- * follow the prepared activation in the workspace and are added in slice
- * order by a second kernel (deterministic).  At least
- * tb_ternary_gemm_workspace_size(M, K); a run with a workspace smaller than
- * this value (but at least that size) computes every tile whole instead.
- * Returns tb_ternary_gemm_workspace_size(M, K) for invalid N. */
+ * tb_ternary_gemm / _run balance the last round of output tiles and read
+ * the weights contiguously:
+ *  - when the 64 x 512 tiles leave the last round of the GPU's compute
+ *    units at most half full, those tiles are split into K slices whose
+ *    partial tiles (fp32) follow the prepared activation in the workspace
+ *    and are added in slice order by a second kernel (deterministic);
+ *  - when M spans at least 4 row tiles (M > 192), the run first copies the
+ *    codes and scales into one contiguous record per (512-column tile,
+ *    group of 128) after those partials (N/512 x K/128 x 17408 bytes,
+ *    rounded up) and the matmul reads that copy (same arithmetic).
+ * At least tb_ternary_gemm_workspace_size(M, K); a run with a workspace
+ * smaller than this value (but at least that size) computes every tile
+ * whole from the weights as stored instead.  Returns
+ * tb_ternary_gemm_workspace_size(M, K) for invalid N. */
 size_t tb_ternary_gemm_workspace_size_n(int64_t M, int64_t K, int64_t N);
 
 /* Packed linear for prefill (any M >= 1), same definition as the GEMV:

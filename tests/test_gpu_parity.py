@@ -162,6 +162,33 @@ def test_gemm_tail_split_matches_oracle_and_whole_tiles(M, N, K, block, xd):
     compare(y1.cpu().numpy(), want, f"gemm split M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("M,N,K,block,xd", [
+    (300, 1000, 1024, 1024, "bf16"),  # 5 row tiles, ragged last column tile (488 rows)
+    (256, 512, 2560, 512, "f32"),     # exactly 4 row tiles, one column tile
+])
+def test_gemm_packed_weights_match_stored_layout(M, N, K, block, xd):
+    """With at least 4 row tiles and a workspace of
+    tb_ternary_gemm_workspace_size_n, the run first copies the codes and
+    scales into one contiguous record per (column tile, group) and the matmul
+    reads that copy; the arithmetic is the same as reading the weights as
+    stored (a workspace of tb_ternary_gemm_workspace_size), so the two agree
+    bitwise when no tile is split, and both match the oracle."""
+    announce(f"gemm packed weights M={M} N={N} K={K} block={block} x={xd}")
+    T = torch()
+    p = synth.make_problem("gemm_pack", N, K, M, [M, N, K, block, 17], xd, block)
+    codes, s, b = pack_to_device(p.t, p.scales)
+    x, sg = x_to_device(p), signs_to_device(p.signs)
+    need, base = tb.tb_ternary_gemm_workspace_size_n(M, K, N), tb.tb_ternary_gemm_workspace_size(M, K)
+    assert need > base
+    yp = tb.tb_ternary_gemm(x, sg, block, codes, s, b, workspace=T.empty(need, dtype=T.uint8, device="cuda"))
+    ys = tb.tb_ternary_gemm(x, sg, block, codes, s, b, workspace=T.empty(base, dtype=T.uint8, device="cuda"))
+    T.cuda.synchronize()
+    assert T.equal(yp, ys)
+    oc, osc, ob = oracle_pack(p)
+    want = oracle.packed_linear(p.x64, p.signs, block, oc, osc, ob)
+    compare(yp.cpu().numpy(), want, f"gemm packed M={M} N={N} K={K}")
+
+
 def test_gemm_biases_not_16_byte_aligned():
     """The epilogue reads the biases as 16-byte vectors only when they are
     16-byte aligned; a pack whose biases start 4 elements into a buffer takes
