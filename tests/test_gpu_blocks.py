@@ -21,6 +21,7 @@ SHAPES = [
     (77, 1536, 512, "f32", 6),          # 512-blocks, 3 chunks
     (17, 6144, 1024, "bf16", 7),        # one partial tile
     (40000, 2048, 1024, "bf16", 8),     # several tiles per wave
+    (300, 26624, 1024, "bf16", 9),      # 26 chunks: two past the 24 a workgroup loads up front
 ]
 
 
