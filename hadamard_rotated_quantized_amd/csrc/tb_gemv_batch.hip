@@ -12,18 +12,22 @@
 //
 // 1. batch_stream_kernel: one workgroup per (128-row block, K slice of whole
 //    chunks).  Its waves first issue the loads of the slice's activation
-//    chunks (every batch row), then the first code loads of their tiles, and
-//    transform the chunks on the matrix cores (tb_xform.h) straight into the
-//    LDS operand image of the slice -- the exact four-limb split and the
-//    group terms -- while the codes are in flight.  Each of the 8 waves then
-//    streams one 16-row tile through a ring of register slots of 8 groups
-//    (8-byte code loads, one 16-byte load for the 8 scales and one for the 8
-//    biases of a row).  A group is 2 v_mfma_i32_16x16x64_i8 per 4 batch rows:
-//    A row 4 b' + l holds limb l of batch row b', the 4 k-blocks hold 4 of
-//    the group's 8 code words, so the accumulator of lane (lane group j, row
-//    c) is the 4 limbs of batch row j (+4 for the second set) at output row
-//    c.  The limbs are recombined in fp32 and the fp16 scale and bias applied
-//    per group.
+//    chunks (every batch row; bf16 x and the signs land by direct-to-LDS
+//    loads in the LDS rows the chunk's transform will write), then the first
+//    code loads of their tiles, and transform the chunks on the matrix cores
+//    (tb_xform.h) straight into the LDS operand image of the slice -- the
+//    exact four-limb split and the group terms -- while the codes are in
+//    flight.  Each of the 8 waves then streams one 16-row tile through a
+//    ring of register slots of 8 groups: four 16-byte code loads (each row's
+//    64 bytes of two groups as one run, regrouped by one lane swap per
+//    dword pair), one 16-byte load for the 8 scales and one for the 8 biases
+//    of a row.  A group is 2 v_mfma_i32_16x16x64_i8 per 4 batch rows: A row
+//    4 b' + l holds limb l of batch row b', the 4 k-blocks hold 4 of the
+//    group's 8 code words, so the accumulator of lane (lane group j, row c)
+//    is the 4 limbs of batch row j (+4 for the second set) at output row c.
+//    The limbs are recombined (limb pairs exactly in int32, the two halves
+//    in one fp32 rounding) and the fp16 scale and bias applied per group; an
+//    octet of groups is one branch-free block of MFMAs and fp32 arithmetic.
 // 2. batch_reduce_kernel (more than one K slice): the slices' partial rows
 //    summed in slice order, so results do not depend on scheduling.
 #include <algorithm>
@@ -40,6 +44,11 @@ constexpr int kBatArow = 144;                   // LDS bytes per (batch row, gro
 constexpr int kBatRing = 2;                     // octets of groups in flight per wave (10 loads each)
 constexpr int kBatMaxTasks = 4;                 // chunk transforms per wave
 constexpr int64_t kBatLdsMax = 150 * 1024;
+// s_waitcnt vmcnt(n) with the other counters left alone: n = the ring's
+// initial loads (4 code loads + scales + biases per octet), issued after the
+// staged chunk inputs
+constexpr int kBatRingLoads = 6 * kBatRing;
+constexpr int kBatWaitStaged = (kBatRingLoads & 15) | ((kBatRingLoads >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 
 // LDS stride between batch rows: 16 mod 32 dwords, so that the two batch rows
 // read by lanes 0-3 and 4-7 of an A-operand read land on disjoint banks.
@@ -83,11 +92,27 @@ static int64_t batch_ws_bytes(int64_t B, int64_t N, const BatchPlan& p) {
 // ---------------------------------------------------------------------------
 // 1. transform + stream: one workgroup per (row block, K slice)
 // ---------------------------------------------------------------------------
-// One ring slot: 8 consecutive groups (an octet) of the lane's row
+// One ring slot: 8 consecutive groups (an octet) of the lane's row.  Code
+// load m brings groups 2 m and 2 m + 1 of the 16 rows: lane group j reads 16
+// bytes, half (j & 1) of group 2 m + (j >> 1), so each row's 64 bytes are
+// one contiguous run; a lane swap (batch_words) then hands every lane group
+// one word pair of each group.
 struct BatchSlot {
-  uint2 w[8];  // code words 2 j and 2 j + 1 of (row c, group) for lane group j
+  v4u w[4];
   uint4 s, b;  // the 8 fp16 scales / biases of (row c, octet), one 16-byte load each
 };
+
+// Code words of groups 2 m and 2 m + 1 from a slot's load m.  Before the
+// swap lane group j holds words 4 (j & 1) .. + 3 of group 2 m + (j >> 1);
+// v_permlane32_swap exchanges the upper lane half of dwords 0, 1 with the
+// lower lane half of dwords 2, 3, after which lane group j holds, for both
+// groups, word pair p = 2 (j & 1) + (j >> 1) (words 2 p, 2 p + 1).
+__device__ __forceinline__ void batch_words(const v4u& w, uint2& g0, uint2& g1) {
+  const auto sx = __builtin_amdgcn_permlane32_swap(w.x, w.z, false, false);
+  const auto sy = __builtin_amdgcn_permlane32_swap(w.y, w.w, false, false);
+  g0 = make_uint2(sx[0], sy[0]);
+  g1 = make_uint2(sx[1], sy[1]);
+}
 
 template <int NS, int L, int DT>
 __global__ __launch_bounds__(kBatThreads, 1) void batch_stream_kernel(
@@ -125,11 +150,10 @@ __global__ __launch_bounds__(kBatThreads, 1) void batch_stream_kernel(
   // those 16-byte loads dword aligned).
   auto load = [&](int o, BatchSlot& st) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int gl = 8 * o + j;
-      const int oc = gl < ng ? c * RBy + (g0 + gl) * 32 + lg * 8 : kOob;
-      const v2u w = __builtin_amdgcn_raw_buffer_load_b64(rc, oc, 0, 0);
-      st.w[j] = make_uint2(w.x, w.y);
+    for (int m = 0; m < 4; ++m) {
+      const int gl = 8 * o + 2 * m + (lg >> 1);
+      const int oc = gl < ng ? c * RBy + (g0 + gl) * 32 + (lg & 1) * 16 : kOob;
+      st.w[m] = __builtin_amdgcn_raw_buffer_load_b128(rc, oc, 0, 0);
     }
     const int os = 8 * o < ng ? (c * G + g0 + 8 * o) * 2 : kOob;
     const v4u us = __builtin_amdgcn_raw_buffer_load_b128(rs, os, 0, 0);
@@ -139,7 +163,8 @@ __global__ __launch_bounds__(kBatThreads, 1) void batch_stream_kernel(
   };
 
   // 2. the slice's activation chunks: loads first (they complete before the
-  //    code loads issued after them), then the transforms into LDS
+  //    code loads issued after them), then the transforms into LDS.  A
+  //    task's x and signs are staged in the LDS rows its transform writes.
   const int ncs = (ng + 7) >> 3;  // chunks of this slice
   const int ntask = B * ncs;      // <= 8 waves x kBatMaxTasks (plan)
   constexpr int ESZ = DT == TB_F32 ? 4 : 2;
@@ -151,6 +176,10 @@ __global__ __launch_bounds__(kBatThreads, 1) void batch_stream_kernel(
   const v4u cf[2] = {cst[0], cst[1]};
   const v4u cs[2] = {cst2[0], cst2[1]};
   XformIn<DT> xin[kBatMaxTasks];
+  auto task_rows = [&](int t) {  // LDS operand rows of task t's chunk
+    const int b = t / ncs, j = t - b * ncs;
+    return lds + b * bstride + j * (8 * kXfLimbs * kBatArow);
+  };
 #pragma unroll
   for (int r = 0; r < kBatMaxTasks; ++r) {
     const int t = wave + kBatWaves * r;
@@ -158,67 +187,99 @@ __global__ __launch_bounds__(kBatThreads, 1) void batch_stream_kernel(
       const int b = t / ncs, cg = (g0 >> 3) + (t - b * ncs);
       const auto rx = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<char*>(static_cast<const char*>(x) + static_cast<int64_t>(b) * K * ESZ), 0, K * ESZ, kRsrcWord3);
-      xform_issue<L, DT>(rx, rsg, static_cast<int64_t>(cg) * 1024, cg * 1024, lane, xin[r]);
+      xform_stage<L, DT>(rx, rsg, static_cast<int64_t>(cg) * 1024, cg * 1024, lane, task_rows(t), xin[r]);
     }
   }
+  __builtin_amdgcn_sched_barrier(0);  // the ring's loads stay behind the staging loads
   BatchSlot ring[kBatRing];
 #pragma unroll
   for (int k = 0; k < kBatRing; ++k) load(k, ring[k]);
   __builtin_amdgcn_sched_barrier(0);
+  // the staged x and signs have landed once at most the ring's loads remain
+  __builtin_amdgcn_s_waitcnt(kBatWaitStaged);
 #pragma unroll
   for (int r = 0; r < kBatMaxTasks; ++r) {
     const int t = wave + kBatWaves * r;
     if (t < ntask) {
       const int b = t / ncs, j = t - b * ncs;
+      xform_fetch<L, DT>(task_rows(t), lane, xin[r]);
       xform_chunk<L, DT>(xin[r], 8 * j, lane, cf, cs, lds + b * bstride, lxf + b * gps, kBatArow);
     }
   }
   __syncthreads();
   if (nrows == 0) return;  // no barrier follows
 
-  // 3. stream the tile's groups
+  // 3. stream the tile's groups.  Every lane reads operand rows of real
+  //    batch rows (sets past B read row B - 1 and their sums are dropped at
+  //    the store), so each octet is one branch-free block of MFMAs and fp32
+  //    arithmetic that the compiler can software-pipeline.
   float yacc[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) yacc[s] = 0.f;
-  // lane (j, c) holds A row c = 4 b' + l (batch row b', limb l) of k-block j
+  // lane (j, c) holds A row c = 4 b' + l (batch row b', limb l) of the k-block
+  // of its code words: word pair wp of each group
   const int ab = c >> 2, al = c & 3;
-  auto group = [&](int gl, uint2 w, uint32_t sdw, uint32_t bdw, int hi) {
-    const v4i bq0 = decode_word(w.x), bq1 = decode_word(w.y);
-    const float sc = half_bits_to_float(static_cast<uint16_t>(sdw >> (16 * hi)));
-    const float bi = half_bits_to_float(static_cast<uint16_t>(bdw >> (16 * hi)));
+  const char* arow[NS];
+  const float2* trow[NS];
+  const int wp = 2 * (lg & 1) + (lg >> 1);  // the word pair (k-block) of lane group lg
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      v4u a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
-      if (4 * s + ab < B) {
-        const char* ap = lds + (4 * s + ab) * bstride + (gl * kXfLimbs + al) * kBatArow + 2 * lg * 16;
-        a0 = *reinterpret_cast<const v4u*>(ap);
-        a1 = *reinterpret_cast<const v4u*>(ap + 16);
-      }
-      v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, a0), bq0, v4i{0, 0, 0, 0}, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, a1), bq1, acc, 0, 0, 0);
-      // lane (j, c): limbs 0..3 of batch row 4 s + j at output row c
-      const int bo = 4 * s + lg;
-      if (bo < B) {
-        const float2 t = lxf[bo * gps + gl];
-        const float v = static_cast<float>(acc[3]) * 16777216.f + static_cast<float>(acc[2]) * 65536.f +
-                        static_cast<float>(acc[1]) * 256.f + static_cast<float>(acc[0]);
-        yacc[s] += sc * (v * t.y) + bi * t.x;
-      }
-    }
-  };
+  for (int s = 0; s < NS; ++s) {
+    arow[s] = lds + min(4 * s + ab, B - 1) * bstride + al * kBatArow + 32 * wp;
+    trow[s] = lxf + min(4 * s + lg, B - 1) * gps;  // group terms of batch row 4 s + j
+  }
   const int nocts = (ng + 7) >> 3;
   for (int base = 0; base < nocts; base += kBatRing) {
 #pragma unroll
     for (int k = 0; k < kBatRing; ++k) {
       const BatchSlot cur = ring[k];
-      load(base + k + kBatRing, ring[k]);  // refill the slot before computing on its data
+      if (base + k + kBatRing < nocts) load(base + k + kBatRing, ring[k]);  // refill before computing
       const int o = base + k;
       if (o < nocts) {
-        const uint32_t sd[4] = {cur.s.x, cur.s.y, cur.s.z, cur.s.w};
-        const uint32_t bd[4] = {cur.b.x, cur.b.y, cur.b.z, cur.b.w};
+        // groups past the slice have zero codes; the scales and biases read
+        // for them belong to the next row and are cleared
+        const int nv = ng - 8 * o;
+        uint32_t sd[4] = {cur.s.x, cur.s.y, cur.s.z, cur.s.w};
+        uint32_t bd[4] = {cur.b.x, cur.b.y, cur.b.z, cur.b.w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (8 * o + j < ng) group(8 * o + j, cur.w[j], sd[j >> 1], bd[j >> 1], j & 1);
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t keep = (2 * q < nv ? 0xFFFFu : 0u) | (2 * q + 1 < nv ? 0xFFFF0000u : 0u);
+          sd[q] &= keep;
+          bd[q] &= keep;
+        }
+        float2 t[NS][8];
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 tv = *reinterpret_cast<const float4*>(trow[s] + 8 * o + 2 * q);
+            t[s][2 * q] = make_float2(tv.x, tv.y);
+            t[s][2 * q + 1] = make_float2(tv.z, tv.w);
+          }
+        uint2 wd[8];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) batch_words(cur.w[m], wd[2 * m], wd[2 * m + 1]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int gl = 8 * o + j;
+          const v4i bq0 = decode_word(wd[j].x), bq1 = decode_word(wd[j].y);
+          const float sc = half_bits_to_float(static_cast<uint16_t>(sd[j >> 1] >> (16 * (j & 1))));
+          const float bi = half_bits_to_float(static_cast<uint16_t>(bd[j >> 1] >> (16 * (j & 1))));
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            const char* ap = arow[s] + gl * (kXfLimbs * kBatArow);
+            const v4u a0 = *reinterpret_cast<const v4u*>(ap);
+            const v4u a1 = *reinterpret_cast<const v4u*>(ap + 16);
+            v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, a0), bq0, v4i{0, 0, 0, 0}, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, a1), bq1, acc, 0, 0, 0);
+            // lane (j, c): limbs 0..3 of batch row 4 s + j at output row c.
+            // |limb sum| <= 128 * 3 * 128 per group, so limb pairs combine
+            // exactly in int32 and in fp32; one rounding joins the halves.
+            const int lo = acc[0] + acc[1] * 256, hi = acc[2] + acc[3] * 256;
+            const float v = fmaf(static_cast<float>(hi), 65536.f, static_cast<float>(lo));
+            yacc[s] = fmaf(v, sc * t[s][j].y, yacc[s]);
+            yacc[s] = fmaf(bi, t[s][j].x, yacc[s]);
+          }
+        }
       }
     }
   }
