@@ -44,11 +44,11 @@ constexpr int kBatArow = 144;                   // LDS bytes per (batch row, gro
 constexpr int kBatRing = 2;                     // octets of groups in flight per wave (10 loads each)
 constexpr int kBatMaxTasks = 4;                 // chunk transforms per wave
 constexpr int64_t kBatLdsMax = 150 * 1024;
-// s_waitcnt vmcnt(n) with the other counters left alone: n = the ring's
-// initial loads (4 code loads + scales + biases per octet), issued after the
+// s_waitcnt vmcnt(n) with the other counters left alone: n = the loads of
+// the ring's first slot (4 code loads, scales, biases), issued after the
 // staged chunk inputs
-constexpr int kBatRingLoads = 6 * kBatRing;
-constexpr int kBatWaitStaged = (kBatRingLoads & 15) | ((kBatRingLoads >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+constexpr int kBatSlotLoads = 6;
+constexpr int kBatWaitStaged = (kBatSlotLoads & 15) | ((kBatSlotLoads >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 
 // LDS stride between batch rows: 16 mod 32 dwords, so that the two batch rows
 // read by lanes 0-3 and 4-7 of an A-operand read land on disjoint banks.
@@ -191,9 +191,11 @@ __global__ __launch_bounds__(kBatThreads, 1) void batch_stream_kernel(
     }
   }
   __builtin_amdgcn_sched_barrier(0);  // the ring's loads stay behind the staging loads
+  // Only the first slot is loaded ahead of the transforms; the others follow
+  // them: fewer loads queued ahead of other waves' activation loads, and the
+  // transforms and the barrier cover most of their latency.
   BatchSlot ring[kBatRing];
-#pragma unroll
-  for (int k = 0; k < kBatRing; ++k) load(k, ring[k]);
+  load(0, ring[0]);
   __builtin_amdgcn_sched_barrier(0);
   // the staged x and signs have landed once at most the ring's loads remain
   __builtin_amdgcn_s_waitcnt(kBatWaitStaged);
@@ -206,6 +208,8 @@ __global__ __launch_bounds__(kBatThreads, 1) void batch_stream_kernel(
       xform_chunk<L, DT>(xin[r], 8 * j, lane, cf, cs, lds + b * bstride, lxf + b * gps, kBatArow);
     }
   }
+#pragma unroll
+  for (int k = 1; k < kBatRing; ++k) load(k, ring[k]);
   __syncthreads();
   if (nrows == 0) return;  // no barrier follows
 
@@ -258,6 +262,11 @@ __global__ __launch_bounds__(kBatThreads, 1) void batch_stream_kernel(
         uint2 wd[8];
 #pragma unroll
         for (int m = 0; m < 4; ++m) batch_words(cur.w[m], wd[2 * m], wd[2 * m + 1]);
+        // the octet is one chunk: its activation scale f (the .y of every
+        // group term) multiplies the octet's scaled sums once
+        float yo[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) yo[s] = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int gl = 8 * o + j;
@@ -276,10 +285,12 @@ __global__ __launch_bounds__(kBatThreads, 1) void batch_stream_kernel(
             // exactly in int32 and in fp32; one rounding joins the halves.
             const int lo = acc[0] + acc[1] * 256, hi = acc[2] + acc[3] * 256;
             const float v = fmaf(static_cast<float>(hi), 65536.f, static_cast<float>(lo));
-            yacc[s] = fmaf(v, sc * t[s][j].y, yacc[s]);
+            yo[s] = fmaf(v, sc, yo[s]);
             yacc[s] = fmaf(bi, t[s][j].x, yacc[s]);
           }
         }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) yacc[s] = fmaf(yo[s], t[s][0].y, yacc[s]);
       }
     }
   }
