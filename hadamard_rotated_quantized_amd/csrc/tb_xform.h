@@ -151,49 +151,6 @@ __device__ __forceinline__ void xform_issue(__amdgpu_buffer_rsrc_t rx, __amdgpu_
   }
 }
 
-// The same inputs brought in through a wave-owned LDS area of at least
-// 3 KB: bf16 x (2 KB) and the signs (1 KB, at byte 2048) land by
-// direct-to-LDS loads of 16 bytes per lane, three load instructions per chunk
-// instead of eight register loads per lane (fp32 x still comes in registers,
-// four 16-byte loads).  The caller waits for these loads (vmcnt) before
-// xform_fetch, and may let the chunk's transform overwrite the area: every
-// read of it is issued before the transform's first LDS write.
-template <int L, int DT>
-__device__ __forceinline__ void xform_stage(__amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rsg, int64_t e0, int k0,
-                                            int lane, char* stage, XformIn<DT>& in) {
-  typedef __attribute__((address_space(3))) void lds_void;
-  if constexpr (DT == TB_F32) {
-    const int base = xf_lane_base(lane);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int off = base + 32 * (q >> 1) + 16 * (q & 1);
-      const v4u u = __builtin_amdgcn_raw_buffer_load_b128(rx, static_cast<int>((e0 + off) * 4), 0, 0);
-      in.x[q][0] = u.x; in.x[q][1] = u.y; in.x[q][2] = u.z; in.x[q][3] = u.w;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(stage + 1024 * i), 16,
-                                               static_cast<int>(e0 * 2) + 1024 * i + 16 * lane, 0, 0, 0);
-  }
-  if constexpr (L > 0)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsg, (lds_void*)(stage + 2048), 16, k0 + 16 * lane, 0, 0, 0);
-}
-
-template <int L, int DT>
-__device__ __forceinline__ void xform_fetch(const char* stage, int lane, XformIn<DT>& in) {
-  const int base = xf_lane_base(lane);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int off = base + 32 * (q >> 1) + 16 * (q & 1);
-    if constexpr (DT != TB_F32) {
-      const uint2 v = *reinterpret_cast<const uint2*>(stage + 2 * off);
-      in.x[q][0] = v.x; in.x[q][1] = v.y;
-    }
-    if constexpr (L > 0) in.sg[q] = *reinterpret_cast<const uint32_t*>(stage + 2048 + off);
-  }
-}
-
 // The rotated chunk U = H (signs .* x) (unnormalized) in the accumulator
 // layout of the second product: lane l, register 4 Q + t holds element
 //   e = (l & 3) | t << 2 | ((l >> 2) & 7) << 4 | (l >> 5) << 7 | Q << 8,
