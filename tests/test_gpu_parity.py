@@ -542,6 +542,10 @@ TWO_PATHS = [
     (6000, 4096, 1, 512, "f32"),     # band kernel, 2 items per wave, 512-blocks
     (1500, 3072, 6, 512, "f32"),     # K-split batch kernel, two sets of 4 batch rows
     (777, 17408, 3, 1024, "f32"),    # K-split batch kernel, several slices, ragged N
+    (1003, 2304, 7, 0, "bf16"),      # batch kernel: second set of 3 batch rows, 18 groups (partial last chunk)
+    (517, 5120, 5, 1024, "f32"),     # batch kernel: fp32 x in registers, staged signs, second set of 1 row
+    (2000, 17408, 7, 1024, "bf16"),  # batch kernel: six slices, staged bf16 x, ragged last row block
+    (300, 9216, 2, 512, "bf16"),     # batch kernel: 512-blocks, 9 chunks
 ]
 
 
