@@ -64,6 +64,10 @@ COUNTER_SUMMARIES = {
               _srcs("tb_gemv_multi.hip", "tb_xform.h")),
     "down_proj_b1": (os.path.join(ROOT, "profiles", "gemv_fused_kernel_down_proj_b1_counters.txt"),
                      _srcs("tb_gemv_fused.hip")),
+    "down_proj_b2": (os.path.join(ROOT, "profiles", "batch_stream_kernel_down_proj_b2_counters.txt"),
+                     _srcs("tb_gemv_batch.hip", "tb_xform.h")),
+    "down_proj_b4": (os.path.join(ROOT, "profiles", "batch_stream_kernel_down_proj_b4_counters.txt"),
+                     _srcs("tb_gemv_batch.hip", "tb_xform.h")),
     "down_proj_b8": (os.path.join(ROOT, "profiles", "batch_stream_kernel_down_proj_b8_counters.txt"),
                      _srcs("tb_gemv_batch.hip", "tb_xform.h")),
 }

@@ -166,7 +166,19 @@ __global__ __launch_bounds__(kBatThreads, 1) void batch_stream_kernel(
   extern __shared__ uint4 bat_lds_dyn[];
   char* const lds = reinterpret_cast<char*>(bat_lds_dyn);
   const int unit = blockIdx.x;
-  const int rb = unit / S, sl = unit - rb * S;
+  // Workgroup w runs on XCD w % 8.  When the row blocks come in eights, all
+  // S slices of a row block go to one XCD, so the cache lines of a row's
+  // scales and biases that several slices share are fetched into one L2.
+  const int rbn = static_cast<int>(gridDim.x) / S;
+  int rb, sl;
+  if ((rbn & 7) == 0) {
+    const int i = unit >> 3;
+    rb = (unit & 7) + 8 * (i / S);
+    sl = i - (i / S) * S;
+  } else {
+    rb = unit / S;
+    sl = unit - rb * S;
+  }
   const int G = K / kGroup, RBy = K / 4;  // groups, code bytes per weight row
   const int gps = 8 * cps;
   const int g0 = sl * gps;
