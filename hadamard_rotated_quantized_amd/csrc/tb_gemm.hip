@@ -829,29 +829,51 @@ __global__ __launch_bounds__(kMxThreads) void gemm_mx_kernel(
 // The packed copy of the weights for gemm_mx_kernel<true>: per (column tile
 // nt of 512 rows, group g) one record of kPkRec bytes at (nt G + g) kPkRec:
 // the 512 rows' 32 code bytes of group g in row order, then their 512 fp16
-// scales.  Rows past N are zeros.  One thread per 16-byte unit of a record.
+// scales.  Rows past N are zeros.  Threads [0, code_threads) copy the codes,
+// 16 bytes of each of 4 rows: 8 consecutive threads read one row's 128
+// bytes of groups 4 g4 .. 4 g4 + 3 (a cache line) and write them to those
+// groups' records, so a wave's load reads 8 whole lines and its store
+// writes runs of 256 bytes.  The threads
+// after them write the scale units, 8 scales (16 bytes) each.
+constexpr int kPkRowsPerThread = 4, kPkRowStep = kMxBN / kPkRowsPerThread;
+static_assert(kMxBN % kPkRowsPerThread == 0 && (kPkRowStep & (kPkRowStep - 1)) == 0, "pack kernel thread map");
 __global__ __launch_bounds__(256) void gemm_pack_kernel(const uint32_t* __restrict__ codes,
                                                         const uint16_t* __restrict__ scales, int N, int G,
-                                                        int64_t units, uint8_t* __restrict__ wpk) {
-  constexpr int kUnits = kPkRec / 16;  // 1088: 1024 of codes, 64 of scales
+                                                        int64_t code_threads, int64_t units, uint8_t* __restrict__ wpk) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= units) return;
-  const int64_t r = i / kUnits;
-  const int u = static_cast<int>(i - r * kUnits);
-  const int nt = static_cast<int>(r / G), g = static_cast<int>(r - static_cast<int64_t>(nt) * G);
   const int W = G * 8;
-  v4u_g v = {0u, 0u, 0u, 0u};
-  if (u < 1024) {
-    const int n = nt * kMxBN + (u >> 1);
-    if (n < N) v = *reinterpret_cast<const v4u_g*>(codes + static_cast<int64_t>(n) * W + g * 8 + (u & 1) * 4);
-  } else {
-    const int n0 = nt * kMxBN + 8 * (u - 1024);
-    uint32_t h[8];
+  if (i < code_threads) {
+    const int G4 = (G + 3) >> 2;
+    const int q = static_cast<int>(i & 7), nl0 = static_cast<int>((i >> 3) & (kPkRowStep - 1));
+    const int64_t rest = i / (8 * kPkRowStep);  // threads per (column tile, group quad)
+    const int nt = static_cast<int>(rest / G4), g4 = static_cast<int>(rest - static_cast<int64_t>(nt) * G4);
+    const int g = 4 * g4 + (q >> 1), half = q & 1;
+    if (g >= G) return;
+    // rows nl0 + kPkRowStep k of the tile: kPkRowsPerThread loads in flight per thread
+    v4u_g v[kPkRowsPerThread];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) h[j] = n0 + j < N ? scales[static_cast<int64_t>(n0 + j) * G + g] : 0u;
-    v = v4u_g{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    for (int k = 0; k < kPkRowsPerThread; ++k) {
+      const int n = nt * kMxBN + nl0 + kPkRowStep * k;
+      v[k] = v4u_g{0u, 0u, 0u, 0u};
+      if (n < N) v[k] = *reinterpret_cast<const v4u_g*>(codes + static_cast<int64_t>(n) * W + g * 8 + half * 4);
+    }
+    uint8_t* const dst = wpk + (static_cast<int64_t>(nt) * G + g) * kPkRec + half * 16;
+#pragma unroll
+    for (int k = 0; k < kPkRowsPerThread; ++k)
+      *reinterpret_cast<v4u_g*>(dst + (nl0 + kPkRowStep * k) * 32) = v[k];
+    return;
   }
-  *reinterpret_cast<v4u_g*>(wpk + r * kPkRec + u * 16) = v;
+  const int64_t j = i - code_threads;
+  if (j >= units) return;
+  const int64_t r = j >> 6;  // record (nt, g)
+  const int u = static_cast<int>(j & 63);
+  const int nt = static_cast<int>(r / G), g = static_cast<int>(r - static_cast<int64_t>(nt) * G);
+  const int n0 = nt * kMxBN + 8 * u;
+  uint32_t h[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) h[k] = n0 + k < N ? scales[static_cast<int64_t>(n0 + k) * G + g] : 0u;
+  *reinterpret_cast<v4u_g*>(wpk + r * kPkRec + kPkScaleOff + u * 16) =
+      v4u_g{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
 }
 
 // y of the tail tiles: the ks slice partials of each element added in slice
@@ -1043,9 +1065,10 @@ static void gemm_run_launch(const void* workspace, size_t ws_bytes, int64_t M, i
   float* part = reinterpret_cast<float*>(const_cast<char*>(ws) + sp.part_off);
   uint8_t* wpk = reinterpret_cast<uint8_t*>(const_cast<char*>(ws) + sp.pk_off);
   if (sp.pk) {
-    const int64_t units = NT * lay.G * (kPkRec / 16);
-    hipLaunchKernelGGL(gemm_pack_kernel, dim3(static_cast<unsigned>((units + 255) / 256)), dim3(256), 0, st, codes,
-                       scales, static_cast<int>(N), static_cast<int>(lay.G), units, wpk);
+    const int64_t code_threads = NT * ((lay.G + 3) / 4) * 8 * kPkRowStep;
+    const int64_t units = NT * lay.G * 64;  // scale units
+    hipLaunchKernelGGL(gemm_pack_kernel, dim3(static_cast<unsigned>((code_threads + units + 255) / 256)), dim3(256), 0,
+                       st, codes, scales, static_cast<int>(N), static_cast<int>(lay.G), code_threads, units, wpk);
   }
   const int64_t per_xcd = (sp.tiles_main + kXcds - 1) / kXcds;
   const int64_t grid = per_xcd * kXcds + sp.tiles_tail * sp.ks;
