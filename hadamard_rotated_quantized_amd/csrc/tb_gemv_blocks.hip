@@ -11,7 +11,9 @@
 //   y[n] = sum_g d[n][g] (sum_{k in g} (c[n][k] - 1) xr[k])
 //        = sum_g d[n][g] (f_g sum_k c q_k - X_g),   xr ~= f_g q (exact limbs)
 //
-// One launch, one workgroup per band of ceil(N / CUs) rows (tiles of 16
+// blocks_gemv_kernel (the register-ring path; blocks_band_kernel below
+// stages whole bands in LDS where they fit): one launch, one workgroup per
+// band of ceil(N / CUs) rows (tiles of 16
 // rows, the last one possibly partial).  Each wave first issues the
 // activation loads of its chunk transforms, then the block loads of its
 // first items, and rotates the activation itself while the blocks are in
@@ -284,6 +286,202 @@ __global__ __launch_bounds__(kBlkThreads, 1) void blocks_gemv_kernel(const void*
 }
 
 // ---------------------------------------------------------------------------
+// staged band: the band's blocks copied into LDS whole
+// ---------------------------------------------------------------------------
+// When a band's blocks fit the LDS next to the operand image, the band is
+// moved in by direct-to-LDS loads of 1 KB per wave instruction (contiguous
+// memory: the band's rows are consecutive) while the transform waves rotate
+// the activation, and every wave then reads its items' blocks from LDS.
+// Roles as in the MLX band kernel: waves below min(chunks, 8) transform, the
+// others copy (all 8 copy when every wave transforms).  Items (16-row tile
+// t, span s) are dealt round robin, item i = t S + s to wave i % 8; MI is the
+// most items a wave gets, so a wave's items carry no branches but the last.
+//
+// LDS: operand image, group terms, trit table, partial row sums, then the
+// staged bytes: the band's blocks from the 16-byte boundary at or below its
+// first byte, with room for the 9-dword windows of the tiles' padding rows.
+struct BlkStage {
+  int64_t stage, total;
+};
+__host__ __device__ inline BlkStage blk_stage_layout(int nch, int tsub, int G, int BB) {
+  BlkStage l;
+  l.stage = (blk_lds_total(nch, tsub) + 15) & ~int64_t(15);
+  // a window reaches at most 2 blocks and 36 bytes past the tiles' rows
+  l.total = l.stage + (16 + static_cast<int64_t>(tsub) * 16 * G * BB + 2 * BB + 64 + 1023) / 1024 * 1024;
+  return l;
+}
+
+template <int L, int DT, int FMT, int MI>
+__global__ __launch_bounds__(kBlkThreads, 1) void blocks_band_kernel(const void* __restrict__ x,
+                                                                      const int8_t* __restrict__ signs,
+                                                                      const uint8_t* __restrict__ blocks, int N, int K,
+                                                                      int R, float* __restrict__ y) {
+  constexpr int NW = kBlkWaves, M = 16, GPS = 4, BB = BlkFmt<FMT>::BYTES, DW = BlkFmt<FMT>::DW;
+  typedef __attribute__((address_space(3))) void lds_void;
+  extern __shared__ uint4 blk_lds_dyn[];
+  char* const lds = reinterpret_cast<char*>(blk_lds_dyn);
+  const int G = K / kGroup, S = (G + GPS - 1) / GPS, nch = blk_nch(K);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lg = lane >> 4, c = lane & 15;
+  const int ar = c & 3, alg = (c >> 2) & 3;
+  const bool a_lane = alg == lg;
+  const int band0 = static_cast<int>(blockIdx.x) * R;
+  const int nrow = min(R, N - band0);
+  const int tsub = (R + M - 1) / M;  // the layout is sized for a full band
+  const BlkStage lay = blk_stage_layout(nch, tsub, G, BB);
+  char* const lds_a = lds;
+  float2* const lds_xf = reinterpret_cast<float2*>(lds + blk_lds_xf(nch));
+  uint32_t* const lut = reinterpret_cast<uint32_t*>(lds + blk_lds_lut(nch));
+  float* const red = reinterpret_cast<float*>(lds + blk_lds_red(nch));
+  char* const stage = lds + lay.stage;
+
+  // 1. transform waves: their chunks' activation loads; copy waves: the band
+  const int ntask_waves = nch < NW ? nch : NW;
+  const bool xwave = wave < ntask_waves;
+  constexpr int ESZ = DT == TB_F32 ? 4 : 2;
+  const auto rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(x), 0, K * ESZ, kRsrcWord3);
+  const auto rsg = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(signs), 0, L > 0 ? K : 0, kRsrcWord3);
+  XformIn<DT> xin[kBlkMaxTasks];
+  if (xwave) {
+#pragma unroll
+    for (int r = 0; r < kBlkMaxTasks; ++r) {
+      const int ch = wave + NW * r;
+      if (ch < nch) xform_issue<L, DT>(rx, rsg, static_cast<int64_t>(ch) * 1024, ch * 1024, lane, xin[r]);
+    }
+  }
+  // the band's bytes [e0, e1) of the block array, staged from e0 rounded
+  // down to 16 bytes (delta bytes earlier); the range ends at e1
+  const int64_t e0 = static_cast<int64_t>(band0) * G * BB, e1 = e0 + static_cast<int64_t>(nrow) * G * BB;
+  const int64_t a0 = e0 & ~int64_t(15);
+  const int delta = static_cast<int>(e0 - a0);
+  const int nbytes = static_cast<int>(e1 - a0);
+  {
+    const int first = ntask_waves < NW ? ntask_waves : 0;
+    const int nload = NW - first;
+    if (wave >= first) {
+      const auto rbl = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blocks) + a0, 0, nbytes, kRsrcWord3);
+      const int slots = (nbytes + 1023) >> 10;
+      for (int q = wave - first; q < slots; q += nload)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rbl, (lds_void*)(stage + q * 1024), 16, q * 1024 + lane * 16, 0, 0, 0);
+    }
+  }
+
+  // 2. the operand image, the trit table, zeroed partial sums
+  for (int i = tid; i < tsub * NW * 16; i += kBlkThreads) red[i] = 0.f;
+  if constexpr (FMT == kPtq1)
+    for (int i = tid; i < 256; i += kBlkThreads) lut[i] = trit_byte_codes(static_cast<uint32_t>(i));
+  if (xwave) {
+    const v4u* cst = reinterpret_cast<const v4u*>(&kXformConst.w[xf_mode<L>()][0][lane][0]);
+    const v4u* cst2 = reinterpret_cast<const v4u*>(&kXformConst.w[xf_mode<L>()][1][lane][0]);
+    const v4u cf[2] = {cst[0], cst[1]};
+    const v4u cs[2] = {cst2[0], cst2[1]};
+#pragma unroll
+    for (int r = 0; r < kBlkMaxTasks; ++r) {
+      const int ch = wave + NW * r;
+      if (ch < nch) xform_chunk<L, DT>(xin[r], 8 * ch, lane, cf, cs, lds_a, lds_xf, kBlkArow);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0): this wave's staging landed
+  __syncthreads();
+
+  // 3. the items.  Lane (lg, c) takes block (row t 16 + c, group 4 s + lg):
+  //    the DW dwords from the one holding its first byte (rows past the band
+  //    read what the stage holds there; their sums are never written)
+  const int items = tsub * S;
+  const int sh = FMT == kPq2 ? 2 * (lg & 1) : 0;  // G is even: PQ2_0 blocks start at byte 0 or 2 of a dword
+  int tt[MI], ss[MI];
+  bool iv[MI];
+#pragma unroll
+  for (int j = 0; j < MI; ++j) {
+    const int i = wave + NW * j;
+    iv[j] = i < items;
+    const int ic = iv[j] ? i : 0;
+    tt[j] = ic / S;
+    ss[j] = ic - tt[j] * S;
+  }
+  BlkSlot<FMT> bl[MI];
+  uint4 av[MI][kWordsPerGroup];
+  float2 xfv[MI];
+#pragma unroll
+  for (int j = 0; j < MI; ++j) {
+#pragma unroll
+    for (int d = 0; d < DW; ++d) bl[j].d[d] = 0u;
+    xfv[j] = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < kWordsPerGroup; ++w) av[j][w] = make_uint4(0, 0, 0, 0);
+    if (j < MI - 1 || iv[j]) {
+      const int t = tt[j], s = ss[j];
+      const int boff = delta + ((t * M + c) * G + s * GPS + lg) * BB - sh;  // dword aligned
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(stage + boff);
+#pragma unroll
+      for (int d = 0; d < DW; ++d) bl[j].d[d] = src[d];
+      xfv[j] = lds_xf[s * GPS + lg];
+      if (a_lane) {
+        const uint4* ap = reinterpret_cast<const uint4*>(lds_a + ((s * GPS + alg) * kXfLimbs + ar) * kBlkArow);
+#pragma unroll
+        for (int w = 0; w < kWordsPerGroup; ++w) av[j][w] = ap[w];
+      }
+    }
+  }
+  float part[MI];
+#pragma unroll
+  for (int j = 0; j < MI; ++j) {
+    part[j] = 0.f;
+    if (j < MI - 1 || iv[j]) {
+      uint32_t w[8], sbits;
+      blk_words<FMT>(bl[j], sh, lut, w, sbits);
+      v4i acc0 = {}, acc1 = {};
+#pragma unroll
+      for (int i = 0; i < kWordsPerGroup; i += 2) {
+        const uint4 u0 = av[j][i], u1 = av[j][i + 1];
+        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w},
+                                                     decode_word(w[i]), acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w},
+                                                     decode_word(w[i + 1]), acc1, 0, 0, 0);
+      }
+      const v4i acc = acc0 + acc1;
+      const float v = static_cast<float>(acc[3]) * 16777216.f + static_cast<float>(acc[2]) * 65536.f +
+                      static_cast<float>(acc[1]) * 256.f + static_cast<float>(acc[0]);
+      const float d = half_bits_to_float(static_cast<uint16_t>(sbits));
+      // groups past K (the last span's padding) contribute nothing
+      part[j] = iv[j] && ss[j] * GPS + lg < G ? d * (v * xfv[j].y - xfv[j].x) : 0.f;
+    }
+  }
+  // per tile: this wave's items in registers, then over the 4 lane groups,
+  // parked in red[t][wave]
+  int tend = tt[0];
+#pragma unroll
+  for (int j = 1; j < MI; ++j) tend = iv[j] ? tt[j] : tend;
+  for (int t = tt[0]; t < tsub && t <= tend; ++t) {
+    float v = 0.f;
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < MI; ++j) {
+      const bool mine = tt[j] == t && iv[j];
+      v += mine ? part[j] : 0.f;
+      any |= mine;
+    }
+    if (any) {
+      v += xor_lane(v, 4, lane);
+      v += xor_lane(v, 5, lane);
+      if (lg == 0) red[(t * NW + wave) * 16 + c] = v;
+    }
+  }
+  __syncthreads();
+  // 4. the band's rows: partial sums added in wave order
+  for (int i = tid; i < tsub * 16; i += kBlkThreads) {
+    const int t = i >> 4, r = i & 15, rib = t * M + r;
+    if (rib < nrow) {
+      float a = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) a += red[(t * NW + w) * 16 + r];
+      y[band0 + rib] = a;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 struct BlkPlan {
@@ -305,9 +503,43 @@ static BlkPlan blk_plan(int64_t N, int64_t K) {
   return p;
 }
 
+// The staged band kernel applies when the block array is 16-byte aligned
+// (the staging loads start at 16-byte boundaries), the band's blocks fit the
+// LDS with the operand image, and every wave takes at most kBlkStageItems
+// items and at most kBlkMaxTasks chunk transforms.
+constexpr int kBlkStageItems = 4;
+template <int FMT>
+static int blk_stage_items(const BlkPlan& p, int64_t K, const uint8_t* blocks) {
+  if (!aligned(blocks, 16)) return 0;
+  const int nch = blk_nch(static_cast<int>(K));
+  const int G = static_cast<int>(K / kGroup), S = (G + 3) / 4, tsub = (p.rows + 15) / 16;
+  const int mi = (tsub * S + kBlkWaves - 1) / kBlkWaves;
+  if (nch > kBlkWaves * kBlkMaxTasks || mi > kBlkStageItems) return 0;
+  if (blk_stage_layout(nch, tsub, G, BlkFmt<FMT>::BYTES).total > kBlkLdsMax) return 0;
+  return mi;
+}
+
+template <int FMT, int L, int DT, int MI>
+static void blocks_band_launch(const void* x, const int8_t* signs, const uint8_t* blocks, int N, int K, float* y,
+                               const BlkPlan& p, hipStream_t st) {
+  auto kern = blocks_band_kernel<L, DT, FMT, MI>;
+  static std::atomic<uint64_t> lds_set{0};
+  lds_limit_once(reinterpret_cast<const void*>(kern), static_cast<int>(kBlkLdsMax), lds_set);
+  const int64_t lds = blk_stage_layout(blk_nch(K), (p.rows + 15) / 16, K / kGroup, BlkFmt<FMT>::BYTES).total;
+  hipLaunchKernelGGL(kern, dim3(p.grid), dim3(kBlkThreads), static_cast<size_t>(lds), st, x, signs, blocks, N, K,
+                     p.rows, y);
+}
+
 template <int FMT, int L, int DT>
 static void blocks_launch_t(const void* x, const int8_t* signs, const uint8_t* blocks, int N, int K, float* y,
                             const BlkPlan& p, hipStream_t st) {
+  switch (blk_stage_items<FMT>(p, K, blocks)) {
+    case 1: return blocks_band_launch<FMT, L, DT, 1>(x, signs, blocks, N, K, y, p, st);
+    case 2: return blocks_band_launch<FMT, L, DT, 2>(x, signs, blocks, N, K, y, p, st);
+    case 3: return blocks_band_launch<FMT, L, DT, 3>(x, signs, blocks, N, K, y, p, st);
+    case 4: return blocks_band_launch<FMT, L, DT, 4>(x, signs, blocks, N, K, y, p, st);
+    default: break;
+  }
   auto kern = blocks_gemv_kernel<L, DT, FMT, kBlkRing>;
   static std::atomic<uint64_t> lds_set{0};
   lds_limit_once(reinterpret_cast<const void*>(kern), static_cast<int>(kBlkLdsMax), lds_set);

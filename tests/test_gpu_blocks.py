@@ -22,6 +22,8 @@ SHAPES = [
     (17, 6144, 1024, "bf16", 7),        # one partial tile
     (40000, 2048, 1024, "bf16", 8),     # several tiles per wave
     (300, 26624, 1024, "bf16", 9),      # 26 chunks: two past the 24 a workgroup loads up front
+    (4352, 1280, 0, "bf16", 10),        # 17-row bands: band starts off 16-byte boundaries (both formats)
+    (4352, 2560, 512, "f32", 11),       # 17-row bands, 512-blocks, 3 chunks
 ]
 
 
