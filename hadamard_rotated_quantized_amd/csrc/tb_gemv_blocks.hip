@@ -306,9 +306,23 @@ struct BlkStage {
 __host__ __device__ inline BlkStage blk_stage_layout(int nch, int tsub, int G, int BB) {
   BlkStage l;
   l.stage = (blk_lds_total(nch, tsub) + 15) & ~int64_t(15);
-  // a window reaches at most 2 blocks and 36 bytes past the tiles' rows
-  l.total = l.stage + (16 + static_cast<int64_t>(tsub) * 16 * G * BB + 2 * BB + 64 + 1023) / 1024 * 1024;
+  // a window reaches at most 7 blocks and 40 bytes past the tiles' rows
+  l.total = l.stage + (16 + static_cast<int64_t>(tsub) * 16 * G * BB + 8 * BB + 64 + 1023) / 1024 * 1024;
   return l;
+}
+
+// Spans of a row in the staged kernel and the group lane group q takes in
+// span s.  PTQ1_0: groups 4 s .. 4 s + 3.  PQ2_0: span pairs cover 8 groups,
+// span 2 h + p taking groups 8 h + 2 q + p, so that the 4 lane groups' blocks
+// (68 bytes apart) start in distinct LDS bank quarters and every block of a
+// span starts at the same byte of a dword (p = 0: byte 0, p = 1: byte 2).
+template <int FMT>
+__host__ __device__ inline int blk_spans(int G) {
+  return FMT == kPq2 ? 2 * ((G + 7) / 8) : (G + 3) / 4;
+}
+template <int FMT>
+__device__ __forceinline__ int blk_group(int s, int q) {
+  return FMT == kPq2 ? 8 * (s >> 1) + 2 * q + (s & 1) : 4 * s + q;
 }
 
 template <int L, int DT, int FMT, int MI>
@@ -316,11 +330,11 @@ __global__ __launch_bounds__(kBlkThreads, 1) void blocks_band_kernel(const void*
                                                                       const int8_t* __restrict__ signs,
                                                                       const uint8_t* __restrict__ blocks, int N, int K,
                                                                       int R, float* __restrict__ y) {
-  constexpr int NW = kBlkWaves, M = 16, GPS = 4, BB = BlkFmt<FMT>::BYTES, DW = BlkFmt<FMT>::DW;
+  constexpr int NW = kBlkWaves, M = 16, BB = BlkFmt<FMT>::BYTES, DW = BlkFmt<FMT>::DW;
   typedef __attribute__((address_space(3))) void lds_void;
   extern __shared__ uint4 blk_lds_dyn[];
   char* const lds = reinterpret_cast<char*>(blk_lds_dyn);
-  const int G = K / kGroup, S = (G + GPS - 1) / GPS, nch = blk_nch(K);
+  const int G = K / kGroup, S = blk_spans<FMT>(G), nch = blk_nch(K);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lg = lane >> 4, c = lane & 15;
@@ -385,11 +399,11 @@ __global__ __launch_bounds__(kBlkThreads, 1) void blocks_band_kernel(const void*
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0): this wave's staging landed
   __syncthreads();
 
-  // 3. the items.  Lane (lg, c) takes block (row t 16 + c, group 4 s + lg):
-  //    the DW dwords from the one holding its first byte (rows past the band
+  // 3. the items.  Lane (lg, c) takes block (row t 16 + c, group
+  //    blk_group(s, lg)): PTQ1_0 its 7 dwords; PQ2_0 the 9 dwords from the
+  //    one holding its first code byte, and its scale (rows past the band
   //    read what the stage holds there; their sums are never written)
   const int items = tsub * S;
-  const int sh = FMT == kPq2 ? 2 * (lg & 1) : 0;  // G is even: PQ2_0 blocks start at byte 0 or 2 of a dword
   int tt[MI], ss[MI];
   bool iv[MI];
 #pragma unroll
@@ -401,24 +415,35 @@ __global__ __launch_bounds__(kBlkThreads, 1) void blocks_band_kernel(const void*
     ss[j] = ic - tt[j] * S;
   }
   BlkSlot<FMT> bl[MI];
+  uint16_t sb16[MI];  // PQ2_0: the block's scale bits
   uint4 av[MI][kWordsPerGroup];
   float2 xfv[MI];
 #pragma unroll
   for (int j = 0; j < MI; ++j) {
 #pragma unroll
     for (int d = 0; d < DW; ++d) bl[j].d[d] = 0u;
+    sb16[j] = 0;
     xfv[j] = make_float2(0.f, 0.f);
 #pragma unroll
     for (int w = 0; w < kWordsPerGroup; ++w) av[j][w] = make_uint4(0, 0, 0, 0);
     if (j < MI - 1 || iv[j]) {
       const int t = tt[j], s = ss[j];
-      const int boff = delta + ((t * M + c) * G + s * GPS + lg) * BB - sh;  // dword aligned
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(stage + boff);
+      const int g = blk_group<FMT>(s, lg);
+      const int b0 = delta + ((t * M + c) * G + g) * BB;  // the block's first byte
+      if constexpr (FMT == kPq2) {
+        sb16[j] = *reinterpret_cast<const uint16_t*>(stage + b0);
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(stage + ((b0 + 2) & ~3));
 #pragma unroll
-      for (int d = 0; d < DW; ++d) bl[j].d[d] = src[d];
-      xfv[j] = lds_xf[s * GPS + lg];
+        for (int d = 0; d < DW; ++d) bl[j].d[d] = src[d];
+      } else {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(stage + b0);  // dword aligned
+#pragma unroll
+        for (int d = 0; d < DW; ++d) bl[j].d[d] = src[d];
+      }
+      xfv[j] = lds_xf[g];
       if (a_lane) {
-        const uint4* ap = reinterpret_cast<const uint4*>(lds_a + ((s * GPS + alg) * kXfLimbs + ar) * kBlkArow);
+        const uint4* ap =
+            reinterpret_cast<const uint4*>(lds_a + (blk_group<FMT>(s, alg) * kXfLimbs + ar) * kBlkArow);
 #pragma unroll
         for (int w = 0; w < kWordsPerGroup; ++w) av[j][w] = ap[w];
       }
@@ -430,7 +455,15 @@ __global__ __launch_bounds__(kBlkThreads, 1) void blocks_band_kernel(const void*
     part[j] = 0.f;
     if (j < MI - 1 || iv[j]) {
       uint32_t w[8], sbits;
-      blk_words<FMT>(bl[j], sh, lut, w, sbits);
+      if constexpr (FMT == kPq2) {
+        // codes from byte 2 (even spans) or 0 (odd spans) of the first dword
+        const int o = (ss[j] & 1) ? 0 : 2;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = __builtin_amdgcn_alignbyte(bl[j].d[i + 1], bl[j].d[i], o);
+        sbits = sb16[j];
+      } else {
+        blk_words<FMT>(bl[j], 0, lut, w, sbits);
+      }
       v4i acc0 = {}, acc1 = {};
 #pragma unroll
       for (int i = 0; i < kWordsPerGroup; i += 2) {
@@ -445,7 +478,7 @@ __global__ __launch_bounds__(kBlkThreads, 1) void blocks_band_kernel(const void*
                       static_cast<float>(acc[1]) * 256.f + static_cast<float>(acc[0]);
       const float d = half_bits_to_float(static_cast<uint16_t>(sbits));
       // groups past K (the last span's padding) contribute nothing
-      part[j] = iv[j] && ss[j] * GPS + lg < G ? d * (v * xfv[j].y - xfv[j].x) : 0.f;
+      part[j] = iv[j] && blk_group<FMT>(ss[j], lg) < G ? d * (v * xfv[j].y - xfv[j].x) : 0.f;
     }
   }
   // per tile: this wave's items in registers, then over the 4 lane groups,
@@ -512,7 +545,7 @@ template <int FMT>
 static int blk_stage_items(const BlkPlan& p, int64_t K, const uint8_t* blocks) {
   if (!aligned(blocks, 16)) return 0;
   const int nch = blk_nch(static_cast<int>(K));
-  const int G = static_cast<int>(K / kGroup), S = (G + 3) / 4, tsub = (p.rows + 15) / 16;
+  const int G = static_cast<int>(K / kGroup), S = blk_spans<FMT>(G), tsub = (p.rows + 15) / 16;
   const int mi = (tsub * S + kBlkWaves - 1) / kBlkWaves;
   if (nch > kBlkWaves * kBlkMaxTasks || mi > kBlkStageItems) return 0;
   if (blk_stage_layout(nch, tsub, G, BlkFmt<FMT>::BYTES).total > kBlkLdsMax) return 0;
