@@ -93,3 +93,29 @@ def test_pq2_lm_head_sized_sampled_rows():
     assert np.array_equal(ob, blk[rows])
     want = oracle.pq2_packed_linear(x.float().cpu().numpy().astype(np.float64), sig, 1024, ob, K)
     compare(y[:, rt].cpu().numpy(), want, "pq2 lm_head rows")
+
+
+@pytest.mark.parametrize("fmt", ["pq2", "ptq1"])
+def test_blocks_off_16_byte_alignment_take_the_ring_path(fmt):
+    """A block array 4 bytes past a 16-byte boundary (allowed: the entry
+    points take 4-byte aligned blocks) cannot be staged by 16-byte
+    direct-to-LDS loads; the call takes the register-ring kernel and gives
+    the aligned array's result bit for bit."""
+    announce(f"{fmt} gemv on a block array 4 bytes off a 16-byte boundary")
+    T = torch()
+    N, K, block = 6144, 5120, 1024
+    p = synth.make_problem(fmt, N, K, 1, [12, N, K], "bf16", block)
+    blk = _blocks(fmt, p)
+    bd = T.from_numpy(blk).cuda()
+    raw = T.zeros(blk.size + 16, dtype=T.uint8, device="cuda")
+    off = raw[4:4 + blk.size].view(blk.shape)
+    off.copy_(bd)
+    assert off.data_ptr() % 16 == 4
+    fn = tb.tb_pq2_gemv if fmt == "pq2" else tb.tb_ptq1_gemv
+    x, sg = x_to_device(p), signs_to_device(p.signs)
+    y_al = fn(x, sg, block, bd)
+    y_off = fn(x, sg, block, off)
+    T.cuda.synchronize()
+    want = (oracle.pq2_packed_linear if fmt == "pq2" else oracle.ptq1_packed_linear)(p.x64, p.signs, block, blk, K)
+    compare(y_off.cpu().numpy(), want, f"{fmt} offset blocks")
+    compare(y_al.cpu().numpy(), want, f"{fmt} aligned blocks")
