@@ -11,16 +11,18 @@
 //   y[n] = sum_g d[n][g] (sum_{k in g} (c[n][k] - 1) xr[k])
 //        = sum_g d[n][g] (f_g sum_k c q_k - X_g),   xr ~= f_g q (exact limbs)
 //
-// blocks_gemv_kernel (the register-ring path; blocks_band_kernel below
-// stages whole bands in LDS where they fit): one launch, one workgroup per
-// band of ceil(N / CUs) rows (tiles of 16
-// rows, the last one possibly partial).  Each wave first issues the
-// activation loads of its chunk transforms, then the block loads of its
-// first items, and rotates the activation itself while the blocks are in
-// flight: the waves transform the 1024-input chunks on the matrix cores and
-// split them exactly into four limbs, writing the operand image and the
-// group terms (X_g, f_g) straight to LDS (tb_xform.h).  The band's work is (tile, span) items, a span being 4
-// groups of the tile's 16 rows; each wave takes a contiguous range of items.
+// Two kernels, one launch each, one workgroup per band of ceil(N / CUs)
+// rows (tiles of 16 rows, the last one possibly partial):
+// blocks_band_kernel (further below) copies a band's blocks into LDS whole
+// where they fit; blocks_gemv_kernel, the general path, streams them through
+// registers.  In blocks_gemv_kernel each wave first issues the activation
+// loads of its chunk transforms, then the block loads of its first items,
+// and rotates the activation itself while the blocks are in flight: the
+// waves transform the 1024-input chunks on the matrix cores and split them
+// exactly into four limbs, writing the operand image and the group terms
+// (X_g, f_g) straight to LDS (tb_xform.h).  The band's work is (tile, span)
+// items, a span being 4 groups of the tile's 16 rows; each wave takes a
+// contiguous range of items.
 // Lane (lane group lg, row c) loads the whole block (row c, group 4 s + lg)
 // with dword-aligned loads, rebuilds its eight 16-code words in registers
 // (PQ2_0: byte-align the code bytes that follow the 2-byte scale; PTQ1_0: a
