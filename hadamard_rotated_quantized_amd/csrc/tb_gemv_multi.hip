@@ -372,8 +372,9 @@ static PlanOffsets plan_offsets(int64_t count, int64_t ntasks, int64_t npieces) 
 // with global tile indices.  A tile costs its weight groups plus 2 (its
 // scale / bias rows and fixed work); a piece takes tiles of one module until
 // its cost reaches max(floor, left / grid), where left is the cost not yet
-// cut, so pieces shrink toward the end and the last ones even out the
-// workgroups' finishing times.
+// cut, rounded up to a multiple of the workgroup's waves (or the module's
+// last tiles), so pieces shrink toward the end and the last ones even out
+// the workgroups' finishing times.
 static std::vector<std::array<int32_t, 3>> multi_pieces(const tb_gemv_module* mods, int64_t count, int grid) {
   int64_t total = 0;
   for (int64_t i = 0; i < count; ++i)
@@ -388,7 +389,10 @@ static std::vector<std::array<int32_t, 3>> multi_pieces(const tb_gemv_module* mo
     int64_t t = 0;
     while (t < ntm) {
       const int64_t want = std::max(floor_cost, left / static_cast<int64_t>(grid));
-      const int64_t take = std::min(ntm - t, std::max<int64_t>(1, (want + tc - 1) / tc));
+      // whole rounds of the workgroup's waves: a piece's tiles are dealt
+      // round robin and its waves meet at a barrier when it ends
+      const int64_t tiles = std::max<int64_t>(1, (want + tc - 1) / tc);
+      const int64_t take = std::min(ntm - t, (tiles + kMultiWaves - 1) / kMultiWaves * kMultiWaves);
       out.push_back({static_cast<int32_t>(i), static_cast<int32_t>(tile + t), static_cast<int32_t>(tile + t + take)});
       t += take;
       left -= take * tc;

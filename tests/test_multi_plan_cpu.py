@@ -77,13 +77,16 @@ def test_plan_tasks_and_pieces_partition_tiles():
     cost_tile = np.concatenate([np.full(t, K // 128 + 2) for t, (N, K) in zip(tiles, SWEEPLIKE)])
     cum = np.concatenate([[0], np.cumsum(cost_tile)])
     floor = max(1, cum[-1] // (p["grid"] * 64))
+    # and a whole number of rounds of the workgroup's 8 waves (unless a
+    # module ends first)
     for m, a, b, _ in pc:
         left = cum[-1] - cum[a]
         want = max(floor, left // p["grid"])
         tc = SWEEPLIKE[m][1] // 128 + 2
         ends_module = b == tile0[m] + tiles[m]
-        assert cum[b] - cum[a] <= want + tc
-        assert ends_module or cum[b] - cum[a] >= want
+        rounds = -(-(-(-want // tc)) // 8)  # ceil(ceil(want / tc) / 8)
+        assert cum[b] - cum[a] <= 8 * rounds * tc
+        assert ends_module or ((b - a) % 8 == 0 and cum[b] - cum[a] >= want)
     # the first pieces are large, the last ones small
     assert (cum[pc[0, 2]] - cum[pc[0, 1]]) > 4 * (cum[pc[-2, 2]] - cum[pc[-2, 1]])
 
