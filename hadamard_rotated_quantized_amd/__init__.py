@@ -61,6 +61,7 @@ _SIGNATURES = {
     "tb_ptq1_gemv": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _I64, _P, _P]),
     "tb_gemv_multi_plan_size": (_SZ, [_P, _I64]),
     "tb_gemv_multi_plan": (_I, [_P, _I64, _I, _I, _P, _SZ, ctypes.POINTER(_SZ)]),
+    "tb_pq2_gemv_multi_plan": (_I, [_P, _I64, _I, _I, _P, _SZ, ctypes.POINTER(_SZ)]),
     "tb_ternary_gemv_multi": (_I, [_P, _P, _P, _SZ, _P]),
 }
 
@@ -473,6 +474,39 @@ def tb_gemv_multi_plan(modules, block: int, x_dtype: int = TB_BF16):
     ws = _SZ(0)
     _check(lib().tb_gemv_multi_plan(arr, len(modules), x_dtype, block, plan.ctypes.data, plan.nbytes,
                                     ctypes.byref(ws)))
+    return plan, int(ws.value)
+
+
+def tb_pq2_gemv_multi_plan(modules, block: int, x_dtype: int = TB_BF16):
+    """tb_gemv_multi_plan on PQ2_0 blocks: modules is a sequence of (x, signs,
+    blocks, y) with blocks the module's (N, K / 128 * 34) uint8 PQ2_0 array
+    on the GPU.  Returns (plan, workspace_bytes); run it with
+    tb_ternary_gemv_multi."""
+    torch = _torch()
+    arr = (TbGemvModule * len(modules))()
+    for i, (x, signs, blocks, y) in enumerate(modules):
+        if x.dim() not in (1, 2) or (x.dim() == 2 and x.shape[0] != 1):
+            raise ValueError(f"module {i}: x must be (K,) or (1, K), got {tuple(x.shape)}")
+        K = int(x.shape[-1])
+        _check_width(K)
+        if blocks.dim() != 2 or blocks.shape[1] != K // 128 * PQ2_BLOCK_BYTES:
+            raise ValueError(f"module {i}: blocks has shape {tuple(blocks.shape)}, "
+                             f"expected (N, {K // 128 * PQ2_BLOCK_BYTES})")
+        N = int(blocks.shape[0])
+        _signs_shape(signs, K, block)
+        if y.numel() != N or y.dim() not in (1, 2):
+            raise ValueError(f"module {i}: y must hold N={N} outputs, got shape {tuple(y.shape)}")
+        _dev(x, "x")
+        _dev(blocks, "blocks", torch.uint8)
+        _dev(y, "y", torch.float32)
+        if signs is not None:
+            _dev(signs, "signs", torch.int8)
+        arr[i] = TbGemvModule(x.data_ptr(), _ptr(signs), blocks.data_ptr(), None, None, y.data_ptr(), N, K)
+    size = int(lib().tb_gemv_multi_plan_size(arr, len(modules)))
+    plan = np.zeros(max(size, 64), np.uint8)
+    ws = _SZ(0)
+    _check(lib().tb_pq2_gemv_multi_plan(arr, len(modules), x_dtype, block, plan.ctypes.data, plan.nbytes,
+                                        ctypes.byref(ws)))
     return plan, int(ws.value)
 
 

@@ -38,6 +38,7 @@
 #include <array>
 #include <map>
 #include <tuple>
+#include <type_traits>
 #include <vector>
 
 #include "tb_xform.h"
@@ -57,10 +58,16 @@ constexpr int64_t kMultiLdsMax = 150 * 1024;
 constexpr int kMultiWsHead = 256;                   // workspace bytes before the first image: the piece counter
 constexpr int kMultiPieceFloor = 64;                // smallest piece: 1 / 64 of a workgroup's mean share
 
+// weight containers of a plan: the MLX affine container (codes, scales,
+// biases) or PQ2_0 blocks (the module's codes pointer holds the blocks)
+constexpr int kMultiMlx = 0, kMultiPq2 = 1;
+constexpr int kPq2Bytes = 34;  // PQ2_0 block: fp16 scale, then 32 code bytes
+
 struct MultiHeader {  // 64 bytes
   int32_t magic, count, tasks, grid;
   int32_t block, x_dtype, max_nch, pieces;
-  int64_t modules_off, tasks_off, pieces_off, total_bytes;
+  int64_t modules_off, tasks_off, pieces_off;
+  int32_t total_bytes, format;
 };
 struct MultiModule {  // 64 bytes
   const void* x;
@@ -124,9 +131,16 @@ struct MultiPair {
   uint4 s, b;  // 8 fp16 scales / biases of the row's 8 groups of the pair
 };
 
-template <int NW, int P>
+// PQ2_0: a lane's span pair is two adjacent blocks, groups 8 p + 2 lg and
+// 8 p + 2 lg + 1 of its row: 68 bytes from a dword boundary (G is even)
+struct MultiPairPq2 {
+  uint32_t d[17];
+};
+
+template <int NW, int P, int FMT>
 __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __restrict__ plan,
                                                                   char* __restrict__ ws) {
+  using Pair = typename std::conditional<FMT == kMultiPq2, MultiPairPq2, MultiPair>::type;
   constexpr int kMultiThreads = 64 * NW;
   constexpr int M = 16, GPS = 4;
   extern __shared__ uint4 lds_dyn[];
@@ -181,10 +195,13 @@ __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __
     // this wave's tiles: ta + wave + NW j, j < ntw.  The unit of the ring is
     // a pair of spans (2 p, 2 p + 1) of one tile: P2 = ceil(S / 2) pairs per
     // tile, pair steps k = j * P2 + p.
-    const int P2 = (S + 1) >> 1;
+    // PQ2_0: span 2 p + h takes groups 8 p + 2 lg + h, so a pair covers 8
+    // groups whatever S is
+    const int P2 = FMT == kMultiPq2 ? (G + 7) >> 3 : (S + 1) >> 1;
     const int ntw = ta + wave < tb ? (tb - ta - wave + NW - 1) / NW : 0;
     const int nsteps = ntw * P2;
-    const auto rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(md.codes), 0, md.N * RB, kRsrcWord3);
+    const auto rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(md.codes), 0,
+                                                      FMT == kMultiPq2 ? md.N * G * kPq2Bytes : md.N * RB, kRsrcWord3);
     const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(md.scales), 0, md.N * G * 2, kRsrcWord3);
     const auto rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(md.biases), 0, md.N * G * 2, kRsrcWord3);
     const auto ry = __builtin_amdgcn_make_buffer_rsrc(md.y, 0, md.N * 4, kRsrcWord3);
@@ -214,8 +231,26 @@ __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __
     // k + lg for its row (the 8 fp16 of the step's 8 groups), so the row's 4
     // lanes read one contiguous run when the steps share a tile.  The lanes
     // exchange them when the round is consumed.
-    auto load = [&](int k, MultiPair& st, bool round_head) {
+    auto load = [&](int k, Pair& st, bool round_head) {
       const bool live = k < nsteps;
+      if constexpr (FMT == kMultiPq2) {
+        // blocks (row, 8 p + 2 lg) and (row, 8 p + 2 lg + 1): 68 contiguous
+        // bytes, the 4 lane groups of a row one run of 272 (offsets past the
+        // buffer read zeros; the constant parts go in soffset)
+        const int row = (ta - md.tile0 + wave + it * NW) * M + c;
+        const int b0 = live ? (row * G + 8 * ip + 2 * lg) * kPq2Bytes : kOob;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const v4u u = __builtin_amdgcn_raw_buffer_load_b128(rc, b0, 16 * q, 0);
+          st.d[4 * q] = u.x; st.d[4 * q + 1] = u.y; st.d[4 * q + 2] = u.z; st.d[4 * q + 3] = u.w;
+        }
+        st.d[16] = __builtin_amdgcn_raw_buffer_load_b32(rc, b0, 64, 0);
+        if (++ip == P2) {
+          ip = 0;
+          ++it;
+        }
+        return;
+      } else {
       const int oc = live ? lane_c + it * (NW * M * RB) + ip * 256 : kOob;
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
@@ -238,9 +273,10 @@ __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __
         ip = 0;
         ++it;
       }
+      }
     };
     static_assert(P % 4 == 0, "a round of scale loads covers 4 ring slots");
-    MultiPair ring[P];
+    Pair ring[P];
 #pragma unroll
     for (int k = 0; k < P; ++k) load(k, ring[k], k % 4 == 0);
 
@@ -284,6 +320,36 @@ __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __
       // groups past K (padding of the last span) contribute nothing
       yacc += s * GPS + lg < G ? sc * (v * xf.y) + bi * xf.x : 0.f;
     };
+    // PQ2_0 span h of pair p: group 8 p + 2 lg + h of the lane's row (A rows
+    // of group 8 p + 2 alg + h); block 0 of the pair: scale in bytes 0-1,
+    // codes from byte 2 (byte-aligned); block 1: scale in bytes 34-35, codes
+    // in dwords 9-16.  bias = -scale.
+    auto span_pq2 = [&](int pp, int h, const uint32_t* d) {
+      const int g = 8 * pp + 2 * lg + h;
+      const float2 xf = lds_xf[g];
+      if (a_lane) {
+        const uint4* ap =
+            reinterpret_cast<const uint4*>(lds_a + ((8 * pp + 2 * alg + h) * kXfLimbs + ar) * kMultiArow);
+#pragma unroll
+        for (int w = 0; w < kWordsPerGroup; ++w) av[w] = ap[w];
+      }
+      const uint32_t sbits = h ? d[8] >> 16 : d[0];
+      v4i acc0 = {}, acc1 = {};
+#pragma unroll
+      for (int w = 0; w < kWordsPerGroup; w += 2) {
+        const uint32_t c0 = h ? d[9 + w] : __builtin_amdgcn_alignbyte(d[w + 1], d[w], 2);
+        const uint32_t c1 = h ? d[10 + w] : __builtin_amdgcn_alignbyte(d[w + 2], d[w + 1], 2);
+        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)av[w].x, (int)av[w].y, (int)av[w].z, (int)av[w].w},
+                                                     decode_word(c0), acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+            v4i{(int)av[w + 1].x, (int)av[w + 1].y, (int)av[w + 1].z, (int)av[w + 1].w}, decode_word(c1), acc1, 0, 0, 0);
+      }
+      const v4i acc = acc0 + acc1;
+      const float sc = half_bits_to_float(static_cast<uint16_t>(sbits));
+      const float v = static_cast<float>(acc[3]) * 16777216.f + static_cast<float>(acc[2]) * 65536.f +
+                      static_cast<float>(acc[1]) * 256.f + static_cast<float>(acc[0]);
+      yacc += g < G ? sc * (v * xf.y - xf.x) : 0.f;
+    };
     // Step sl of a round needs, from lane group sl of its row, dword
     // (lg >> 1) of the step's 8 halves for the pair's first span and dword
     // 2 + (lg >> 1) for its second (the lane's group is 8 p + lg / 8 p + 4 + lg).
@@ -295,10 +361,31 @@ __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __
     uint32_t s0x = 0, s0y = 0, s1x = 0, s1y = 0, s2x = 0, s2y = 0, s3x = 0, s3y = 0;
     uint32_t b0x = 0, b0y = 0, b1x = 0, b1y = 0, b2x = 0, b2y = 0, b3x = 0, b3y = 0;
     auto xl = [&](uint32_t v, int j) { return static_cast<uint32_t>(xor_lane_i(static_cast<int>(v), j, lane)); };
+    if constexpr (FMT == kMultiPq2) {
+      for (int base = 0; base < nsteps; base += P) {
+#pragma unroll
+        for (int sl = 0; sl < P; ++sl) {
+          const Pair cur = ring[sl];
+          load(base + sl + P, ring[sl], false);  // refill the slot before computing on its data
+          if (base + sl < nsteps) {
+            span_pq2(p, 0, cur.d);
+            span_pq2(p, 1, cur.d);
+            if (++p == P2) {
+              float t = yacc + xor_lane(yacc, 4, lane);
+              t += xor_lane(t, 5, lane);
+              if (lg == 0) ybuf[(j - j0) * 16 + c] = t;
+              yacc = 0.f;
+              p = 0;
+              if (++j - j0 == kMultiYbuf) flush(j);
+            }
+          }
+        }
+      }
+    } else {
     for (int base = 0; base < nsteps; base += P) {
 #pragma unroll
       for (int sl = 0; sl < P; ++sl) {
-        const MultiPair cur = ring[sl];
+        const Pair cur = ring[sl];
         if (sl % 4 == 0) {
           const uint32_t osx = k1 ? cur.s.y : cur.s.x, osy = k1 ? cur.s.w : cur.s.z;  // own class
           const uint32_t tsx = k1 ? cur.s.x : cur.s.y, tsy = k1 ? cur.s.z : cur.s.w;  // other class
@@ -342,6 +429,7 @@ __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __
           }
         }
       }
+    }
     }
     flush(j);
     __syncthreads();  // the next piece's number and image replace this one's
@@ -438,9 +526,8 @@ extern "C" size_t tb_gemv_multi_plan_size(const tb_gemv_module* mods, int64_t co
   return static_cast<size_t>(plan_offsets(count, multi_total_tasks(mods, count), np).total);
 }
 
-extern "C" int tb_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int x_dtype, int block, void* plan,
-                                  size_t plan_bytes, size_t* workspace_bytes) {
-  const char* who = "tb_gemv_multi_plan";
+static int multi_plan(const tb_gemv_module* mods, int64_t count, int x_dtype, int block, int fmt, void* plan,
+                      size_t plan_bytes, size_t* workspace_bytes, const char* who) {
   if (!mods || count <= 0 || !plan || !workspace_bytes) {
     set_error("%s: null argument or empty module list", who);
     return TB_ERR_ARG;
@@ -471,17 +558,30 @@ extern "C" int tb_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int
       return TB_ERR_SHAPE;
     }
     if (m.N == 0) continue;
-    if (!m.x || !m.codes || !m.scales || !m.biases || !m.y || (block > 0) != (m.signs != nullptr)) {
-      set_error("%s: module %lld: null pointer (signs must be given exactly when block > 0)", who, (long long)i);
-      return TB_ERR_ARG;
+    if (fmt == kMultiPq2) {
+      if (!m.x || !m.codes || m.scales || m.biases || !m.y || (block > 0) != (m.signs != nullptr)) {
+        set_error("%s: module %lld: null pointer, or scales / biases given (PQ2_0 blocks carry them; signs "
+                  "must be given exactly when block > 0)", who, (long long)i);
+        return TB_ERR_ARG;
+      }
+      if (!aligned(m.x, 16) || !aligned(m.codes, 4) || !aligned(m.y, 4) || (m.signs && !aligned(m.signs, 4))) {
+        set_error("%s: module %lld: x needs 16-byte, blocks, y and signs 4-byte alignment", who, (long long)i);
+        return TB_ERR_ALIGN;
+      }
+    } else {
+      if (!m.x || !m.codes || !m.scales || !m.biases || !m.y || (block > 0) != (m.signs != nullptr)) {
+        set_error("%s: module %lld: null pointer (signs must be given exactly when block > 0)", who, (long long)i);
+        return TB_ERR_ARG;
+      }
+      if (!aligned(m.x, 16) || !aligned(m.codes, 16) || !aligned(m.scales, 4) || !aligned(m.biases, 4) ||
+          !aligned(m.y, 4) || (m.signs && !aligned(m.signs, 4))) {
+        set_error("%s: module %lld: x and codes need 16-byte, scales, biases, y and signs 4-byte alignment", who,
+                  (long long)i);
+        return TB_ERR_ALIGN;
+      }
     }
-    if (!aligned(m.x, 16) || !aligned(m.codes, 16) || !aligned(m.scales, 4) || !aligned(m.biases, 4) ||
-        !aligned(m.y, 4) || (m.signs && !aligned(m.signs, 4))) {
-      set_error("%s: module %lld: x and codes need 16-byte, scales, biases, y and signs 4-byte alignment", who,
-                (long long)i);
-      return TB_ERR_ALIGN;
-    }
-    if (m.N > (1 << 26) || m.K > (1 << 20) || m.N * (m.K / 4) > INT32_MAX) {
+    if (m.N > (1 << 26) || m.K > (1 << 20) || m.N * (m.K / 4) > INT32_MAX ||
+        (m.N + 16) * (m.K / kGroup) * kPq2Bytes + 512 > INT32_MAX) {
       set_error("%s: module %lld: N=%lld K=%lld is too large for one module", who, (long long)i, (long long)m.N,
                 (long long)m.K);
       return TB_ERR_SHAPE;
@@ -504,7 +604,8 @@ extern "C" int tb_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int
   const int grid = device_cus();
   const int64_t ntasks = multi_total_tasks(mods, count);
   const std::vector<std::array<int32_t, 3>> pcs = multi_pieces(mods, count, grid);
-  if (pcs.size() >= (size_t(1) << 30)) {
+  if (pcs.size() >= (size_t(1) << 30) ||
+      plan_offsets(count, ntasks, static_cast<int64_t>(pcs.size())).total >= INT32_MAX) {
     set_error("%s: the module list is too large for one plan", who);
     return TB_ERR_SHAPE;
   }
@@ -528,7 +629,8 @@ extern "C" int tb_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int
   hd.modules_off = po.modules;
   hd.tasks_off = po.tasks;
   hd.pieces_off = po.pieces;
-  hd.total_bytes = static_cast<int64_t>(need);
+  hd.total_bytes = static_cast<int32_t>(need);
+  hd.format = fmt;
   std::memcpy(p, &hd, sizeof hd);
   MultiModule* md = reinterpret_cast<MultiModule*>(p + hd.modules_off);
   int32_t* tk = reinterpret_cast<int32_t*>(p + hd.tasks_off);
@@ -572,17 +674,29 @@ extern "C" int tb_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int
   return TB_OK;
 }
 
+extern "C" int tb_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int x_dtype, int block, void* plan,
+                                  size_t plan_bytes, size_t* workspace_bytes) {
+  return multi_plan(mods, count, x_dtype, block, kMultiMlx, plan, plan_bytes, workspace_bytes, "tb_gemv_multi_plan");
+}
+
+extern "C" int tb_pq2_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int x_dtype, int block, void* plan,
+                                      size_t plan_bytes, size_t* workspace_bytes) {
+  return multi_plan(mods, count, x_dtype, block, kMultiPq2, plan, plan_bytes, workspace_bytes,
+                    "tb_pq2_gemv_multi_plan");
+}
+
 template <int L, int DT>
 static void multi_prep_launch(const void* plan, void* ws, int tasks, hipStream_t st) {
   hipLaunchKernelGGL((multi_prep_kernel<L, DT>), dim3((tasks + 3) / 4), dim3(256), 0, st,
                      static_cast<const char*>(plan), static_cast<char*>(ws));
 }
 
-template <int NW, int P>
+template <int NW, int P, int FMT>
 static void multi_stream_launch(const void* plan, void* ws, int grid, size_t lds, hipStream_t st) {
   static std::atomic<uint64_t> lds_set{0};
-  lds_limit_once(reinterpret_cast<const void*>(multi_stream_kernel<NW, P>), static_cast<int>(kMultiLdsMax), lds_set);
-  hipLaunchKernelGGL((multi_stream_kernel<NW, P>), dim3(grid), dim3(64 * NW), lds, st,
+  lds_limit_once(reinterpret_cast<const void*>(multi_stream_kernel<NW, P, FMT>), static_cast<int>(kMultiLdsMax),
+                 lds_set);
+  hipLaunchKernelGGL((multi_stream_kernel<NW, P, FMT>), dim3(grid), dim3(64 * NW), lds, st,
                      static_cast<const char*>(plan), static_cast<char*>(ws));
 }
 
@@ -595,7 +709,8 @@ extern "C" int tb_ternary_gemv_multi(const void* plan_host, const void* plan_dev
   }
   MultiHeader hd;
   std::memcpy(&hd, plan_host, sizeof hd);
-  if (hd.magic != kPlanMagic || hd.count <= 0 || hd.grid <= 0 || hd.pieces < 0) {
+  if (hd.magic != kPlanMagic || hd.count <= 0 || hd.grid <= 0 || hd.pieces < 0 ||
+      (hd.format != kMultiMlx && hd.format != kMultiPq2)) {
     set_error("%s: the host plan was not built by tb_gemv_multi_plan", who);
     return TB_ERR_ARG;
   }
@@ -626,7 +741,8 @@ extern "C" int tb_ternary_gemv_multi(const void* plan_host, const void* plan_dev
     }
     TB_LAUNCH_CHECK(who);
     const size_t lds = static_cast<size_t>(multi_lds_total(hd.max_nch));
-    multi_stream_launch<kMultiWaves, kMultiRing>(plan_device, workspace, hd.grid, lds, st);
+    if (hd.format == kMultiPq2) multi_stream_launch<kMultiWaves, kMultiRing, kMultiPq2>(plan_device, workspace, hd.grid, lds, st);
+    else multi_stream_launch<kMultiWaves, kMultiRing, kMultiMlx>(plan_device, workspace, hd.grid, lds, st);
     TB_LAUNCH_CHECK(who);
   }
   return TB_OK;

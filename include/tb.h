@@ -294,6 +294,17 @@ size_t tb_gemv_multi_plan_size(const tb_gemv_module* mods, int64_t count);
 int tb_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int x_dtype, int block,
                        void* plan, size_t plan_bytes, size_t* workspace_bytes);
 
+/* tb_gemv_multi_plan on PQ2_0 blocks (the block container below) [P2
+ * "packing-format engineering": the same weights as 34-byte GGUF blocks,
+ * 2.125 bits/weight, consumed as stored]: each module's codes pointer holds
+ * its (N, K/128 * 34) byte array of PQ2_0 blocks (4-byte aligned), and its
+ * scales and biases pointers must be NULL (each block carries its scale;
+ * bias = -scale).  Same plan size (tb_gemv_multi_plan_size), workspace and
+ * run (tb_ternary_gemv_multi); the errors of tb_gemv_multi_plan, with
+ * TB_ERR_ARG also for non-NULL scales or biases. */
+int tb_pq2_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int x_dtype, int block,
+                           void* plan, size_t plan_bytes, size_t* workspace_bytes);
+
 /* Run a plan: plan_host is the buffer tb_gemv_multi_plan filled (read on the
  * host for the launch sizes), plan_device a copy of it in device memory
  * (16-byte aligned, read by the kernels; the caller owns both).  workspace:

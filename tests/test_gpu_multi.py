@@ -125,3 +125,65 @@ def test_multi_shared_inputs_match_oracle_and_single_calls():
         T.cuda.synchronize()
         d = (y1.double() - m[5].double()).abs().max().item()
         assert d <= 1e-6 * y1.abs().max().item(), (key, N, d)
+
+
+def _run_multi_pq2(shapes, block, xd, seed):
+    """PQ2_0 modules (host packer + transcode, checked against the oracle's
+    blocks byte for byte) in one plan, run once."""
+    T = torch()
+    probs, mods, blks = [], [], []
+    for i, (N, K) in enumerate(shapes):
+        p = synth.make_problem("multi", N, K, 1, [seed, i, N, K], xd, block)
+        c, s, b = tb.tb_pack(p.t, p.scales)
+        blk = tb.tb_pq2_from_mlx(c, s, b)
+        assert np.array_equal(blk, oracle.pq2_from_mlx(*oracle.pack(p.t, p.scales)))
+        y = T.full((1, N), float("nan"), dtype=T.float32, device="cuda")
+        mods.append((x_to_device(p), signs_to_device(p.signs), T.from_numpy(blk).cuda(), y))
+        probs.append(p)
+        blks.append(blk)
+    plan, wsb = tb.tb_pq2_gemv_multi_plan(mods, block, tb.TB_F32 if xd == "f32" else tb.TB_BF16)
+    pd = T.from_numpy(plan).cuda()
+    ws = T.empty(wsb, dtype=T.uint8, device="cuda")
+    tb.tb_ternary_gemv_multi(plan, pd, ws)
+    T.cuda.synchronize()
+    return probs, mods, blks, plan, pd, ws
+
+
+PQ2_CASES = [
+    ("bf16", 1024, [(1, 1024), (45, 2048), (300, 5120), (1000, 6144), (16, 17408), (0, 1024), (4099, 1024)]),
+    ("f32", 512, [(17, 1024), (33, 1536), (200, 512)]),
+    ("bf16", 0, [(45, 256), (300, 768), (16, 1024)]),
+]
+
+
+@pytest.mark.parametrize("xd,block,shapes", PQ2_CASES)
+def test_pq2_multi_matches_oracle(xd, block, shapes):
+    announce(f"pq2 multi x={xd} block={block} shapes={shapes}")
+    probs, mods, blks, *_ = _run_multi_pq2(shapes, block, xd, 80)
+    for p, m, blk in zip(probs, mods, blks):
+        if p.N == 0:
+            continue
+        want = oracle.pq2_packed_linear(p.x64, p.signs, block, blk, p.K)
+        compare(m[3].cpu().numpy(), want, f"pq2 multi module N={p.N} K={p.K}")
+
+
+def test_pq2_multi_rerun_is_bitwise_stable_and_matches_single_calls():
+    """Rerunning a PQ2_0 plan gives the same bits; each module agrees with
+    its single tb_pq2_gemv call within 1e-6 of max |y|."""
+    announce("pq2 multi rerun + single-call agreement")
+    T = torch()
+    shapes = [(300, 5120), (1024, 5120), (77, 6144), (513, 17408)]
+    probs, mods, blks, plan, pd, ws = _run_multi_pq2(shapes, 1024, "bf16", 81)
+    first = [m[3].clone() for m in mods]
+    for m in mods:
+        m[3].fill_(float("nan"))
+    tb.tb_ternary_gemv_multi(plan, pd, ws)
+    T.cuda.synchronize()
+    for f, m in zip(first, mods):
+        assert T.equal(f, m[3])
+    for p, m in zip(probs, mods):
+        x, sg, bd, y = m
+        y1 = tb.tb_pq2_gemv(x, sg, 1024, bd)
+        T.cuda.synchronize()
+        d = (y1.double() - y.double()).abs().max().item()
+        assert d <= 1e-6 * y1.abs().max().item(), (p.N, p.K, d)

@@ -2,8 +2,8 @@
 that the pieces partition the concatenated tile list, each within one
 module, shrinking toward the end.  The plan layout parsed here is the one
 tb_gemv_multi.hip writes: a 64-byte header (int32 magic, count, tasks, grid,
-block, x_dtype, max_nch, pieces; int64 modules_off, tasks_off, pieces_off,
-total_bytes), 64 bytes per module, int32 pairs (module, chunk) per transform
+block, x_dtype, max_nch, pieces; int64 modules_off, tasks_off, pieces_off;
+int32 total_bytes, format), 64 bytes per module, int32 pairs (module, chunk) per transform
 task, and int32 quadruples (module, first tile, end tile, 0) per piece."""
 import ctypes
 
@@ -175,3 +175,44 @@ def test_same_x_different_signs_or_width_is_not_shared():
     arr = _mods_shared([(256, 5120, 0), (256, 4096, 0)])  # same pointers, another width
     p, _ = _plan_arr(arr, 2)
     assert p["tasks"] == 9 and p["NK"][0, 3] != p["NK"][1, 3]
+
+
+def test_pq2_plan_format_and_checks():
+    """PQ2_0 plans: the header's format word is 1 (0 for the MLX container),
+    the pieces and tasks are those of the same shapes in the MLX container,
+    scales or biases given are refused, and the blocks need 4-byte (not
+    16-byte) alignment."""
+    shapes = [(10240, 5120), (1024, 5120), (5120, 17408), (45, 2048)]
+
+    def pq2_plan(arr):
+        size = tb.lib().tb_gemv_multi_plan_size(arr, len(shapes))
+        plan = np.zeros(max(size, 64), np.uint8)
+        ws = ctypes.c_size_t(0)
+        st = tb.lib().tb_pq2_gemv_multi_plan(arr, len(shapes), tb.TB_BF16, 1024, plan.ctypes.data, plan.nbytes,
+                                             ctypes.byref(ws))
+        return st, plan, ws.value
+
+    arr = _mods(shapes)
+    for m in arr:
+        m.scales = None
+        m.biases = None
+        m.codes += 4  # 4-byte aligned blocks are accepted
+    st, plan, ws = pq2_plan(arr)
+    assert st == tb.TB_OK, tb.lib().tb_last_error()
+    st0, plan0, ws0 = _plan(shapes)
+    assert st0 == tb.TB_OK
+    assert int(plan[60:64].view(np.int32)[0]) == 1 and int(plan0[60:64].view(np.int32)[0]) == 0
+    p, p0 = _parse(plan), _parse(plan0)
+    assert ws == ws0 and np.array_equal(p["pc"], p0["pc"]) and np.array_equal(p["tk"], p0["tk"])
+    # scales given: refused
+    arr = _mods(shapes)
+    for m in arr:
+        m.biases = None
+    assert pq2_plan(arr)[0] == -1
+    # blocks 2 bytes off a dword: refused
+    arr = _mods(shapes)
+    for m in arr:
+        m.scales = None
+        m.biases = None
+    arr[1].codes += 2
+    assert pq2_plan(arr)[0] == -8
