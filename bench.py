@@ -280,33 +280,53 @@ def sweep_setup(dev, check_rows=512, lm_head_rows=2048):
                 lin=lin, emb=emb, emb_ids=emb_ids, plan=plan_of(lin), plan_of=plan_of)
 
 
-def sweep_pq2_measure(sw, nrep, wbytes_mlx):
-    """The sweep's 401 linears as PQ2_0 blocks (the same weights, 2.125
-    bits/weight) in one multi-module plan: its step time, rate on its own
-    bytes, and agreement with the MLX-container sweep module by module.  The
-    blocks are the MLX containers' scales and code bytes side by side (the
-    PQ2_0 layout; checked against the library's host transcode on the first
-    module's first rows)."""
+def _device_blocks(fmt, codes, sc, N, K):
+    """The PQ2_0 or PTQ1_0 blocks of one MLX container on the device (bench
+    input preparation): PQ2_0 puts each group's scale bytes before its 32 code
+    bytes; PTQ1_0 puts the scale before the group's codes in base 3, five per
+    byte, the first code the lowest digit (the last byte holds three)."""
+    import torch
+    G = K // 128
+    sb = sc.view(torch.uint8).view(N, G, 2)
+    cb = codes.view(torch.uint8).view(N, G, 32)
+    if fmt == "pq2":
+        return torch.cat([sb, cb], dim=2).reshape(N, G * 34)
+    c = torch.stack([(cb >> (2 * j)) & 3 for j in range(4)], dim=-1).reshape(N, G, 128).to(torch.int16)
+    c = torch.nn.functional.pad(c, (0, 2)).view(N, G, 26, 5)
+    w = torch.tensor([1, 3, 9, 27, 81], dtype=torch.int16, device=codes.device)
+    trits = (c * w).sum(dim=-1).to(torch.uint8)
+    return torch.cat([sb, trits], dim=2).reshape(N, G * 28)
+
+
+def sweep_blocks_measure(sw, nrep, wbytes_mlx, fmt):
+    """The sweep's 401 linears as PQ2_0 or PTQ1_0 blocks (the same weights,
+    2.125 / 1.75 bits/weight) in one multi-module plan: its step time, rate on
+    its own bytes, and agreement with the MLX-container sweep module by
+    module.  The blocks are built from the MLX containers on the device and
+    checked against the library's host packers on the first module's first
+    rows."""
     import torch
 
     import hadamard_rotated_quantized_amd as tb
 
     mods, ys, packs, signs = sw["mods"], sw["ys"], sw["packs"], sw["signs"]
     dev = ys[0].device
+    nb = 34 if fmt == "pq2" else 28
     blocks, yq = [], []
     for i in sw["lin"]:
         codes, sc, b = packs[i]
-        N, K = mods[i][1], mods[i][2]
-        G = K // 128
-        blocks.append(torch.cat([sc.view(torch.uint8).view(N, G, 2), codes.view(torch.uint8).view(N, G, 32)],
-                                dim=2).reshape(N, G * 34))
+        blocks.append(_device_blocks(fmt, codes, sc, mods[i][1], mods[i][2]))
         yq.append(torch.empty_like(ys[i]))
     i0 = sw["lin"][0]
     c0, s0, b0 = (t[:16].cpu().numpy() for t in packs[i0])
-    if not np.array_equal(tb.tb_pq2_from_mlx(c0.view(np.uint32), s0.view(np.uint16), b0.view(np.uint16)),
-                          blocks[0][:16].cpu().numpy()):
-        raise SystemExit("sweep PQ2_0 blocks differ from the library's transcode")
-    plan, wsb = tb.tb_pq2_gemv_multi_plan(
+    if fmt == "pq2":
+        want0 = tb.tb_pq2_from_mlx(c0.view(np.uint32), s0.view(np.uint16), b0.view(np.uint16))
+    else:
+        want0 = tb.tb_ptq1_pack(tb.tb_unpack(c0.view(np.uint32), mods[i0][2]), s0.view(np.uint16))
+    if not np.array_equal(want0, blocks[0][:16].cpu().numpy()):
+        raise SystemExit(f"sweep {fmt} blocks differ from the library's host packer")
+    planner = tb.tb_pq2_gemv_multi_plan if fmt == "pq2" else tb.tb_ptq1_gemv_multi_plan
+    plan, wsb = planner(
         [(sw["xs"][sw["sites"][i]], signs[mods[i][2]], blocks[k], yq[k]) for k, i in enumerate(sw["lin"])], 1024)
     pd = torch.from_numpy(plan).to(dev)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
@@ -317,17 +337,18 @@ def sweep_pq2_measure(sw, nrep, wbytes_mlx):
         d = (yq[k].double() - ys[i].double()).abs().max().item() / max(ys[i].abs().max().item(), 1e-30)
         worst = max(worst, d)
     if not worst <= 1e-6:
-        raise SystemExit(f"sweep PQ2_0 result differs from the MLX container's: {worst:.2e} of max |y|")
+        raise SystemExit(f"sweep {fmt} result differs from the MLX container's: {worst:.2e} of max |y|")
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         tb.tb_ternary_gemv_multi(plan, pd, ws)
     g.replay()
     _warm(torch, g)
     sec = _time_graph(torch, g, nrep, spacer=g) / nrep
-    qbytes = sum(mods[i][1] * (mods[i][2] // 128) * 34 for i in sw["lin"])
+    qbytes = sum(mods[i][1] * (mods[i][2] // 128) * nb for i in sw["lin"])
     rate = qbytes / sec / 1e9
-    out = {"about": "the same 401 linears as PQ2_0 blocks (34 bytes per 128 weights) in one multi-module plan "
-                    "(transform launch + persistent streaming launch; no embedding lookup)",
+    out = {"about": f"the same 401 linears as {'PQ2_0' if fmt == 'pq2' else 'PTQ1_0'} blocks ({nb} bytes per 128 "
+                    "weights) in one multi-module plan (transform launch + persistent streaming launch; no "
+                    "embedding lookup)",
            "weight_bytes": qbytes, "ms_per_step": round(sec * 1e3, 4), "GB/s": round(rate, 1),
            "frac_hbm": round(rate / HBM_PEAK_GBS, 4),
            "mlx_equivalent_GBps": round(wbytes_mlx / sec / 1e9, 1),
@@ -426,7 +447,8 @@ def sweep_measure(n_steps, with_cpu, with_context):
                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4),
                         "traffic": measured_traffic("sweep")},
            "parity_worst_rel_l2": worst, "parity": checked}
-    out["pq2"] = sweep_pq2_measure(sw, nrep, wbytes)
+    out["pq2"] = sweep_blocks_measure(sw, nrep, wbytes, "pq2")
+    out["ptq1"] = sweep_blocks_measure(sw, nrep, wbytes, "ptq1")
     if with_cpu:
         # the oracle per row of each shape (timed above on the checked rows),
         # scaled to every row of every module of the sweep

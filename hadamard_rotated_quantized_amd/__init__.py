@@ -62,6 +62,7 @@ _SIGNATURES = {
     "tb_gemv_multi_plan_size": (_SZ, [_P, _I64]),
     "tb_gemv_multi_plan": (_I, [_P, _I64, _I, _I, _P, _SZ, ctypes.POINTER(_SZ)]),
     "tb_pq2_gemv_multi_plan": (_I, [_P, _I64, _I, _I, _P, _SZ, ctypes.POINTER(_SZ)]),
+    "tb_ptq1_gemv_multi_plan": (_I, [_P, _I64, _I, _I, _P, _SZ, ctypes.POINTER(_SZ)]),
     "tb_ternary_gemv_multi": (_I, [_P, _P, _P, _SZ, _P]),
 }
 
@@ -482,6 +483,17 @@ def tb_pq2_gemv_multi_plan(modules, block: int, x_dtype: int = TB_BF16):
     blocks, y) with blocks the module's (N, K / 128 * 34) uint8 PQ2_0 array
     on the GPU.  Returns (plan, workspace_bytes); run it with
     tb_ternary_gemv_multi."""
+    return _blocks_multi_plan(lib().tb_pq2_gemv_multi_plan, PQ2_BLOCK_BYTES, modules, block, x_dtype)
+
+
+def tb_ptq1_gemv_multi_plan(modules, block: int, x_dtype: int = TB_BF16):
+    """tb_gemv_multi_plan on PTQ1_0 blocks: modules is a sequence of (x,
+    signs, blocks, y) with blocks the module's (N, K / 128 * 28) uint8
+    PTQ1_0 array on the GPU.  Returns (plan, workspace_bytes)."""
+    return _blocks_multi_plan(lib().tb_ptq1_gemv_multi_plan, PTQ1_BLOCK_BYTES, modules, block, x_dtype)
+
+
+def _blocks_multi_plan(fn, nbytes, modules, block, x_dtype):
     torch = _torch()
     arr = (TbGemvModule * len(modules))()
     for i, (x, signs, blocks, y) in enumerate(modules):
@@ -489,9 +501,9 @@ def tb_pq2_gemv_multi_plan(modules, block: int, x_dtype: int = TB_BF16):
             raise ValueError(f"module {i}: x must be (K,) or (1, K), got {tuple(x.shape)}")
         K = int(x.shape[-1])
         _check_width(K)
-        if blocks.dim() != 2 or blocks.shape[1] != K // 128 * PQ2_BLOCK_BYTES:
+        if blocks.dim() != 2 or blocks.shape[1] != K // 128 * nbytes:
             raise ValueError(f"module {i}: blocks has shape {tuple(blocks.shape)}, "
-                             f"expected (N, {K // 128 * PQ2_BLOCK_BYTES})")
+                             f"expected (N, {K // 128 * nbytes})")
         N = int(blocks.shape[0])
         _signs_shape(signs, K, block)
         if y.numel() != N or y.dim() not in (1, 2):
@@ -505,8 +517,7 @@ def tb_pq2_gemv_multi_plan(modules, block: int, x_dtype: int = TB_BF16):
     size = int(lib().tb_gemv_multi_plan_size(arr, len(modules)))
     plan = np.zeros(max(size, 64), np.uint8)
     ws = _SZ(0)
-    _check(lib().tb_pq2_gemv_multi_plan(arr, len(modules), x_dtype, block, plan.ctypes.data, plan.nbytes,
-                                        ctypes.byref(ws)))
+    _check(fn(arr, len(modules), x_dtype, block, plan.ctypes.data, plan.nbytes, ctypes.byref(ws)))
     return plan, int(ws.value)
 
 

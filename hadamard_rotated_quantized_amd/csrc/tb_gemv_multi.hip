@@ -59,9 +59,12 @@ constexpr int kMultiWsHead = 256;                   // workspace bytes before th
 constexpr int kMultiPieceFloor = 64;                // smallest piece: 1 / 64 of a workgroup's mean share
 
 // weight containers of a plan: the MLX affine container (codes, scales,
-// biases) or PQ2_0 blocks (the module's codes pointer holds the blocks)
-constexpr int kMultiMlx = 0, kMultiPq2 = 1;
-constexpr int kPq2Bytes = 34;  // PQ2_0 block: fp16 scale, then 32 code bytes
+// biases), or PQ2_0 / PTQ1_0 blocks (the module's codes pointer holds the
+// blocks)
+constexpr int kMultiMlx = 0, kMultiPq2 = 1, kMultiPtq1 = 2;
+constexpr int kPq2Bytes = 34;   // PQ2_0 block: fp16 scale, then 32 code bytes
+constexpr int kPtq1Bytes = 28;  // PTQ1_0 block: fp16 scale, then 26 trit bytes (5 codes each, base 3)
+__host__ __device__ inline int multi_block_bytes(int fmt) { return fmt == kMultiPq2 ? kPq2Bytes : kPtq1Bytes; }
 
 struct MultiHeader {  // 64 bytes
   int32_t magic, count, tasks, grid;
@@ -90,9 +93,11 @@ __host__ __device__ inline int64_t multi_lds_xf(int max_nch) {
   return static_cast<int64_t>(max_nch) * 8 * kXfLimbs * kMultiArow;
 }
 __host__ __device__ inline int64_t multi_lds_ybuf(int max_nch) { return multi_lds_xf(max_nch) + max_nch * 8 * 8; }
-__host__ __device__ inline int64_t multi_lds_total(int max_nch) {
+__host__ __device__ inline int64_t multi_lds_lut(int max_nch) {
   return multi_lds_ybuf(max_nch) + kMultiWaves * kMultiYbuf * 16 * 4;
 }
+// (the trit table, 256 dwords, is used by PTQ1_0 plans only)
+__host__ __device__ inline int64_t multi_lds_total(int max_nch) { return multi_lds_lut(max_nch) + 256 * 4; }
 
 // ---------------------------------------------------------------------------
 // 1. transform every chunk of every module's input
@@ -136,11 +141,16 @@ struct MultiPair {
 struct MultiPairPq2 {
   uint32_t d[17];
 };
+// PTQ1_0: likewise two adjacent blocks, 56 bytes from an 8-byte boundary
+struct MultiPairPtq1 {
+  uint32_t d[14];
+};
 
 template <int NW, int P, int FMT>
 __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __restrict__ plan,
                                                                   char* __restrict__ ws) {
-  using Pair = typename std::conditional<FMT == kMultiPq2, MultiPairPq2, MultiPair>::type;
+  using Pair = typename std::conditional<
+      FMT == kMultiPq2, MultiPairPq2, typename std::conditional<FMT == kMultiPtq1, MultiPairPtq1, MultiPair>::type>::type;
   constexpr int kMultiThreads = 64 * NW;
   constexpr int M = 16, GPS = 4;
   extern __shared__ uint4 lds_dyn[];
@@ -160,6 +170,20 @@ __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __
   const int ar = c & 3, alg = (c >> 2) & 3;
   const bool a_lane = alg == lg;
   float* const ybuf = reinterpret_cast<float*>(lds + multi_lds_ybuf(max_nch)) + wave * (kMultiYbuf * 16);
+  // PTQ1_0: trit byte -> its five 2-bit codes at bits 0, 2, .., 8 (lowest
+  // base-3 digit first), written before the first piece's barrier
+  uint32_t* const lut = reinterpret_cast<uint32_t*>(lds + multi_lds_lut(max_nch));
+  if constexpr (FMT == kMultiPtq1) {
+    for (int i = tid; i < 256; i += kMultiThreads) {
+      uint32_t b = static_cast<uint32_t>(i), v = 0;
+#pragma unroll
+      for (int m = 0; m < 5; ++m) {
+        v |= (b % 3u) << (2 * m);
+        b /= 3u;
+      }
+      lut[i] = v;
+    }
+  }
 
   int img_off = -1;  // workspace offset of the operand image in LDS
   for (;;) {
@@ -197,11 +221,12 @@ __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __
     // tile, pair steps k = j * P2 + p.
     // PQ2_0: span 2 p + h takes groups 8 p + 2 lg + h, so a pair covers 8
     // groups whatever S is
-    const int P2 = FMT == kMultiPq2 ? (G + 7) >> 3 : (S + 1) >> 1;
+    const int P2 = FMT != kMultiMlx ? (G + 7) >> 3 : (S + 1) >> 1;
     const int ntw = ta + wave < tb ? (tb - ta - wave + NW - 1) / NW : 0;
     const int nsteps = ntw * P2;
-    const auto rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(md.codes), 0,
-                                                      FMT == kMultiPq2 ? md.N * G * kPq2Bytes : md.N * RB, kRsrcWord3);
+    const auto rc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t*>(md.codes), 0, FMT == kMultiMlx ? md.N * RB : md.N * G * multi_block_bytes(FMT),
+        kRsrcWord3);
     const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(md.scales), 0, md.N * G * 2, kRsrcWord3);
     const auto rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(md.biases), 0, md.N * G * 2, kRsrcWord3);
     const auto ry = __builtin_amdgcn_make_buffer_rsrc(md.y, 0, md.N * 4, kRsrcWord3);
@@ -245,6 +270,23 @@ __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __
           st.d[4 * q] = u.x; st.d[4 * q + 1] = u.y; st.d[4 * q + 2] = u.z; st.d[4 * q + 3] = u.w;
         }
         st.d[16] = __builtin_amdgcn_raw_buffer_load_b32(rc, b0, 64, 0);
+        if (++ip == P2) {
+          ip = 0;
+          ++it;
+        }
+        return;
+      } else if constexpr (FMT == kMultiPtq1) {
+        // blocks (row, 8 p + 2 lg) and (row, 8 p + 2 lg + 1): 56 contiguous bytes
+        const int row = (ta - md.tile0 + wave + it * NW) * M + c;
+        const int b0 = live ? (row * G + 8 * ip + 2 * lg) * kPtq1Bytes : kOob;
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+          const v4u u = __builtin_amdgcn_raw_buffer_load_b128(rc, b0, 16 * q, 0);
+          st.d[4 * q] = u.x; st.d[4 * q + 1] = u.y; st.d[4 * q + 2] = u.z; st.d[4 * q + 3] = u.w;
+        }
+        const v2u u = __builtin_amdgcn_raw_buffer_load_b64(rc, b0, 48, 0);
+        st.d[12] = u.x;
+        st.d[13] = u.y;
         if (++ip == P2) {
           ip = 0;
           ++it;
@@ -350,6 +392,45 @@ __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __
                       static_cast<float>(acc[1]) * 256.f + static_cast<float>(acc[0]);
       yacc += g < G ? sc * (v * xf.y - xf.x) : 0.f;
     };
+    // PTQ1_0 span h of pair p: group 8 p + 2 lg + h; block h at byte 28 h of
+    // the pair (scale first, then 26 trit bytes); the table turns each trit
+    // byte into its five codes at bits 10 i .. 10 i + 9 of the 256 code bits
+    auto span_ptq1 = [&](int pp, int h, const uint32_t* d) {
+      const int g = 8 * pp + 2 * lg + h;
+      const float2 xf = lds_xf[g];
+      if (a_lane) {
+        const uint4* ap =
+            reinterpret_cast<const uint4*>(lds_a + ((8 * pp + 2 * alg + h) * kXfLimbs + ar) * kMultiArow);
+#pragma unroll
+        for (int w = 0; w < kWordsPerGroup; ++w) av[w] = ap[w];
+      }
+      uint32_t wd[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wd[i] = 0u;
+#pragma unroll
+      for (int i = 0; i < 26; ++i) {
+        const int byte = kPtq1Bytes * h + 2 + i;
+        const uint32_t v = lut[(d[byte >> 2] >> (8 * (byte & 3))) & 0xFFu];
+        const int pos = 10 * i, wi = pos >> 5, o = pos & 31;
+        wd[wi] |= v << o;
+        if (o > 22 && wi + 1 < 8) wd[wi + 1] |= v >> (32 - o);
+      }
+      const uint32_t sbits = d[7 * h] & 0xFFFFu;
+      v4i acc0 = {}, acc1 = {};
+#pragma unroll
+      for (int w = 0; w < kWordsPerGroup; w += 2) {
+        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)av[w].x, (int)av[w].y, (int)av[w].z, (int)av[w].w},
+                                                     decode_word(wd[w]), acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+            v4i{(int)av[w + 1].x, (int)av[w + 1].y, (int)av[w + 1].z, (int)av[w + 1].w}, decode_word(wd[w + 1]),
+            acc1, 0, 0, 0);
+      }
+      const v4i acc = acc0 + acc1;
+      const float sc = half_bits_to_float(static_cast<uint16_t>(sbits));
+      const float v = static_cast<float>(acc[3]) * 16777216.f + static_cast<float>(acc[2]) * 65536.f +
+                      static_cast<float>(acc[1]) * 256.f + static_cast<float>(acc[0]);
+      yacc += g < G ? sc * (v * xf.y - xf.x) : 0.f;
+    };
     // Step sl of a round needs, from lane group sl of its row, dword
     // (lg >> 1) of the step's 8 halves for the pair's first span and dword
     // 2 + (lg >> 1) for its second (the lane's group is 8 p + lg / 8 p + 4 + lg).
@@ -361,15 +442,20 @@ __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __
     uint32_t s0x = 0, s0y = 0, s1x = 0, s1y = 0, s2x = 0, s2y = 0, s3x = 0, s3y = 0;
     uint32_t b0x = 0, b0y = 0, b1x = 0, b1y = 0, b2x = 0, b2y = 0, b3x = 0, b3y = 0;
     auto xl = [&](uint32_t v, int j) { return static_cast<uint32_t>(xor_lane_i(static_cast<int>(v), j, lane)); };
-    if constexpr (FMT == kMultiPq2) {
+    if constexpr (FMT != kMultiMlx) {
       for (int base = 0; base < nsteps; base += P) {
 #pragma unroll
         for (int sl = 0; sl < P; ++sl) {
           const Pair cur = ring[sl];
           load(base + sl + P, ring[sl], false);  // refill the slot before computing on its data
           if (base + sl < nsteps) {
-            span_pq2(p, 0, cur.d);
-            span_pq2(p, 1, cur.d);
+            if constexpr (FMT == kMultiPq2) {
+              span_pq2(p, 0, cur.d);
+              span_pq2(p, 1, cur.d);
+            } else {
+              span_ptq1(p, 0, cur.d);
+              span_ptq1(p, 1, cur.d);
+            }
             if (++p == P2) {
               float t = yacc + xor_lane(yacc, 4, lane);
               t += xor_lane(t, 5, lane);
@@ -558,9 +644,9 @@ static int multi_plan(const tb_gemv_module* mods, int64_t count, int x_dtype, in
       return TB_ERR_SHAPE;
     }
     if (m.N == 0) continue;
-    if (fmt == kMultiPq2) {
+    if (fmt != kMultiMlx) {
       if (!m.x || !m.codes || m.scales || m.biases || !m.y || (block > 0) != (m.signs != nullptr)) {
-        set_error("%s: module %lld: null pointer, or scales / biases given (PQ2_0 blocks carry them; signs "
+        set_error("%s: module %lld: null pointer, or scales / biases given (the blocks carry the scales; signs "
                   "must be given exactly when block > 0)", who, (long long)i);
         return TB_ERR_ARG;
       }
@@ -685,6 +771,12 @@ extern "C" int tb_pq2_gemv_multi_plan(const tb_gemv_module* mods, int64_t count,
                     "tb_pq2_gemv_multi_plan");
 }
 
+extern "C" int tb_ptq1_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int x_dtype, int block,
+                                       void* plan, size_t plan_bytes, size_t* workspace_bytes) {
+  return multi_plan(mods, count, x_dtype, block, kMultiPtq1, plan, plan_bytes, workspace_bytes,
+                    "tb_ptq1_gemv_multi_plan");
+}
+
 template <int L, int DT>
 static void multi_prep_launch(const void* plan, void* ws, int tasks, hipStream_t st) {
   hipLaunchKernelGGL((multi_prep_kernel<L, DT>), dim3((tasks + 3) / 4), dim3(256), 0, st,
@@ -710,7 +802,7 @@ extern "C" int tb_ternary_gemv_multi(const void* plan_host, const void* plan_dev
   MultiHeader hd;
   std::memcpy(&hd, plan_host, sizeof hd);
   if (hd.magic != kPlanMagic || hd.count <= 0 || hd.grid <= 0 || hd.pieces < 0 ||
-      (hd.format != kMultiMlx && hd.format != kMultiPq2)) {
+      (hd.format != kMultiMlx && hd.format != kMultiPq2 && hd.format != kMultiPtq1)) {
     set_error("%s: the host plan was not built by tb_gemv_multi_plan", who);
     return TB_ERR_ARG;
   }
@@ -742,6 +834,7 @@ extern "C" int tb_ternary_gemv_multi(const void* plan_host, const void* plan_dev
     TB_LAUNCH_CHECK(who);
     const size_t lds = static_cast<size_t>(multi_lds_total(hd.max_nch));
     if (hd.format == kMultiPq2) multi_stream_launch<kMultiWaves, kMultiRing, kMultiPq2>(plan_device, workspace, hd.grid, lds, st);
+    else if (hd.format == kMultiPtq1) multi_stream_launch<kMultiWaves, kMultiRing, kMultiPtq1>(plan_device, workspace, hd.grid, lds, st);
     else multi_stream_launch<kMultiWaves, kMultiRing, kMultiMlx>(plan_device, workspace, hd.grid, lds, st);
     TB_LAUNCH_CHECK(who);
   }

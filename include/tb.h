@@ -305,6 +305,14 @@ int tb_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int x_dtype, i
 int tb_pq2_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int x_dtype, int block,
                            void* plan, size_t plan_bytes, size_t* workspace_bytes);
 
+/* The same on PTQ1_0 blocks [P2 "packing-format engineering": dense trits,
+ * 28 bytes per 128 weights, 1.75 bits/weight]: each module's codes pointer
+ * holds its (N, K/128 * 28) byte array of PTQ1_0 blocks (4-byte aligned);
+ * scales and biases NULL.  Trit bytes above 242 decode to unspecified codes
+ * (tb_ptq1_unpack rejects them). */
+int tb_ptq1_gemv_multi_plan(const tb_gemv_module* mods, int64_t count, int x_dtype, int block,
+                            void* plan, size_t plan_bytes, size_t* workspace_bytes);
+
 /* Run a plan: plan_host is the buffer tb_gemv_multi_plan filled (read on the
  * host for the launch sizes), plan_device a copy of it in device memory
  * (16-byte aligned, read by the kernels; the caller owns both).  workspace:

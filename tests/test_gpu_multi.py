@@ -127,21 +127,26 @@ def test_multi_shared_inputs_match_oracle_and_single_calls():
         assert d <= 1e-6 * y1.abs().max().item(), (key, N, d)
 
 
-def _run_multi_pq2(shapes, block, xd, seed):
-    """PQ2_0 modules (host packer + transcode, checked against the oracle's
+def _run_multi_pq2(shapes, block, xd, seed, fmt="pq2"):
+    """PQ2_0 or PTQ1_0 modules (host packers, checked against the oracle's
     blocks byte for byte) in one plan, run once."""
     T = torch()
     probs, mods, blks = [], [], []
     for i, (N, K) in enumerate(shapes):
         p = synth.make_problem("multi", N, K, 1, [seed, i, N, K], xd, block)
-        c, s, b = tb.tb_pack(p.t, p.scales)
-        blk = tb.tb_pq2_from_mlx(c, s, b)
-        assert np.array_equal(blk, oracle.pq2_from_mlx(*oracle.pack(p.t, p.scales)))
+        if fmt == "pq2":
+            c, s, b = tb.tb_pack(p.t, p.scales)
+            blk = tb.tb_pq2_from_mlx(c, s, b)
+            assert np.array_equal(blk, oracle.pq2_from_mlx(*oracle.pack(p.t, p.scales)))
+        else:
+            blk = tb.tb_ptq1_pack(p.t, p.scales)
+            assert np.array_equal(blk, oracle.ptq1_pack(p.t, p.scales))
         y = T.full((1, N), float("nan"), dtype=T.float32, device="cuda")
         mods.append((x_to_device(p), signs_to_device(p.signs), T.from_numpy(blk).cuda(), y))
         probs.append(p)
         blks.append(blk)
-    plan, wsb = tb.tb_pq2_gemv_multi_plan(mods, block, tb.TB_F32 if xd == "f32" else tb.TB_BF16)
+    planner = tb.tb_pq2_gemv_multi_plan if fmt == "pq2" else tb.tb_ptq1_gemv_multi_plan
+    plan, wsb = planner(mods, block, tb.TB_F32 if xd == "f32" else tb.TB_BF16)
     pd = T.from_numpy(plan).cuda()
     ws = T.empty(wsb, dtype=T.uint8, device="cuda")
     tb.tb_ternary_gemv_multi(plan, pd, ws)
@@ -156,24 +161,28 @@ PQ2_CASES = [
 ]
 
 
+@pytest.mark.parametrize("fmt", ["pq2", "ptq1"])
 @pytest.mark.parametrize("xd,block,shapes", PQ2_CASES)
-def test_pq2_multi_matches_oracle(xd, block, shapes):
-    announce(f"pq2 multi x={xd} block={block} shapes={shapes}")
-    probs, mods, blks, *_ = _run_multi_pq2(shapes, block, xd, 80)
+def test_block_multi_matches_oracle(fmt, xd, block, shapes):
+    announce(f"{fmt} multi x={xd} block={block} shapes={shapes}")
+    probs, mods, blks, *_ = _run_multi_pq2(shapes, block, xd, 80, fmt)
+    ref = oracle.pq2_packed_linear if fmt == "pq2" else oracle.ptq1_packed_linear
     for p, m, blk in zip(probs, mods, blks):
         if p.N == 0:
             continue
-        want = oracle.pq2_packed_linear(p.x64, p.signs, block, blk, p.K)
-        compare(m[3].cpu().numpy(), want, f"pq2 multi module N={p.N} K={p.K}")
+        want = ref(p.x64, p.signs, block, blk, p.K)
+        compare(m[3].cpu().numpy(), want, f"{fmt} multi module N={p.N} K={p.K}")
 
 
-def test_pq2_multi_rerun_is_bitwise_stable_and_matches_single_calls():
-    """Rerunning a PQ2_0 plan gives the same bits; each module agrees with
-    its single tb_pq2_gemv call within 1e-6 of max |y|."""
-    announce("pq2 multi rerun + single-call agreement")
+@pytest.mark.parametrize("fmt", ["pq2", "ptq1"])
+def test_block_multi_rerun_is_bitwise_stable_and_matches_single_calls(fmt):
+    """Rerunning a PQ2_0 / PTQ1_0 plan gives the same bits; each module
+    agrees with its single tb_pq2_gemv / tb_ptq1_gemv call within 1e-6 of
+    max |y|."""
+    announce(f"{fmt} multi rerun + single-call agreement")
     T = torch()
     shapes = [(300, 5120), (1024, 5120), (77, 6144), (513, 17408)]
-    probs, mods, blks, plan, pd, ws = _run_multi_pq2(shapes, 1024, "bf16", 81)
+    probs, mods, blks, plan, pd, ws = _run_multi_pq2(shapes, 1024, "bf16", 81, fmt)
     first = [m[3].clone() for m in mods]
     for m in mods:
         m[3].fill_(float("nan"))
@@ -183,7 +192,7 @@ def test_pq2_multi_rerun_is_bitwise_stable_and_matches_single_calls():
         assert T.equal(f, m[3])
     for p, m in zip(probs, mods):
         x, sg, bd, y = m
-        y1 = tb.tb_pq2_gemv(x, sg, 1024, bd)
+        y1 = (tb.tb_pq2_gemv if fmt == "pq2" else tb.tb_ptq1_gemv)(x, sg, 1024, bd)
         T.cuda.synchronize()
         d = (y1.double() - y.double()).abs().max().item()
         assert d <= 1e-6 * y1.abs().max().item(), (p.N, p.K, d)

@@ -177,19 +177,20 @@ def test_same_x_different_signs_or_width_is_not_shared():
     assert p["tasks"] == 9 and p["NK"][0, 3] != p["NK"][1, 3]
 
 
-def test_pq2_plan_format_and_checks():
-    """PQ2_0 plans: the header's format word is 1 (0 for the MLX container),
-    the pieces and tasks are those of the same shapes in the MLX container,
-    scales or biases given are refused, and the blocks need 4-byte (not
-    16-byte) alignment."""
+@pytest.mark.parametrize("fmt,word", [("pq2", 1), ("ptq1", 2)])
+def test_block_plan_format_and_checks(fmt, word):
+    """PQ2_0 / PTQ1_0 plans: the header's format word is 1 / 2 (0 for the
+    MLX container), the pieces and tasks are those of the same shapes in the
+    MLX container, scales or biases given are refused, and the blocks need
+    4-byte (not 16-byte) alignment."""
     shapes = [(10240, 5120), (1024, 5120), (5120, 17408), (45, 2048)]
+    fn = tb.lib().tb_pq2_gemv_multi_plan if fmt == "pq2" else tb.lib().tb_ptq1_gemv_multi_plan
 
     def pq2_plan(arr):
         size = tb.lib().tb_gemv_multi_plan_size(arr, len(shapes))
         plan = np.zeros(max(size, 64), np.uint8)
         ws = ctypes.c_size_t(0)
-        st = tb.lib().tb_pq2_gemv_multi_plan(arr, len(shapes), tb.TB_BF16, 1024, plan.ctypes.data, plan.nbytes,
-                                             ctypes.byref(ws))
+        st = fn(arr, len(shapes), tb.TB_BF16, 1024, plan.ctypes.data, plan.nbytes, ctypes.byref(ws))
         return st, plan, ws.value
 
     arr = _mods(shapes)
@@ -201,7 +202,7 @@ def test_pq2_plan_format_and_checks():
     assert st == tb.TB_OK, tb.lib().tb_last_error()
     st0, plan0, ws0 = _plan(shapes)
     assert st0 == tb.TB_OK
-    assert int(plan[60:64].view(np.int32)[0]) == 1 and int(plan0[60:64].view(np.int32)[0]) == 0
+    assert int(plan[60:64].view(np.int32)[0]) == word and int(plan0[60:64].view(np.int32)[0]) == 0
     p, p0 = _parse(plan), _parse(plan0)
     assert ws == ws0 and np.array_equal(p["pc"], p0["pc"]) and np.array_equal(p["tk"], p0["tk"])
     # scales given: refused
