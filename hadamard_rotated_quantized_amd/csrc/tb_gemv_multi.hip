@@ -34,6 +34,14 @@
 //    base-256 limbs, one A row each, read from LDS), with the fp16 scale and
 //    bias applied in fp32; a tile's rows are written once, after its last
 //    span.
+//
+// The same plan and kernels take the weights as PQ2_0 or PTQ1_0 blocks
+// (kwkr.cn/news/564617, "packing-format engineering"; a plan holds one
+// container for all its modules).  There a lane's span pair is two adjacent
+// blocks of its row (groups 8 p + 2 lg and 8 p + 2 lg + 1, with the A rows
+// in the same group order), one contiguous run of 68 or 56 bytes that
+// carries the codes and both scales; PTQ1_0's trit bytes go through a
+// 256-entry table in LDS to the 2-bit codes the other paths decode.
 #include <algorithm>
 #include <array>
 #include <map>
