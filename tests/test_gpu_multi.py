@@ -127,7 +127,7 @@ def test_multi_shared_inputs_match_oracle_and_single_calls():
         assert d <= 1e-6 * y1.abs().max().item(), (key, N, d)
 
 
-def _run_multi_pq2(shapes, block, xd, seed, fmt="pq2"):
+def _run_multi_blocks(shapes, block, xd, seed, fmt="pq2"):
     """PQ2_0 or PTQ1_0 modules (host packers, checked against the oracle's
     blocks byte for byte) in one plan, run once."""
     T = torch()
@@ -154,7 +154,7 @@ def _run_multi_pq2(shapes, block, xd, seed, fmt="pq2"):
     return probs, mods, blks, plan, pd, ws
 
 
-PQ2_CASES = [
+BLOCK_CASES = [
     ("bf16", 1024, [(1, 1024), (45, 2048), (300, 5120), (1000, 6144), (16, 17408), (0, 1024), (4099, 1024)]),
     ("f32", 512, [(17, 1024), (33, 1536), (200, 512)]),
     ("bf16", 0, [(45, 256), (300, 768), (16, 1024)]),
@@ -162,10 +162,10 @@ PQ2_CASES = [
 
 
 @pytest.mark.parametrize("fmt", ["pq2", "ptq1"])
-@pytest.mark.parametrize("xd,block,shapes", PQ2_CASES)
+@pytest.mark.parametrize("xd,block,shapes", BLOCK_CASES)
 def test_block_multi_matches_oracle(fmt, xd, block, shapes):
     announce(f"{fmt} multi x={xd} block={block} shapes={shapes}")
-    probs, mods, blks, *_ = _run_multi_pq2(shapes, block, xd, 80, fmt)
+    probs, mods, blks, *_ = _run_multi_blocks(shapes, block, xd, 80, fmt)
     ref = oracle.pq2_packed_linear if fmt == "pq2" else oracle.ptq1_packed_linear
     for p, m, blk in zip(probs, mods, blks):
         if p.N == 0:
@@ -182,7 +182,7 @@ def test_block_multi_rerun_is_bitwise_stable_and_matches_single_calls(fmt):
     announce(f"{fmt} multi rerun + single-call agreement")
     T = torch()
     shapes = [(300, 5120), (1024, 5120), (77, 6144), (513, 17408)]
-    probs, mods, blks, plan, pd, ws = _run_multi_pq2(shapes, 1024, "bf16", 81, fmt)
+    probs, mods, blks, plan, pd, ws = _run_multi_blocks(shapes, 1024, "bf16", 81, fmt)
     first = [m[3].clone() for m in mods]
     for m in mods:
         m[3].fill_(float("nan"))
@@ -196,3 +196,25 @@ def test_block_multi_rerun_is_bitwise_stable_and_matches_single_calls(fmt):
         T.cuda.synchronize()
         d = (y1.double() - y.double()).abs().max().item()
         assert d <= 1e-6 * y1.abs().max().item(), (p.N, p.K, d)
+
+
+@pytest.mark.parametrize("fmt", ["pq2", "ptq1"])
+def test_block_multi_graph_replays_match_eager(fmt):
+    """A PQ2_0 / PTQ1_0 plan captured in a HIP graph: every replay (with the
+    outputs cleared between them) gives the eager run's bits."""
+    announce(f"{fmt} multi graph replay")
+    T = torch()
+    shapes = [(600, 5120), (100, 17408)]
+    probs, mods, blks, plan, pd, ws = _run_multi_blocks(shapes, 1024, "bf16", 82, fmt)
+    eager = [m[3].clone() for m in mods]
+    g = T.cuda.CUDAGraph()
+    with T.cuda.graph(g):
+        tb.tb_ternary_gemv_multi(plan, pd, ws)
+    for r in range(3):
+        for m in mods:
+            m[3].zero_()
+        T.cuda.synchronize()
+        g.replay()
+        T.cuda.synchronize()
+        for e, m in zip(eager, mods):
+            assert T.equal(e, m[3]), r
