@@ -104,13 +104,67 @@ __host__ __device__ inline int64_t multi_lds_ybuf(int max_nch) { return multi_ld
 __host__ __device__ inline int64_t multi_lds_lut(int max_nch) {
   return multi_lds_ybuf(max_nch) + kMultiWaves * kMultiYbuf * 16 * 4;
 }
-// (the trit table, 256 dwords, is used by PTQ1_0 plans only)
-__host__ __device__ inline int64_t multi_lds_total(int max_nch) { return multi_lds_lut(max_nch) + 256 * 4; }
+// (the trit table, 256 entries of 8 bytes, is used by PTQ1_0 plans only)
+__host__ __device__ inline int64_t multi_lds_total(int max_nch) { return multi_lds_lut(max_nch) + 256 * 8; }
 
 // ---------------------------------------------------------------------------
 // 1. transform every chunk of every module's input
 // ---------------------------------------------------------------------------
+// The operand image in natural element order, for PTQ1_0 plans: byte p of a
+// (group, limb) row is element p of the group.  xform_chunk (tb_xform.h)
+// writes each 16-element block transposed (byte 4 x + t = element x + 4 t),
+// the order the 2-bit code-word decode produces; PTQ1_0's trit table gives
+// the codes in natural order instead.  Same scaling and limbs as
+// xform_chunk; before the stores the lanes of each quad (the four lanes that
+// hold one 16-element block) transpose their dwords bytewise (two DPP
+// exchanges and two byte permutes per dword).
 template <int L, int DT>
+__device__ __forceinline__ void xform_chunk_natural(const XformIn<DT>& in, int g0, int lane, const v4u cfirst[2],
+                                                    const v4u csecond[2], char* img, float2* xf) {
+  float v128;
+  const v16f U = xform_rotate<L, DT>(in, lane, cfirst, csecond, v128);
+  float m = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(U[r]));
+#pragma unroll
+  for (int j = 0; j < 6; ++j) m = fmaxf(m, xor_lane(m, j, lane));
+  const uint32_t mb = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(__float_as_uint(m))));
+  int e = static_cast<int>((mb >> 23) & 0xFF) - 127;
+  e = mb == 0 ? 0 : (e < -90 ? -90 : e);
+  const float sigma = __uint_as_float(static_cast<uint32_t>(29 - e + 127) << 23);
+  const float f = __uint_as_float(static_cast<uint32_t>(e - 29 + 127) << 23) * inv_sqrt_block_or_one<L>();
+  uint32_t qd[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) qd[r] = static_cast<uint32_t>(static_cast<int>(U[r] * sigma)) + 0x808080u;
+  // quad transpose selectors: with lane x ^ 2, then with lane x ^ 1
+  const int x = lane & 3;
+  const uint32_t sel1 = (x >> 1) ? 0x03020706u : 0x05040100u;
+  const uint32_t sel2 = (x & 1) ? 0x03070105u : 0x06020400u;
+  auto quad_t = [&](uint32_t d) {
+    const uint32_t p = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(d), 0x4E, 0xF, 0xF, false));
+    const uint32_t d1 = __builtin_amdgcn_perm(p, d, sel1);
+    const uint32_t q = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(d1), 0xB1, 0xF, 0xF, false));
+    return __builtin_amdgcn_perm(q, d1, sel2);
+  };
+  const int h = lane >> 5;
+  char* const arow = img + static_cast<int64_t>(g0 + h) * (kXfLimbs * 128) + (lane & 31) * 4;
+#pragma unroll
+  for (int Q = 0; Q < 4; ++Q) {
+    const uint32_t a0 = qd[4 * Q], a1 = qd[4 * Q + 1], a2 = qd[4 * Q + 2], a3 = qd[4 * Q + 3];
+    const uint32_t l0 = (__builtin_amdgcn_perm(a1, a0, 0x0C0C0400u) | __builtin_amdgcn_perm(a3, a2, 0x04000C0Cu)) ^ 0x80808080u;
+    const uint32_t l1 = (__builtin_amdgcn_perm(a1, a0, 0x0C0C0501u) | __builtin_amdgcn_perm(a3, a2, 0x05010C0Cu)) ^ 0x80808080u;
+    const uint32_t l2 = (__builtin_amdgcn_perm(a1, a0, 0x0C0C0602u) | __builtin_amdgcn_perm(a3, a2, 0x06020C0Cu)) ^ 0x80808080u;
+    const uint32_t l3 = __builtin_amdgcn_perm(a1, a0, 0x0C0C0703u) | __builtin_amdgcn_perm(a3, a2, 0x07030C0Cu);
+    char* row = arow + static_cast<int64_t>(2 * Q) * (kXfLimbs * 128);
+    *reinterpret_cast<uint32_t*>(row) = quad_t(l0);
+    *reinterpret_cast<uint32_t*>(row + 128) = quad_t(l1);
+    *reinterpret_cast<uint32_t*>(row + 256) = quad_t(l2);
+    *reinterpret_cast<uint32_t*>(row + 384) = quad_t(l3);
+  }
+  xform_group_sums<L>(U, v128, g0, lane, f, xf);
+}
+
+template <int L, int DT, bool NAT>
 __global__ __launch_bounds__(256) void multi_prep_kernel(const char* __restrict__ plan, char* __restrict__ ws) {
   const MultiHeader* hd = reinterpret_cast<const MultiHeader*>(plan);
   const int lane = threadIdx.x & 63;
@@ -133,7 +187,8 @@ __global__ __launch_bounds__(256) void multi_prep_kernel(const char* __restrict_
   const v4u cs[2] = {cst2[0], cst2[1]};
   char* img = ws + md.ws_off;
   float2* xf = reinterpret_cast<float2*>(img + static_cast<int64_t>(multi_nch(md.K)) * kMultiImgChunk);
-  xform_chunk<L, DT>(in, 8 * c, lane, cf, cs, img, xf, 128);
+  if constexpr (NAT) xform_chunk_natural<L, DT>(in, 8 * c, lane, cf, cs, img, xf);
+  else xform_chunk<L, DT>(in, 8 * c, lane, cf, cs, img, xf, 128);
 }
 
 // ---------------------------------------------------------------------------
@@ -178,18 +233,19 @@ __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __
   const int ar = c & 3, alg = (c >> 2) & 3;
   const bool a_lane = alg == lg;
   float* const ybuf = reinterpret_cast<float*>(lds + multi_lds_ybuf(max_nch)) + wave * (kMultiYbuf * 16);
-  // PTQ1_0: trit byte -> its five 2-bit codes at bits 0, 2, .., 8 (lowest
-  // base-3 digit first), written before the first piece's barrier
-  uint32_t* const lut = reinterpret_cast<uint32_t*>(lds + multi_lds_lut(max_nch));
+  // PTQ1_0: trit byte -> its five codes (lowest base-3 digit first) as
+  // bytes 0-4 of an 8-byte entry, written before the first piece's barrier
+  uint2* const lut = reinterpret_cast<uint2*>(lds + multi_lds_lut(max_nch));
   if constexpr (FMT == kMultiPtq1) {
     for (int i = tid; i < 256; i += kMultiThreads) {
-      uint32_t b = static_cast<uint32_t>(i), v = 0;
+      uint32_t b = static_cast<uint32_t>(i), lo = 0, hi = 0;
 #pragma unroll
-      for (int m = 0; m < 5; ++m) {
-        v |= (b % 3u) << (2 * m);
+      for (int m = 0; m < 4; ++m) {
+        lo |= (b % 3u) << (8 * m);
         b /= 3u;
       }
-      lut[i] = v;
+      hi = b % 3u;
+      lut[i] = make_uint2(lo, hi);
     }
   }
 
@@ -412,26 +468,38 @@ __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __
 #pragma unroll
         for (int w = 0; w < kWordsPerGroup; ++w) av[w] = ap[w];
       }
-      uint32_t wd[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) wd[i] = 0u;
+      // the group's 128 codes as bytes in natural order (the operand image of
+      // PTQ1_0 plans is in natural order too): code 5 i + j is byte j of
+      // trit byte i's table entry; byte dword o (codes 4 o .. 4 o + 3)
+      // starts at entry i = 4 o / 5, byte j = 4 o % 5
+      uint2 ent[26];
 #pragma unroll
       for (int i = 0; i < 26; ++i) {
         const int byte = kPtq1Bytes * h + 2 + i;
-        const uint32_t v = lut[(d[byte >> 2] >> (8 * (byte & 3))) & 0xFFu];
-        const int pos = 10 * i, wi = pos >> 5, o = pos & 31;
-        wd[wi] |= v << o;
-        if (o > 22 && wi + 1 < 8) wd[wi + 1] |= v >> (32 - o);
+        ent[i] = lut[(d[byte >> 2] >> (8 * (byte & 3))) & 0xFFu];
+      }
+      uint32_t cb[32];
+#pragma unroll
+      for (int o = 0; o < 32; ++o) {
+        const int i = (4 * o) / 5, j = (4 * o) % 5;
+        const uint2 a = ent[i];
+        const uint2 b = i + 1 < 26 ? ent[i + 1] : make_uint2(0u, 0u);
+        if (j == 0) cb[o] = a.x;
+        else if (j == 1) cb[o] = __builtin_amdgcn_alignbyte(a.y, a.x, 1);
+        else if (j == 2) cb[o] = __builtin_amdgcn_alignbyte(a.y, a.x, 2) | (b.x << 24);
+        else if (j == 3) cb[o] = __builtin_amdgcn_alignbyte(a.y, a.x, 3) | (b.x << 16);
+        else cb[o] = a.y | (b.x << 8);
       }
       const uint32_t sbits = d[7 * h] & 0xFFFFu;
       v4i acc0 = {}, acc1 = {};
 #pragma unroll
       for (int w = 0; w < kWordsPerGroup; w += 2) {
-        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)av[w].x, (int)av[w].y, (int)av[w].z, (int)av[w].w},
-                                                     decode_word(wd[w]), acc0, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+            v4i{(int)av[w].x, (int)av[w].y, (int)av[w].z, (int)av[w].w},
+            v4i{(int)cb[4 * w], (int)cb[4 * w + 1], (int)cb[4 * w + 2], (int)cb[4 * w + 3]}, acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-            v4i{(int)av[w + 1].x, (int)av[w + 1].y, (int)av[w + 1].z, (int)av[w + 1].w}, decode_word(wd[w + 1]),
-            acc1, 0, 0, 0);
+            v4i{(int)av[w + 1].x, (int)av[w + 1].y, (int)av[w + 1].z, (int)av[w + 1].w},
+            v4i{(int)cb[4 * w + 4], (int)cb[4 * w + 5], (int)cb[4 * w + 6], (int)cb[4 * w + 7]}, acc1, 0, 0, 0);
       }
       const v4i acc = acc0 + acc1;
       const float sc = half_bits_to_float(static_cast<uint16_t>(sbits));
@@ -786,9 +854,13 @@ extern "C" int tb_ptq1_gemv_multi_plan(const tb_gemv_module* mods, int64_t count
 }
 
 template <int L, int DT>
-static void multi_prep_launch(const void* plan, void* ws, int tasks, hipStream_t st) {
-  hipLaunchKernelGGL((multi_prep_kernel<L, DT>), dim3((tasks + 3) / 4), dim3(256), 0, st,
-                     static_cast<const char*>(plan), static_cast<char*>(ws));
+static void multi_prep_launch(const void* plan, void* ws, int tasks, bool natural, hipStream_t st) {
+  if (natural)
+    hipLaunchKernelGGL((multi_prep_kernel<L, DT, true>), dim3((tasks + 3) / 4), dim3(256), 0, st,
+                       static_cast<const char*>(plan), static_cast<char*>(ws));
+  else
+    hipLaunchKernelGGL((multi_prep_kernel<L, DT, false>), dim3((tasks + 3) / 4), dim3(256), 0, st,
+                       static_cast<const char*>(plan), static_cast<char*>(ws));
 }
 
 template <int NW, int P, int FMT>
@@ -830,14 +902,15 @@ extern "C" int tb_ternary_gemv_multi(const void* plan_host, const void* plan_dev
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (hd.tasks > 0) {
     const int L = hd.block;
+    const bool nat = hd.format == kMultiPtq1;  // PTQ1_0: the operand image in natural element order
     if (hd.x_dtype == TB_F32) {
-      if (L == 0) multi_prep_launch<0, TB_F32>(plan_device, workspace, hd.tasks, st);
-      else if (L == 512) multi_prep_launch<512, TB_F32>(plan_device, workspace, hd.tasks, st);
-      else multi_prep_launch<1024, TB_F32>(plan_device, workspace, hd.tasks, st);
+      if (L == 0) multi_prep_launch<0, TB_F32>(plan_device, workspace, hd.tasks, nat, st);
+      else if (L == 512) multi_prep_launch<512, TB_F32>(plan_device, workspace, hd.tasks, nat, st);
+      else multi_prep_launch<1024, TB_F32>(plan_device, workspace, hd.tasks, nat, st);
     } else {
-      if (L == 0) multi_prep_launch<0, TB_BF16>(plan_device, workspace, hd.tasks, st);
-      else if (L == 512) multi_prep_launch<512, TB_BF16>(plan_device, workspace, hd.tasks, st);
-      else multi_prep_launch<1024, TB_BF16>(plan_device, workspace, hd.tasks, st);
+      if (L == 0) multi_prep_launch<0, TB_BF16>(plan_device, workspace, hd.tasks, nat, st);
+      else if (L == 512) multi_prep_launch<512, TB_BF16>(plan_device, workspace, hd.tasks, nat, st);
+      else multi_prep_launch<1024, TB_BF16>(plan_device, workspace, hd.tasks, nat, st);
     }
     TB_LAUNCH_CHECK(who);
     const size_t lds = static_cast<size_t>(multi_lds_total(hd.max_nch));
