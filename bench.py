@@ -61,7 +61,7 @@ COUNTER_SUMMARIES = {
     "prefill_gate_up": (os.path.join(ROOT, "profiles", "gemm_mx_kernel_prefill_gate_up_counters.txt"),
                         _srcs("tb_gemm.hip", "tb_xform.h")),
     "sweep": (os.path.join(ROOT, "profiles", "multi_stream_kernel_sweep_counters.txt"),
-              _srcs("tb_gemv_multi.hip", "tb_xform.h")),
+              _srcs("tb_gemv_multi.hip", "tb_ptq1_nat.h", "tb_xform.h")),
     "down_proj_b1": (os.path.join(ROOT, "profiles", "gemv_fused_kernel_down_proj_b1_counters.txt"),
                      _srcs("tb_gemv_fused.hip")),
     "down_proj_b2": (os.path.join(ROOT, "profiles", "batch_stream_kernel_down_proj_b2_counters.txt"),

@@ -26,7 +26,9 @@
 // Lane (lane group lg, row c) loads the whole block (row c, group 4 s + lg)
 // with dword-aligned loads, rebuilds its eight 16-code words in registers
 // (PQ2_0: byte-align the code bytes that follow the 2-byte scale; PTQ1_0: a
-// 256-entry LDS table maps a trit byte to its five 2-bit codes), and the
+// 256-entry LDS table maps a trit byte to its five codes as bytes, the
+// operand in natural element order against limb rows written in that order
+// too, tb_ptq1_nat.h), and the
 // span is 8 v_mfma_i32_16x16x64_i8 against a block-diagonal activation
 // operand (A row (group a, limb l) non-zero only in k-block a, so one
 // instruction keeps the 4 groups apart).  A ring of P items of loads is in
@@ -34,7 +36,7 @@
 // in LDS; the band's rows are the sums over the waves in wave order.
 #include <algorithm>
 
-#include "tb_xform.h"
+#include "tb_ptq1_nat.h"
 
 namespace tb {
 
@@ -62,7 +64,8 @@ __host__ __device__ inline int blk_nch(int K) { return (K + 1023) >> 10; }
 // LDS: operand image, group terms, trit table, partial row sums
 __host__ __device__ inline int64_t blk_lds_xf(int nch) { return static_cast<int64_t>(nch) * 8 * kXfLimbs * kBlkArow; }
 __host__ __device__ inline int64_t blk_lds_lut(int nch) { return blk_lds_xf(nch) + nch * 8 * 8; }
-__host__ __device__ inline int64_t blk_lds_red(int nch) { return blk_lds_lut(nch) + 256 * 4; }
+// (the trit table: 256 entries of 8 bytes, used by PTQ1_0)
+__host__ __device__ inline int64_t blk_lds_red(int nch) { return blk_lds_lut(nch) + 256 * 8; }
 __host__ __device__ inline int64_t blk_lds_total(int nch, int tiles) {
   return blk_lds_red(nch) + static_cast<int64_t>(tiles) * kBlkWaves * 16 * 4;
 }
@@ -72,50 +75,19 @@ struct BlkSlot {
   uint32_t d[BlkFmt<FMT>::DW];
 };
 
-// Trit byte b -> its five 2-bit codes at bits 0, 2, .., 8 (lowest base-3
-// digit first); bytes above 242 hold no valid trits and decode to whatever
-// digits the division gives (the host-side unpack rejects them).
-__device__ __forceinline__ uint32_t trit_byte_codes(uint32_t b) {
-  uint32_t v = 0;
+// PQ2_0: the block's eight 16-code words and its scale bits, from the window
+// of 36 bytes from the dword holding the block's first byte (the block
+// starts at byte sh, 0 or 2, of it; its codes at byte sh + 2).  PTQ1_0 blocks
+// decode through the trit table (tb_ptq1_nat.h).
+__device__ __forceinline__ void pq2_words(const BlkSlot<kPq2>& sl, int sh, uint32_t w[8], uint32_t& scale) {
+  uint32_t e[9];
 #pragma unroll
-  for (int m = 0; m < 5; ++m) {
-    v |= (b % 3u) << (2 * m);
-    b /= 3u;
-  }
-  return v;
-}
-
-// The block's eight 16-code words and its scale bits.
-template <int FMT>
-__device__ __forceinline__ void blk_words(const BlkSlot<FMT>& sl, int sh, const uint32_t* lut, uint32_t w[8],
-                                          uint32_t& scale) {
-  if constexpr (FMT == kPq2) {
-    // window of 36 bytes from the dword holding the block's first byte; the
-    // block starts at byte sh (0 or 2) of it, its codes at byte sh + 2
-    uint32_t e[9];
+  for (int i = 0; i < 8; ++i) e[i] = sh ? sl.d[i + 1] : sl.d[i];
+  e[8] = sl.d[8];
+  const uint32_t bs = sh ? 0u : 2u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) e[i] = sh ? sl.d[i + 1] : sl.d[i];
-    e[8] = sl.d[8];
-    const uint32_t bs = sh ? 0u : 2u;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = __builtin_amdgcn_alignbyte(e[i + 1], e[i], bs);
-    scale = sh ? (sl.d[0] >> 16) : (sl.d[0] & 0xFFFFu);
-  } else {
-    // trit byte i sits at byte 2 + i of the 28-byte block; its five codes go
-    // to bits 10 i .. 10 i + 9 of the 256 code bits
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = 0u;
-#pragma unroll
-    for (int i = 0; i < 26; ++i) {
-      const int byte = 2 + i;
-      const uint32_t b = (sl.d[byte >> 2] >> (8 * (byte & 3))) & 0xFFu;
-      const uint32_t v = lut[b];
-      const int pos = 10 * i, wi = pos >> 5, o = pos & 31;
-      w[wi] |= v << o;
-      if (o > 22 && wi + 1 < 8) w[wi + 1] |= v >> (32 - o);
-    }
-    scale = sl.d[0] & 0xFFFFu;
-  }
+  for (int i = 0; i < 8; ++i) w[i] = __builtin_amdgcn_alignbyte(e[i + 1], e[i], bs);
+  scale = sh ? (sl.d[0] >> 16) : (sl.d[0] & 0xFFFFu);
 }
 
 template <int L, int DT, int FMT, int P>
@@ -134,7 +106,7 @@ __global__ __launch_bounds__(kBlkThreads, 1) void blocks_gemv_kernel(const void*
   const bool a_lane = alg == lg;
   char* const lds_a = lds;
   float2* const lds_xf = reinterpret_cast<float2*>(lds + blk_lds_xf(nch));
-  uint32_t* const lut = reinterpret_cast<uint32_t*>(lds + blk_lds_lut(nch));
+  uint2* const lut8 = reinterpret_cast<uint2*>(lds + blk_lds_lut(nch));  // PTQ1_0 trit table
   float* const red = reinterpret_cast<float*>(lds + blk_lds_red(nch));
 
   // the band: rows band0 .. band0 + nrow - 1 in tiles of 16 (the last may be
@@ -208,18 +180,23 @@ __global__ __launch_bounds__(kBlkThreads, 1) void blocks_gemv_kernel(const void*
     const v4u* cst2 = reinterpret_cast<const v4u*>(&kXformConst.w[xf_mode<L>()][1][lane][0]);
     const v4u cf[2] = {cst[0], cst[1]};
     const v4u cs[2] = {cst2[0], cst2[1]};
+    // PTQ1_0: limb rows in natural element order, to match its code bytes
+    auto xform = [&](const XformIn<DT>& in, int ch) {
+      if constexpr (FMT == kPtq1) xform_chunk_natural<L, DT>(in, 8 * ch, lane, cf, cs, lds_a, lds_xf, kBlkArow);
+      else xform_chunk<L, DT>(in, 8 * ch, lane, cf, cs, lds_a, lds_xf, kBlkArow);
+    };
 #pragma unroll
     for (int r = 0; r < kBlkMaxTasks; ++r) {
       const int ch = wave + NW * r;
-      if (ch < nch) xform_chunk<L, DT>(xin[r], 8 * ch, lane, cf, cs, lds_a, lds_xf, kBlkArow);
+      if (ch < nch) xform(xin[r], ch);
     }
     for (int ch = wave + NW * kBlkMaxTasks; ch < nch; ch += NW) {
       XformIn<DT> in;
       xform_issue<L, DT>(rx, rsg, static_cast<int64_t>(ch) * 1024, ch * 1024, lane, in);
-      xform_chunk<L, DT>(in, 8 * ch, lane, cf, cs, lds_a, lds_xf, kBlkArow);
+      xform(in, ch);
     }
     if constexpr (FMT == kPtq1)
-      for (int i = tid; i < 256; i += kBlkThreads) lut[i] = trit_byte_codes(static_cast<uint32_t>(i));
+      for (int i = tid; i < 256; i += kBlkThreads) lut8[i] = trit_entry(static_cast<uint32_t>(i));
     for (int i = tid; i < tsub * NW * 16; i += kBlkThreads) red[i] = 0.f;
   }
   __syncthreads();
@@ -236,8 +213,22 @@ __global__ __launch_bounds__(kBlkThreads, 1) void blocks_gemv_kernel(const void*
       const BlkSlot<FMT> cur = ring[q];
       load(ring[q]);  // refill the slot before computing on its data
       if (base + q < nit) {
-        uint32_t w[8], sbits;
-        blk_words<FMT>(cur, sh, lut, w, sbits);
+        // MFMA operands of the block's codes: PQ2_0 the 2-bit words decoded;
+        // PTQ1_0 the codes as bytes in natural order (trit table)
+        v4i bq[kWordsPerGroup];
+        uint32_t sbits;
+        if constexpr (FMT == kPq2) {
+          uint32_t w[8];
+          pq2_words(cur, sh, w, sbits);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) bq[i] = decode_word(w[i]);
+        } else {
+          uint32_t cb[32];
+          ptq1_code_bytes([&](int i) { return (cur.d[(2 + i) >> 2] >> (8 * ((2 + i) & 3))) & 0xFFu; }, lut8, cb);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) bq[i] = v4i{(int)cb[4 * i], (int)cb[4 * i + 1], (int)cb[4 * i + 2], (int)cb[4 * i + 3]};
+          sbits = cur.d[0] & 0xFFFFu;
+        }
         if (a_lane) {
           const uint4* ap = reinterpret_cast<const uint4*>(lds_a + ((cs * GPS + alg) * kXfLimbs + ar) * kBlkArow);
 #pragma unroll
@@ -247,10 +238,9 @@ __global__ __launch_bounds__(kBlkThreads, 1) void blocks_gemv_kernel(const void*
 #pragma unroll
         for (int i = 0; i < kWordsPerGroup; i += 2) {
           acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)av[i].x, (int)av[i].y, (int)av[i].z, (int)av[i].w},
-                                                       decode_word(w[i]), acc0, 0, 0, 0);
+                                                       bq[i], acc0, 0, 0, 0);
           acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-              v4i{(int)av[i + 1].x, (int)av[i + 1].y, (int)av[i + 1].z, (int)av[i + 1].w}, decode_word(w[i + 1]), acc1,
-              0, 0, 0);
+              v4i{(int)av[i + 1].x, (int)av[i + 1].y, (int)av[i + 1].z, (int)av[i + 1].w}, bq[i + 1], acc1, 0, 0, 0);
         }
         const v4i acc = acc0 + acc1;
         const float2 xf = lds_xf[cs * GPS + lg];
@@ -348,7 +338,7 @@ __global__ __launch_bounds__(kBlkThreads, 1) void blocks_band_kernel(const void*
   const BlkStage lay = blk_stage_layout(nch, tsub, G, BB);
   char* const lds_a = lds;
   float2* const lds_xf = reinterpret_cast<float2*>(lds + blk_lds_xf(nch));
-  uint32_t* const lut = reinterpret_cast<uint32_t*>(lds + blk_lds_lut(nch));
+  uint2* const lut8 = reinterpret_cast<uint2*>(lds + blk_lds_lut(nch));  // PTQ1_0 trit table
   float* const red = reinterpret_cast<float*>(lds + blk_lds_red(nch));
   char* const stage = lds + lay.stage;
 
@@ -386,7 +376,7 @@ __global__ __launch_bounds__(kBlkThreads, 1) void blocks_band_kernel(const void*
   // 2. the operand image, the trit table, zeroed partial sums
   for (int i = tid; i < tsub * NW * 16; i += kBlkThreads) red[i] = 0.f;
   if constexpr (FMT == kPtq1)
-    for (int i = tid; i < 256; i += kBlkThreads) lut[i] = trit_byte_codes(static_cast<uint32_t>(i));
+    for (int i = tid; i < 256; i += kBlkThreads) lut8[i] = trit_entry(static_cast<uint32_t>(i));
   if (xwave) {
     const v4u* cst = reinterpret_cast<const v4u*>(&kXformConst.w[xf_mode<L>()][0][lane][0]);
     const v4u* cst2 = reinterpret_cast<const v4u*>(&kXformConst.w[xf_mode<L>()][1][lane][0]);
@@ -395,7 +385,11 @@ __global__ __launch_bounds__(kBlkThreads, 1) void blocks_band_kernel(const void*
 #pragma unroll
     for (int r = 0; r < kBlkMaxTasks; ++r) {
       const int ch = wave + NW * r;
-      if (ch < nch) xform_chunk<L, DT>(xin[r], 8 * ch, lane, cf, cs, lds_a, lds_xf, kBlkArow);
+      if (ch < nch) {
+        // PTQ1_0: limb rows in natural element order, to match its code bytes
+        if constexpr (FMT == kPtq1) xform_chunk_natural<L, DT>(xin[r], 8 * ch, lane, cf, cs, lds_a, lds_xf, kBlkArow);
+        else xform_chunk<L, DT>(xin[r], 8 * ch, lane, cf, cs, lds_a, lds_xf, kBlkArow);
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0): this wave's staging landed
@@ -456,24 +450,31 @@ __global__ __launch_bounds__(kBlkThreads, 1) void blocks_band_kernel(const void*
   for (int j = 0; j < MI; ++j) {
     part[j] = 0.f;
     if (j < MI - 1 || iv[j]) {
-      uint32_t w[8], sbits;
+      // the MFMA operands of the block's 8 code words: PQ2_0 the 2-bit words
+      // decoded; PTQ1_0 the codes as bytes in natural order (trit table)
+      v4i bq[kWordsPerGroup];
+      uint32_t sbits;
       if constexpr (FMT == kPq2) {
         // codes from byte 2 (even spans) or 0 (odd spans) of the first dword
         const int o = (ss[j] & 1) ? 0 : 2;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) w[i] = __builtin_amdgcn_alignbyte(bl[j].d[i + 1], bl[j].d[i], o);
+        for (int i = 0; i < 8; ++i) bq[i] = decode_word(__builtin_amdgcn_alignbyte(bl[j].d[i + 1], bl[j].d[i], o));
         sbits = sb16[j];
       } else {
-        blk_words<FMT>(bl[j], 0, lut, w, sbits);
+        uint32_t cb[32];
+        ptq1_code_bytes([&](int i) { return (bl[j].d[(2 + i) >> 2] >> (8 * ((2 + i) & 3))) & 0xFFu; }, lut8, cb);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bq[i] = v4i{(int)cb[4 * i], (int)cb[4 * i + 1], (int)cb[4 * i + 2], (int)cb[4 * i + 3]};
+        sbits = bl[j].d[0] & 0xFFFFu;
       }
       v4i acc0 = {}, acc1 = {};
 #pragma unroll
       for (int i = 0; i < kWordsPerGroup; i += 2) {
         const uint4 u0 = av[j][i], u1 = av[j][i + 1];
-        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w},
-                                                     decode_word(w[i]), acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w},
-                                                     decode_word(w[i + 1]), acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w}, bq[i], acc0, 0, 0,
+                                                     0);
+        acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w}, bq[i + 1], acc1,
+                                                     0, 0, 0);
       }
       const v4i acc = acc0 + acc1;
       const float v = static_cast<float>(acc[3]) * 16777216.f + static_cast<float>(acc[2]) * 65536.f +

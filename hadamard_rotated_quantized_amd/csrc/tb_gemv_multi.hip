@@ -49,7 +49,7 @@
 #include <type_traits>
 #include <vector>
 
-#include "tb_xform.h"
+#include "tb_ptq1_nat.h"
 
 namespace tb {
 
@@ -110,60 +110,6 @@ __host__ __device__ inline int64_t multi_lds_total(int max_nch) { return multi_l
 // ---------------------------------------------------------------------------
 // 1. transform every chunk of every module's input
 // ---------------------------------------------------------------------------
-// The operand image in natural element order, for PTQ1_0 plans: byte p of a
-// (group, limb) row is element p of the group.  xform_chunk (tb_xform.h)
-// writes each 16-element block transposed (byte 4 x + t = element x + 4 t),
-// the order the 2-bit code-word decode produces; PTQ1_0's trit table gives
-// the codes in natural order instead.  Same scaling and limbs as
-// xform_chunk; before the stores the lanes of each quad (the four lanes that
-// hold one 16-element block) transpose their dwords bytewise (two DPP
-// exchanges and two byte permutes per dword).
-template <int L, int DT>
-__device__ __forceinline__ void xform_chunk_natural(const XformIn<DT>& in, int g0, int lane, const v4u cfirst[2],
-                                                    const v4u csecond[2], char* img, float2* xf) {
-  float v128;
-  const v16f U = xform_rotate<L, DT>(in, lane, cfirst, csecond, v128);
-  float m = 0.f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(U[r]));
-#pragma unroll
-  for (int j = 0; j < 6; ++j) m = fmaxf(m, xor_lane(m, j, lane));
-  const uint32_t mb = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(__float_as_uint(m))));
-  int e = static_cast<int>((mb >> 23) & 0xFF) - 127;
-  e = mb == 0 ? 0 : (e < -90 ? -90 : e);
-  const float sigma = __uint_as_float(static_cast<uint32_t>(29 - e + 127) << 23);
-  const float f = __uint_as_float(static_cast<uint32_t>(e - 29 + 127) << 23) * inv_sqrt_block_or_one<L>();
-  uint32_t qd[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) qd[r] = static_cast<uint32_t>(static_cast<int>(U[r] * sigma)) + 0x808080u;
-  // quad transpose selectors: with lane x ^ 2, then with lane x ^ 1
-  const int x = lane & 3;
-  const uint32_t sel1 = (x >> 1) ? 0x03020706u : 0x05040100u;
-  const uint32_t sel2 = (x & 1) ? 0x03070105u : 0x06020400u;
-  auto quad_t = [&](uint32_t d) {
-    const uint32_t p = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(d), 0x4E, 0xF, 0xF, false));
-    const uint32_t d1 = __builtin_amdgcn_perm(p, d, sel1);
-    const uint32_t q = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(d1), 0xB1, 0xF, 0xF, false));
-    return __builtin_amdgcn_perm(q, d1, sel2);
-  };
-  const int h = lane >> 5;
-  char* const arow = img + static_cast<int64_t>(g0 + h) * (kXfLimbs * 128) + (lane & 31) * 4;
-#pragma unroll
-  for (int Q = 0; Q < 4; ++Q) {
-    const uint32_t a0 = qd[4 * Q], a1 = qd[4 * Q + 1], a2 = qd[4 * Q + 2], a3 = qd[4 * Q + 3];
-    const uint32_t l0 = (__builtin_amdgcn_perm(a1, a0, 0x0C0C0400u) | __builtin_amdgcn_perm(a3, a2, 0x04000C0Cu)) ^ 0x80808080u;
-    const uint32_t l1 = (__builtin_amdgcn_perm(a1, a0, 0x0C0C0501u) | __builtin_amdgcn_perm(a3, a2, 0x05010C0Cu)) ^ 0x80808080u;
-    const uint32_t l2 = (__builtin_amdgcn_perm(a1, a0, 0x0C0C0602u) | __builtin_amdgcn_perm(a3, a2, 0x06020C0Cu)) ^ 0x80808080u;
-    const uint32_t l3 = __builtin_amdgcn_perm(a1, a0, 0x0C0C0703u) | __builtin_amdgcn_perm(a3, a2, 0x07030C0Cu);
-    char* row = arow + static_cast<int64_t>(2 * Q) * (kXfLimbs * 128);
-    *reinterpret_cast<uint32_t*>(row) = quad_t(l0);
-    *reinterpret_cast<uint32_t*>(row + 128) = quad_t(l1);
-    *reinterpret_cast<uint32_t*>(row + 256) = quad_t(l2);
-    *reinterpret_cast<uint32_t*>(row + 384) = quad_t(l3);
-  }
-  xform_group_sums<L>(U, v128, g0, lane, f, xf);
-}
-
 template <int L, int DT, bool NAT>
 __global__ __launch_bounds__(256) void multi_prep_kernel(const char* __restrict__ plan, char* __restrict__ ws) {
   const MultiHeader* hd = reinterpret_cast<const MultiHeader*>(plan);
@@ -187,7 +133,7 @@ __global__ __launch_bounds__(256) void multi_prep_kernel(const char* __restrict_
   const v4u cs[2] = {cst2[0], cst2[1]};
   char* img = ws + md.ws_off;
   float2* xf = reinterpret_cast<float2*>(img + static_cast<int64_t>(multi_nch(md.K)) * kMultiImgChunk);
-  if constexpr (NAT) xform_chunk_natural<L, DT>(in, 8 * c, lane, cf, cs, img, xf);
+  if constexpr (NAT) xform_chunk_natural<L, DT>(in, 8 * c, lane, cf, cs, img, xf, 128);
   else xform_chunk<L, DT>(in, 8 * c, lane, cf, cs, img, xf, 128);
 }
 
@@ -236,18 +182,8 @@ __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __
   // PTQ1_0: trit byte -> its five codes (lowest base-3 digit first) as
   // bytes 0-4 of an 8-byte entry, written before the first piece's barrier
   uint2* const lut = reinterpret_cast<uint2*>(lds + multi_lds_lut(max_nch));
-  if constexpr (FMT == kMultiPtq1) {
-    for (int i = tid; i < 256; i += kMultiThreads) {
-      uint32_t b = static_cast<uint32_t>(i), lo = 0, hi = 0;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        lo |= (b % 3u) << (8 * m);
-        b /= 3u;
-      }
-      hi = b % 3u;
-      lut[i] = make_uint2(lo, hi);
-    }
-  }
+  if constexpr (FMT == kMultiPtq1)
+    for (int i = tid; i < 256; i += kMultiThreads) lut[i] = trit_entry(static_cast<uint32_t>(i));
 
   int img_off = -1;  // workspace offset of the operand image in LDS
   for (;;) {
@@ -469,27 +405,12 @@ __global__ __launch_bounds__(64 * NW, 1) void multi_stream_kernel(const char* __
         for (int w = 0; w < kWordsPerGroup; ++w) av[w] = ap[w];
       }
       // the group's 128 codes as bytes in natural order (the operand image of
-      // PTQ1_0 plans is in natural order too): code 5 i + j is byte j of
-      // trit byte i's table entry; byte dword o (codes 4 o .. 4 o + 3)
-      // starts at entry i = 4 o / 5, byte j = 4 o % 5
-      uint2 ent[26];
-#pragma unroll
-      for (int i = 0; i < 26; ++i) {
-        const int byte = kPtq1Bytes * h + 2 + i;
-        ent[i] = lut[(d[byte >> 2] >> (8 * (byte & 3))) & 0xFFu];
-      }
+      // PTQ1_0 plans is in natural order too)
       uint32_t cb[32];
-#pragma unroll
-      for (int o = 0; o < 32; ++o) {
-        const int i = (4 * o) / 5, j = (4 * o) % 5;
-        const uint2 a = ent[i];
-        const uint2 b = i + 1 < 26 ? ent[i + 1] : make_uint2(0u, 0u);
-        if (j == 0) cb[o] = a.x;
-        else if (j == 1) cb[o] = __builtin_amdgcn_alignbyte(a.y, a.x, 1);
-        else if (j == 2) cb[o] = __builtin_amdgcn_alignbyte(a.y, a.x, 2) | (b.x << 24);
-        else if (j == 3) cb[o] = __builtin_amdgcn_alignbyte(a.y, a.x, 3) | (b.x << 16);
-        else cb[o] = a.y | (b.x << 8);
-      }
+      ptq1_code_bytes([&](int i) {
+        const int byte = kPtq1Bytes * h + 2 + i;
+        return (d[byte >> 2] >> (8 * (byte & 3))) & 0xFFu;
+      }, lut, cb);
       const uint32_t sbits = d[7 * h] & 0xFFFFu;
       v4i acc0 = {}, acc1 = {};
 #pragma unroll
