@@ -129,8 +129,8 @@ __device__ __forceinline__ void transform_chunk(float v[16], int lane, float* sc
   }
 }
 
-// cfg: batch rows B (bits 0-3), subtiles per workgroup (bits 5-7, split
-// modes), grid size (bits 8-31).  aux: split modes, rows per workgroup;
+// cfg: batch rows B (bits 0-3), remainder flag (bit 4), subtiles per
+// workgroup (bits 5-7, split modes), grid size (bits 8-31).  aux: split modes, rows per workgroup;
 // persistent mode, tile groups (8 tiles of M rows).  The 14 argument SGPRs
 // the dispatcher can preload (16 user SGPRs minus the kernel-argument
 // pointer) hold everything but y, which is needed last.
@@ -141,6 +141,15 @@ __device__ __forceinline__ void transform_chunk(float v[16], int lane, float* sc
 // 1 KB per wave instruction -- fully coalesced, where the per-item loads of
 // a tile touch 16 rows per instruction -- and fetches the scale and bias of
 // each of its (at most kStagedItems) items with 2-byte loads up front.
+//
+// Remainder flag (one batch row, kSplitRing): the band's last subtile holds
+// at most 4 rows, and a 16-row MFMA item would spend three quarters of its
+// decode and matmul on padding.  Those rows go through 4x4x4 MFMA blocks
+// instead: a unit is 8 groups, block b = (group, half of its 8 words);
+// block b's A is the 4 limb rows (limb 3 zero) of its 64 activations, its B
+// the same 64 codes of the 4 rows, so D[b][limb][row] is one half-group's
+// limb sums, row r's in lane 4 b + r.  Wave w takes units 7 - w, 15 - w, ...
+// (the waves with fewer 16-row items first).
 template <int NB, int M, int L, int DT, int MODE>
 __global__ __launch_bounds__(kFusedThreads, NB == 8 ? 2 : 4) void gemv_fused_kernel(
     const void* __restrict__ x, const int8_t* __restrict__ signs, const uint32_t* __restrict__ codes,
@@ -236,7 +245,7 @@ __global__ __launch_bounds__(kFusedThreads, NB == 8 ? 2 : 4) void gemv_fused_ker
   if constexpr (SPLIT) {
     band0 = bid * aux;
     nrows = min(aux, N - band0);
-    const int items = tsub * S;
+    const int items = (tsub - ((cfg >> 4) & 1)) * S;
     total = items > wave ? (items - wave + kFusedWaves - 1) / kFusedWaves : 0;
   } else {
     total = ((aux - 1 - bid) / grid + 1) * S;
@@ -374,6 +383,36 @@ __global__ __launch_bounds__(kFusedThreads, NB == 8 ? 2 : 4) void gemv_fused_ker
   if constexpr (SPLIT) {
     for (int i = tid; i < tsub * kFusedWaves * NB * M; i += kFusedThreads) red[i] = 0.f;
   }
+  // remainder units (see above): this lane is block rbk, limb and row rri
+  constexpr bool REMK = NB == 1 && M == 16 && MODE == kSplitRing;
+  constexpr int RR = REMK ? 3 : 1;  // units in flight per wave
+  const bool remp = REMK && ((cfg >> 4) & 1);
+  const int rbk = lane >> 2, rri = lane & 3;
+  const int rfirst = kFusedWaves - 1 - wave;
+  const int nru = (G + 7) >> 3;
+  const int rtotal = remp && nru > rfirst ? (nru - rfirst + kFusedWaves - 1) / kFusedWaves : 0;
+  const int rrow = (tsub - 1) * M + rri;  // band row of this lane's codes
+  struct RemUnit {
+    uint4 w;
+    uint16_t s, bias;
+  };
+  auto rem_group = [&](int k) { return (rfirst + kFusedWaves * k) * 8 + (rbk >> 1); };
+  auto load_rem = [&](int k, RemUnit& u) {
+    const int g = rem_group(k);
+    const bool live = k < rtotal && g < G;
+    const int co = live ? rrow * (W * 4) + g * 32 + (rbk & 1) * 16 : kOob;
+    const int so = live ? rrow * (G * 2) + g * 2 : kOob;
+    const v4u w = __builtin_amdgcn_raw_buffer_load_b128(rc, co, 0, 0);
+    u.w = make_uint4(w.x, w.y, w.z, w.w);
+    u.s = __builtin_amdgcn_raw_buffer_load_b16(rs, so, 0, 0);
+    u.bias = __builtin_amdgcn_raw_buffer_load_b16(rb, so, 0, 0);
+  };
+  RemUnit ru[RR];
+  if (rtotal > 0) {
+#pragma unroll
+    for (int k = 0; k < RR; ++k) load_rem(k, ru[k]);
+  }
+
   if constexpr (STAGED) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's band slots have landed
   __syncthreads();
 
@@ -500,6 +539,53 @@ __global__ __launch_bounds__(kFusedThreads, NB == 8 ? 2 : 4) void gemv_fused_ker
       }
     }
   }
+  if constexpr (REMK) {
+    if (rtotal > 0) {
+      float yr = 0.f;
+      auto consume_rem = [&](const RemUnit& u, int k) {
+        const int g = rem_group(k);
+        const int h = rbk & 1;
+        const bool gin = g < G;
+        const uint4* ap = (gin && rri < kLimbs) ? lds_a + (g * kLimbs + rri) * kLdsRow + 4 * h : lds_zero;
+        const uint32_t wv[4] = {u.w.x, u.w.y, u.w.z, u.w.w};
+        v4i acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint4 a = ap[t];
+          const uint32_t w = wv[t];
+          acc0 = __builtin_amdgcn_mfma_i32_4x4x4i8(static_cast<int>(a.x), static_cast<int>(w & 0x03030303u), acc0,
+                                                   0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_i32_4x4x4i8(static_cast<int>(a.y),
+                                                   static_cast<int>((w >> 2) & 0x03030303u), acc1, 0, 0, 0);
+          acc0 = __builtin_amdgcn_mfma_i32_4x4x4i8(static_cast<int>(a.z),
+                                                   static_cast<int>((w >> 4) & 0x03030303u), acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_i32_4x4x4i8(static_cast<int>(a.w),
+                                                   static_cast<int>((w >> 6) & 0x03030303u), acc1, 0, 0, 0);
+        }
+        const v4i acc = acc0 + acc1;
+        const float v = static_cast<float>(acc[2]) * 65536.f + static_cast<float>(acc[1]) * 256.f +
+                        static_cast<float>(acc[0]);
+        // the bias term once per group (in its first half)
+        const float2 xf = gin ? lds_xf[g] : make_float2(0.f, 0.f);
+        const float sc = gin ? half_bits_to_float(u.s) : 0.f;
+        const float bi = (gin && h == 0) ? half_bits_to_float(u.bias) : 0.f;
+        yr += sc * (v * xf.y) + bi * xf.x;
+      };
+      for (int base = 0; base < rtotal; base += RR) {
+#pragma unroll
+        for (int sl = 0; sl < RR; ++sl) {
+          if (base + sl < rtotal) {
+            consume_rem(ru[sl], base + sl);
+            if (base + sl + RR < rtotal) load_rem(base + sl + RR, ru[sl]);
+          }
+        }
+      }
+      // add up the 16 blocks of each row (lanes r, r + 4, ..., r + 60)
+#pragma unroll
+      for (int j = 2; j < 6; ++j) yr += xor_lane(yr, j, lane);
+      if (lane < 4) red[((tsub - 1) * kFusedWaves + wave) * M + lane] = yr;
+    }
+  }
   if constexpr (SPLIT) {
     // add up the waves' partial sums of every row of the band
     __syncthreads();
@@ -518,6 +604,7 @@ __global__ __launch_bounds__(kFusedThreads, NB == 8 ? 2 : 4) void gemv_fused_ker
 // Launch shape of one call.
 struct FusedPlan {
   int mode;
+  int rem;  // 4-row remainder blocks (split ring mode, one batch row)
   int tsub, aux, grid;
   int64_t lds;
 };
@@ -528,6 +615,7 @@ static FusedPlan fused_plan(int64_t B, int64_t K, int64_t N, int cus) {
   const int64_t Gp = padded_groups(K);
   const int64_t rb = K / kCodesPerWord * 4;  // code bytes per row
   FusedPlan p;
+  p.rem = 0;
   // split modes: one band of about N / CUs rows (at least 16) per workgroup
   const int64_t rows = std::max<int64_t>((N + cus - 1) / cus, 16);
   const int64_t tsub = (rows + M - 1) / M;
@@ -550,6 +638,8 @@ static FusedPlan fused_plan(int64_t B, int64_t K, int64_t N, int cus) {
     } else {
       p.mode = kSplitRing;
       p.lds = base;
+      const int64_t rr = rows % M;
+      p.rem = (B == 1 && rr >= 1 && rr <= 4) ? 1 : 0;
     }
   } else {
     // persistent mode: tile groups of 8 tiles, at most 2 workgroups per CU
@@ -628,7 +718,7 @@ void gemv_fused_launch(const void* x, int x_dtype, int64_t B, int64_t K, const i
                        const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, int64_t N,
                        float* y, hipStream_t st) {
   const FusedPlan p = fused_plan(B, K, N, device_cus());
-  const int cfg = static_cast<int>(B) | (p.tsub << 5) | (p.grid << 8);
+  const int cfg = static_cast<int>(B) | (p.rem << 4) | (p.tsub << 5) | (p.grid << 8);
   const int n = static_cast<int>(N), k = static_cast<int>(K);
   const size_t lds = static_cast<size_t>(p.lds);
   if (B == 1)

@@ -546,6 +546,9 @@ TWO_PATHS = [
     (517, 5120, 5, 1024, "f32"),     # batch kernel: fp32 x in registers, staged signs, second set of 1 row
     (2000, 17408, 7, 1024, "bf16"),  # batch kernel: six slices, staged bf16 x, ragged last row block
     (300, 9216, 2, 512, "bf16"),     # batch kernel: 512-blocks, 9 chunks
+    (4997, 17408, 1, 1024, "bf16"),  # fused, 20-row bands: 4-row remainder blocks, last band of 17 rows
+    (4370, 17408, 1, 1024, "f32"),   # fused, 18-row bands (2-row remainder), last band of 14 rows
+    (4352, 16896, 1, 512, "bf16"),   # fused, 17-row bands (1-row remainder), 132 groups: last unit half padding
 ]
 
 
