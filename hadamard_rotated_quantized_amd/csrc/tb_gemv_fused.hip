@@ -638,8 +638,11 @@ static FusedPlan fused_plan(int64_t B, int64_t K, int64_t N, int cus) {
     } else {
       p.mode = kSplitRing;
       p.lds = base;
+      // remainder blocks where measured faster: bands of 2 to 4 subtiles
+      // (down_proj, 20 rows: -6%); at 5 (gate_proj, 68 rows) they were 3%
+      // slower than the 16-row subtile
       const int64_t rr = rows % M;
-      p.rem = (B == 1 && rr >= 1 && rr <= 4) ? 1 : 0;
+      p.rem = (B == 1 && rr >= 1 && rr <= 4 && tsub <= 4) ? 1 : 0;
     }
   } else {
     // persistent mode: tile groups of 8 tiles, at most 2 workgroups per CU
