@@ -55,6 +55,15 @@
 //   chains interleave.  Partial sums meet in LDS and every row of y is
 //   written once.
 //
+// * Remainder blocks.  When the band's last subtile would hold at most 8
+//   real rows, those rows (one or two quads of 4) go through
+//   v_mfma_i32_4x4x4_16b_i8 instead of 16-row items: a unit is (quad, 8
+//   groups); each of the 16 blocks is one (group, half of its words) pair
+//   with the group's 4 limb rows as A and the quad's codes as B, so block
+//   b's result is the limb sums of its half-group for each row of the quad,
+//   row r's in lane 4 b + r.  Units are dealt round robin from the first
+//   wave with one 16-row item fewer.
+//
 // Used for batch 1, blocks 0 / 512 / 1024, at most 3 chunk transforms per
 // wave, bands of at most 7 subtiles and an LDS footprint within the limit;
 // tb_ternary_gemv takes other paths otherwise.
@@ -97,14 +106,16 @@ __host__ __device__ inline BandLds band_lds_layout(int64_t nch, int64_t tsub, in
   return l;
 }
 
-// rows: output rows per band (the last band may be short); tsub: 16-row
-// subtiles per band.
+// rows: output rows per band (the last band may be short); tsq: 16-row
+// subtiles per band (bits 0-7) and remainder quads (bits 8-9).
 template <int L, int DT, int MI>
 __global__ __launch_bounds__(kBandThreads, 1) void gemv_band_kernel(
     const void* __restrict__ x, const int8_t* __restrict__ signs, const uint32_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases, int N, int K, int rows,
-    int tsub, float* __restrict__ y) {
+    int tsq, float* __restrict__ y) {
   constexpr int M = 16, GPS = 4;
+  const int tsub = tsq & 0xFF;   // 16-row subtiles per band
+  const int quads = tsq >> 8;    // remainder quads (0: none)
   extern __shared__ uint4 lds_dyn[];
   char* const lds = reinterpret_cast<char*>(lds_dyn);
 
@@ -214,7 +225,7 @@ __global__ __launch_bounds__(kBandThreads, 1) void gemv_band_kernel(
   const int lg = lane >> 4, c = lane & 15;
   const int ar = c & 3, alg = (c >> 2) & 3;
   const bool a_lane = alg == lg;
-  const int items = tsub * S;
+  const int items = (tsub - (quads > 0)) * S;
   const uint32_t lane_c = static_cast<uint32_t>(c * RB + lg * 32);
   auto stage_at = [](uint32_t off) { return off + (off >> 10) * (kBandSlot - 1024); };
 
@@ -315,6 +326,63 @@ __global__ __launch_bounds__(kBandThreads, 1) void gemv_band_kernel(
       if (lg == 0) red[(t * kBandWaves + wave) * 16 + c] = v;
     }
   }
+  // ---- 3b. remainder blocks (see above): unit u = (quad u / nru, groups
+  //          8 (u % nru) ..), this lane block rbk (group 8 (u % nru) +
+  //          rbk / 2, half rbk & 1) and quad row rri
+  if (quads > 0) {
+    const int nru = (G + 7) >> 3;
+    const int nunits = quads * nru;
+    const int rbk = lane >> 2, rri = lane & 3, h = rbk & 1;
+    float yq0 = 0.f, yq1 = 0.f;
+    for (int u = (wave - items % kBandWaves + kBandWaves) % kBandWaves; u < nunits; u += kBandWaves) {
+      const int qd = u >= nru;
+      const int g = (u - qd * nru) * 8 + (rbk >> 1);
+      const bool gin = g < G;
+      const int row = (tsub - 1) * M + qd * 4 + rri;
+      const uint4 cq = gin ? *reinterpret_cast<const uint4*>(
+                                 st_codes + stage_at(static_cast<uint32_t>(row * RB + g * 32 + h * 16)))
+                           : make_uint4(0, 0, 0, 0);
+      // groups past G (a partial last unit) lie within the last chunk's image
+      const uint4* ap = reinterpret_cast<const uint4*>(lds_a + (g * kXfLimbs + rri) * kBandArow) + 4 * h;
+      const uint32_t wv[4] = {cq.x, cq.y, cq.z, cq.w};
+      v4i acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint4 a = ap[t];
+        const uint32_t w = wv[t];
+        acc0 = __builtin_amdgcn_mfma_i32_4x4x4i8(static_cast<int>(a.x), static_cast<int>(w & 0x03030303u), acc0, 0,
+                                                 0, 0);
+        acc1 = __builtin_amdgcn_mfma_i32_4x4x4i8(static_cast<int>(a.y), static_cast<int>((w >> 2) & 0x03030303u),
+                                                 acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_i32_4x4x4i8(static_cast<int>(a.z), static_cast<int>((w >> 4) & 0x03030303u),
+                                                 acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_i32_4x4x4i8(static_cast<int>(a.w), static_cast<int>((w >> 6) & 0x03030303u),
+                                                 acc1, 0, 0, 0);
+      }
+      const v4i acc = acc0 + acc1;
+      const float v = static_cast<float>(acc[3]) * 16777216.f + static_cast<float>(acc[2]) * 65536.f +
+                      static_cast<float>(acc[1]) * 256.f + static_cast<float>(acc[0]);
+      const int si = gin ? row * G + g : 0;
+      // the bias term once per group (in its first half)
+      const float sc = gin ? half_bits_to_float(st_sc[si]) : 0.f;
+      const float bi = (gin && h == 0) ? half_bits_to_float(st_bi[si]) : 0.f;
+      const float2 xf = gin ? lds_xf[g] : make_float2(0.f, 0.f);
+      const float pr = sc * (v * xf.y) + bi * xf.x;
+      if (qd) yq1 += pr;
+      else yq0 += pr;
+    }
+    // add up the 16 blocks of each row (lanes r, r + 4, ..., r + 60)
+#pragma unroll
+    for (int j = 2; j < 6; ++j) {
+      yq0 += xor_lane(yq0, j, lane);
+      yq1 += xor_lane(yq1, j, lane);
+    }
+    if (lane < 4) {
+      float* rr = red + ((tsub - 1) * kBandWaves + wave) * 16 + lane;
+      rr[0] = yq0;
+      if (quads > 1) rr[4] = yq1;
+    }
+  }
   __syncthreads();
   for (int i = tid; i < tsub * M; i += kBandThreads) {
     const int t = i >> 4, cc = i & 15;
@@ -331,7 +399,7 @@ __global__ __launch_bounds__(kBandThreads, 1) void gemv_band_kernel(
 // host side
 // --------------------------------------------------------------------------
 struct BandPlan {
-  int rows, tsub, grid, mi;
+  int rows, tsub, grid, mi, quads;
   int64_t lds;
   bool ok;
 };
@@ -350,7 +418,10 @@ static BandPlan band_plan(int64_t K, int64_t N, int cus) {
   p.rows = static_cast<int>(rows);
   p.tsub = static_cast<int>(tsub);
   p.grid = static_cast<int>((N + rows - 1) / rows);
-  p.mi = static_cast<int>((tsub * S + kBandWaves - 1) / kBandWaves);  // matmul items per wave
+  // a last subtile of at most 8 real rows goes through remainder blocks
+  const int64_t rr = rows - (tsub - 1) * 16;
+  p.quads = (tsub >= 2 && rr <= 8) ? static_cast<int>((rr + 3) / 4) : 0;
+  p.mi = static_cast<int>(((tsub - (p.quads > 0)) * S + kBandWaves - 1) / kBandWaves);  // 16-row items per wave
   const int64_t cslots = (tsub * 16 * RB + 96 + 1023) / 1024 + 1;
   const int64_t sbslots = (tsub * 16 * G * 2 + 64 + 1023) / 1024;
   const int64_t nss = (rows * G * 2 + 1023) / 1024;
@@ -376,7 +447,7 @@ static void band_launch_t(const void* x, const int8_t* signs, const uint32_t* co
   static std::atomic<uint64_t> lds_set{0};
   lds_limit_once(reinterpret_cast<const void*>(kern), static_cast<int>(kBandLdsMax), lds_set);
   hipLaunchKernelGGL(kern, dim3(p.grid), dim3(kBandThreads), static_cast<size_t>(p.lds), st, x, signs, codes, scales,
-                     biases, N, K, p.rows, p.tsub, y);
+                     biases, N, K, p.rows, p.tsub | (p.quads << 8), y);
 }
 
 template <int L, int DT>

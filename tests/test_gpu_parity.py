@@ -549,6 +549,7 @@ TWO_PATHS = [
     (4997, 17408, 1, 1024, "bf16"),  # fused, 20-row bands: 4-row remainder blocks, last band of 17 rows
     (4370, 17408, 1, 1024, "f32"),   # fused, 18-row bands (2-row remainder), last band of 14 rows
     (4352, 16896, 1, 512, "bf16"),   # fused, 17-row bands (1-row remainder), 132 groups: last unit half padding
+    (4998, 6144, 1, 1024, "f32"),    # band kernel, 20-row bands: one remainder quad, last band of 18 rows
 ]
 
 
